@@ -1,0 +1,256 @@
+"""fp8_fine_grained_quant_amd -- Python binding of libfp8q (MI355X, gfx950).
+
+Argument marshalling only: every step runs in the HIP kernels of libfp8q.so,
+reached through its C ABI (include/fp8q.h).  PyTorch supplies device memory
+and the current HIP stream.  There is no CPU fallback: if the library is
+missing or a call is rejected, an exception is raised.
+
+Raw entry points (same names and argument order as the C ABI, with torch
+tensors in place of pointer + leading dimension):
+
+    fp8q_quant_act_1x128(x, q, scale)
+    fp8q_quant_weight_128x128(w, q, q_t, scale)        # q_t may be None
+    fp8q_quant_transpose(x, q_t, scale_t)
+    fp8q_gemm_fprop(xq, xs, wq, ws, y)
+    fp8q_gemm_dgrad(dyq, dys, wq_t, ws, dx)
+    fp8q_gemm_wgrad(dyq_t, dys_t, xq_t, xs_t, dw, accumulate=False)
+    fp8q_grouped_gemm(xq, xs, wq, ws, offsets, y)
+
+Each GEMM also takes exact=True, which calls the *_exact entry point (BF16
+matrix instruction on exactly converted codes: the exact-accumulation variant).
+
+Convenience wrappers that allocate the outputs: quant_act_1x128,
+quant_weight_128x128, quant_transpose, gemm_fprop, gemm_dgrad, gemm_wgrad,
+grouped_gemm.
+"""
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfp8q.so")
+
+FP8Q_BF16, FP8Q_F32 = 0, 1
+_STATUS = ["FP8Q_OK", "FP8Q_ERR_NULL", "FP8Q_ERR_SHAPE", "FP8Q_ERR_STRIDE",
+           "FP8Q_ERR_ALIGN", "FP8Q_ERR_DTYPE", "FP8Q_ERR_LAUNCH"]
+EXPORTS = ["fp8q_status_string", "fp8q_quant_act_1x128", "fp8q_quant_weight_128x128",
+           "fp8q_quant_transpose", "fp8q_gemm_fprop", "fp8q_gemm_dgrad", "fp8q_gemm_wgrad",
+           "fp8q_grouped_gemm", "fp8q_gemm_fprop_exact", "fp8q_gemm_dgrad_exact", "fp8q_gemm_wgrad_exact",
+           "fp8q_grouped_gemm_exact"]
+
+
+class Fp8qError(RuntimeError):
+    def __init__(self, status, name):
+        self.status = status
+        super().__init__(f"{name}: {status_string(status)}")
+
+
+_lib = None
+
+
+def load_library(path=LIB_PATH):
+    """Load libfp8q.so (once) and declare its C signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"libfp8q.so not built ({path}); run __graft_entry__.build()")
+    lib = ctypes.CDLL(path)
+    P, I64, I32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    sig = {
+        "fp8q_status_string": ([I32], ctypes.c_char_p),
+        "fp8q_quant_act_1x128": ([P, I32, I64, I64, I64, P, I64, P, I64, P], I32),
+        "fp8q_quant_weight_128x128": ([P, I32, I64, I64, I64, P, I64, P, I64, P, I64, P], I32),
+        "fp8q_quant_transpose": ([P, I32, I64, I64, I64, P, I64, P, I64, P], I32),
+        "fp8q_gemm_fprop": ([P, P, P, P, I64, I64, I64, P, I32, I64, P], I32),
+        "fp8q_gemm_dgrad": ([P, P, P, P, I64, I64, I64, P, I32, I64, P], I32),
+        "fp8q_gemm_wgrad": ([P, P, P, P, I64, I64, I64, P, I64, I32, P], I32),
+        "fp8q_grouped_gemm": ([P, P, P, P, P, I64, I64, I64, I64, P, I32, I64, P], I32),
+    }
+    for name in ["fp8q_gemm_fprop", "fp8q_gemm_dgrad", "fp8q_gemm_wgrad", "fp8q_grouped_gemm"]:
+        sig[name + "_exact"] = sig[name]
+    for name, (args, res) in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    _lib = lib
+    return lib
+
+
+def status_string(status):
+    return load_library().fp8q_status_string(int(status)).decode()
+
+
+# ----------------------------------------------------------------- marshalling
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _ld(t):
+    """Row stride (elements) of a 2-D tensor whose rows are contiguous."""
+    if t.dim() != 2 or (t.shape[1] > 1 and t.stride(1) != 1):
+        raise ValueError("expected a 2-D tensor with contiguous rows")
+    return t.stride(0) if t.shape[0] > 1 else max(t.shape[1], t.stride(0))
+
+
+def _dtype_code(t):
+    if t.dtype == torch.bfloat16:
+        return FP8Q_BF16
+    if t.dtype == torch.float32:
+        return FP8Q_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _check(status, name):
+    if status != 0:
+        raise Fp8qError(status, name)
+
+
+def _on_gpu(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("fp8q works on GPU tensors only")
+
+
+def fp8q_quant_act_1x128(x, q, scale, stream=None):
+    _on_gpu(x, q, scale)
+    rows, cols = x.shape
+    _check(load_library().fp8q_quant_act_1x128(_ptr(x), _dtype_code(x), rows, cols, _ld(x), _ptr(q), _ld(q),
+                                                _ptr(scale), _ld(scale), _stream(stream)),
+           "fp8q_quant_act_1x128")
+
+
+def fp8q_quant_weight_128x128(w, q, q_t, scale, stream=None):
+    _on_gpu(w, q, q_t, scale)
+    rows, cols = w.shape
+    ld_qt = _ld(q_t) if q_t is not None else 0
+    _check(load_library().fp8q_quant_weight_128x128(_ptr(w), _dtype_code(w), rows, cols, _ld(w), _ptr(q),
+                                                     _ld(q), _ptr(q_t), ld_qt, _ptr(scale), _ld(scale),
+                                                     _stream(stream)),
+           "fp8q_quant_weight_128x128")
+
+
+def fp8q_quant_transpose(x, q_t, scale_t, stream=None):
+    _on_gpu(x, q_t, scale_t)
+    rows, cols = x.shape
+    _check(load_library().fp8q_quant_transpose(_ptr(x), _dtype_code(x), rows, cols, _ld(x), _ptr(q_t),
+                                                _ld(q_t), _ptr(scale_t), _ld(scale_t), _stream(stream)),
+           "fp8q_quant_transpose")
+
+
+def _fn(name, exact):
+    return getattr(load_library(), name + ("_exact" if exact else ""))
+
+
+def _contig(*ts):
+    for t in ts:
+        if not t.is_contiguous():
+            raise ValueError("GEMM operands and scales must be contiguous")
+
+
+def fp8q_gemm_fprop(xq, xs, wq, ws, y, stream=None, exact=False):
+    _on_gpu(xq, xs, wq, ws, y)
+    _contig(xq, xs, wq, ws)
+    m, k = xq.shape
+    n = wq.shape[0]
+    _check(_fn("fp8q_gemm_fprop", exact)(_ptr(xq), _ptr(xs), _ptr(wq), _ptr(ws), m, n, k, _ptr(y),
+                                           _dtype_code(y), _ld(y), _stream(stream)),
+           "fp8q_gemm_fprop")
+
+
+def fp8q_gemm_dgrad(dyq, dys, wq_t, ws, dx, stream=None, exact=False):
+    _on_gpu(dyq, dys, wq_t, ws, dx)
+    _contig(dyq, dys, wq_t, ws)
+    m, n = dyq.shape
+    k = wq_t.shape[0]
+    _check(_fn("fp8q_gemm_dgrad", exact)(_ptr(dyq), _ptr(dys), _ptr(wq_t), _ptr(ws), m, n, k, _ptr(dx),
+                                           _dtype_code(dx), _ld(dx), _stream(stream)),
+           "fp8q_gemm_dgrad")
+
+
+def fp8q_gemm_wgrad(dyq_t, dys_t, xq_t, xs_t, dw, accumulate=False, stream=None, exact=False):
+    _on_gpu(dyq_t, dys_t, xq_t, xs_t, dw)
+    _contig(dyq_t, dys_t, xq_t, xs_t)
+    n, t = dyq_t.shape
+    k = xq_t.shape[0]
+    if dw.dtype != torch.float32:
+        raise TypeError("dW is FP32")
+    _check(_fn("fp8q_gemm_wgrad", exact)(_ptr(dyq_t), _ptr(dys_t), _ptr(xq_t), _ptr(xs_t), t, n, k, _ptr(dw),
+                                           _ld(dw), int(bool(accumulate)), _stream(stream)),
+           "fp8q_gemm_wgrad")
+
+
+def fp8q_grouped_gemm(xq, xs, wq, ws, offsets, y, stream=None, exact=False):
+    _on_gpu(xq, xs, wq, ws, offsets, y)
+    _contig(xq, xs, wq, ws, offsets)
+    if offsets.dtype != torch.int32:
+        raise TypeError("offsets are int32")
+    m_total, k = xq.shape
+    e, n, _ = wq.shape
+    _check(_fn("fp8q_grouped_gemm", exact)(_ptr(xq), _ptr(xs), _ptr(wq), _ptr(ws), _ptr(offsets), e, m_total,
+                                             n, k, _ptr(y), _dtype_code(y), _ld(y), _stream(stream)),
+           "fp8q_grouped_gemm")
+
+
+# ---------------------------------------------------------------- convenience
+def _cdiv(a, b):
+    return (a + b - 1) // b
+
+
+def quant_act_1x128(x, stream=None):
+    rows, cols = x.shape
+    q = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
+    s = torch.empty((rows, _cdiv(cols, 128)), dtype=torch.float32, device=x.device)
+    fp8q_quant_act_1x128(x, q, s, stream)
+    return q, s
+
+
+def quant_weight_128x128(w, transpose=True, stream=None):
+    rows, cols = w.shape
+    q = torch.empty((rows, cols), dtype=torch.uint8, device=w.device)
+    q_t = torch.empty((cols, rows), dtype=torch.uint8, device=w.device) if transpose else None
+    s = torch.empty((_cdiv(rows, 128), _cdiv(cols, 128)), dtype=torch.float32, device=w.device)
+    fp8q_quant_weight_128x128(w, q, q_t, s, stream)
+    return q, s, q_t
+
+
+def quant_transpose(x, stream=None):
+    rows, cols = x.shape
+    q_t = torch.empty((cols, rows), dtype=torch.uint8, device=x.device)
+    s_t = torch.empty((cols, _cdiv(rows, 128)), dtype=torch.float32, device=x.device)
+    fp8q_quant_transpose(x, q_t, s_t, stream)
+    return q_t, s_t
+
+
+def gemm_fprop(xq, xs, wq, ws, out_dtype=torch.bfloat16, stream=None, exact=False):
+    y = torch.empty((xq.shape[0], wq.shape[0]), dtype=out_dtype, device=xq.device)
+    fp8q_gemm_fprop(xq, xs, wq, ws, y, stream, exact)
+    return y
+
+
+def gemm_dgrad(dyq, dys, wq_t, ws, out_dtype=torch.bfloat16, stream=None, exact=False):
+    dx = torch.empty((dyq.shape[0], wq_t.shape[0]), dtype=out_dtype, device=dyq.device)
+    fp8q_gemm_dgrad(dyq, dys, wq_t, ws, dx, stream, exact)
+    return dx
+
+
+def gemm_wgrad(dyq_t, dys_t, xq_t, xs_t, dw=None, stream=None, exact=False):
+    accumulate = dw is not None
+    if dw is None:
+        dw = torch.empty((dyq_t.shape[0], xq_t.shape[0]), dtype=torch.float32, device=dyq_t.device)
+    fp8q_gemm_wgrad(dyq_t, dys_t, xq_t, xs_t, dw, accumulate, stream, exact)
+    return dw
+
+
+def grouped_gemm(xq, xs, wq, ws, offsets, out_dtype=torch.bfloat16, stream=None, exact=False):
+    y = torch.empty((xq.shape[0], wq.shape[1]), dtype=out_dtype, device=xq.device)
+    fp8q_grouped_gemm(xq, xs, wq, ws, offsets, y, stream, exact)
+    return y

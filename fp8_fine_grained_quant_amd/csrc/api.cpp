@@ -1,0 +1,233 @@
+// C ABI of libfp8q: host-side argument validation, then the asynchronous
+// launch on the caller's stream.  Nothing here allocates, synchronises,
+// prints or throws.  The entry points and their rules are documented in
+// include/fp8q.h.
+
+#include "../../include/fp8q.h"
+#include "launch.h"
+
+#include <stdint.h>
+
+namespace {
+
+using fp8q::GemmArgs;
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+inline bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline int esize(fp8q_dtype t) { return t == FP8Q_BF16 ? 2 : 4; }
+inline bool valid_dtype(fp8q_dtype t) { return t == FP8Q_BF16 || t == FP8Q_F32; }
+inline fp8q_status launched(hipError_t e) { return e == hipSuccess ? FP8Q_OK : FP8Q_ERR_LAUNCH; }
+
+constexpr int64_t kMaxGroups = (int64_t(1) << 31) - 1;
+constexpr int64_t kMaxDim = (int64_t(1) << 31) - 1;
+
+// Checks shared by the three quantizers: input [rows, cols] with stride ld_in
+// (elements of size in_es), code output with stride ld_out bytes covering
+// out_len bytes per row, scale array of scale_rows x scale_cols with stride
+// ld_s.
+fp8q_status check_quant(const void* in, int in_es, int64_t rows, int64_t cols, int64_t ld_in,
+                        const void* out, int64_t ld_out, int64_t out_len, const float* s, int64_t ld_s,
+                        int64_t scale_cols) {
+  if (rows < 0 || cols < 0 || rows > kMaxDim || cols > kMaxDim) return FP8Q_ERR_SHAPE;
+  if (rows == 0 || cols == 0) return FP8Q_OK;
+  if (!in || !out || !s) return FP8Q_ERR_NULL;
+  if (ld_in < cols || ld_out < out_len || ld_s < scale_cols) return FP8Q_ERR_STRIDE;
+  if (!aligned16(in) || !aligned16(out) || !aligned4(s)) return FP8Q_ERR_ALIGN;
+  if ((ld_in * in_es) % 16 != 0 || ld_out % 16 != 0) return FP8Q_ERR_ALIGN;
+  return FP8Q_OK;
+}
+
+fp8q_status check_gemm_out(const void* y, fp8q_dtype yt, int64_t ld_y, int64_t ncols) {
+  if (!valid_dtype(yt)) return FP8Q_ERR_DTYPE;
+  if (!y) return FP8Q_ERR_NULL;
+  if (ld_y < ncols) return FP8Q_ERR_STRIDE;
+  if (!aligned16(y) || (ld_y * esize(yt)) % 16 != 0) return FP8Q_ERR_ALIGN;
+  return FP8Q_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* fp8q_status_string(fp8q_status s) {
+  switch (s) {
+    case FP8Q_OK: return "FP8Q_OK";
+    case FP8Q_ERR_NULL: return "FP8Q_ERR_NULL: required pointer is NULL";
+    case FP8Q_ERR_SHAPE: return "FP8Q_ERR_SHAPE: negative size or size rule broken";
+    case FP8Q_ERR_STRIDE: return "FP8Q_ERR_STRIDE: leading dimension smaller than the row length";
+    case FP8Q_ERR_ALIGN: return "FP8Q_ERR_ALIGN: pointer or row stride not aligned as required";
+    case FP8Q_ERR_DTYPE: return "FP8Q_ERR_DTYPE: unsupported element type";
+    case FP8Q_ERR_LAUNCH: return "FP8Q_ERR_LAUNCH: the HIP runtime refused a launch";
+  }
+  return "FP8Q: unknown status";
+}
+
+fp8q_status fp8q_quant_act_1x128(const void* x, fp8q_dtype xt, int64_t rows, int64_t cols, int64_t ld_x,
+                                 uint8_t* q, int64_t ld_q, float* scale, int64_t ld_s, hipStream_t stream) {
+  if (!valid_dtype(xt)) return FP8Q_ERR_DTYPE;
+  const fp8q_status c = check_quant(x, esize(xt), rows, cols, ld_x, q, ld_q, cols, scale, ld_s, cdiv(cols, 128));
+  if (c != FP8Q_OK || rows == 0 || cols == 0) return c;
+  if (rows * cdiv(cols, 128) > kMaxGroups) return FP8Q_ERR_SHAPE;
+  return launched(fp8q::launch_quant_act(x, xt == FP8Q_BF16, rows, cols, ld_x, q, ld_q, scale, ld_s, stream));
+}
+
+fp8q_status fp8q_quant_weight_128x128(const void* w, fp8q_dtype wt, int64_t rows, int64_t cols, int64_t ld_w,
+                                      uint8_t* q, int64_t ld_q, uint8_t* q_t, int64_t ld_qt,
+                                      float* scale, int64_t ld_s, hipStream_t stream) {
+  if (!valid_dtype(wt)) return FP8Q_ERR_DTYPE;
+  fp8q_status c = check_quant(w, esize(wt), rows, cols, ld_w, q, ld_q, cols, scale, ld_s, cdiv(cols, 128));
+  if (c != FP8Q_OK || rows == 0 || cols == 0) return c;
+  if (q_t) {
+    if (ld_qt < rows) return FP8Q_ERR_STRIDE;
+    if (!aligned16(q_t) || ld_qt % 16 != 0) return FP8Q_ERR_ALIGN;
+  }
+  if (cdiv(rows, 128) > 65535) return FP8Q_ERR_SHAPE;  // grid y limit
+  return launched(fp8q::launch_quant_weight(w, wt == FP8Q_BF16, rows, cols, ld_w, q, ld_q, q_t, ld_qt, scale,
+                                            ld_s, stream));
+}
+
+fp8q_status fp8q_quant_transpose(const void* x, fp8q_dtype xt, int64_t rows, int64_t cols, int64_t ld_x,
+                                 uint8_t* q_t, int64_t ld_qt, float* scale_t, int64_t ld_st, hipStream_t stream) {
+  if (!valid_dtype(xt)) return FP8Q_ERR_DTYPE;
+  const fp8q_status c =
+      check_quant(x, esize(xt), rows, cols, ld_x, q_t, ld_qt, rows, scale_t, ld_st, cdiv(rows, 128));
+  if (c != FP8Q_OK || rows == 0 || cols == 0) return c;
+  if (cdiv(rows, 128) > 65535) return FP8Q_ERR_SHAPE;
+  return launched(
+      fp8q::launch_quant_transpose(x, xt == FP8Q_BF16, rows, cols, ld_x, q_t, ld_qt, scale_t, ld_st, stream));
+}
+
+}  // extern "C"
+
+static fp8q_status fp8q_gemm_fprop_impl(int exact, const uint8_t* xq, const float* xs, const uint8_t* wq, const float* ws,
+                            int64_t M, int64_t N, int64_t K, void* y, fp8q_dtype yt, int64_t ld_y,
+                            hipStream_t stream) {
+  if (M < 0 || N < 0 || K < 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim) return FP8Q_ERR_SHAPE;
+  if (N % 128 != 0 || K % 128 != 0) return FP8Q_ERR_SHAPE;
+  if (!valid_dtype(yt)) return FP8Q_ERR_DTYPE;
+  if (M == 0 || N == 0) return FP8Q_OK;
+  if (K == 0) return FP8Q_ERR_SHAPE;  // an empty contraction would leave Y undefined
+  if (!xq || !xs || !wq || !ws) return FP8Q_ERR_NULL;
+  const fp8q_status c = check_gemm_out(y, yt, ld_y, N);
+  if (c != FP8Q_OK) return c;
+  if (!aligned16(xq) || !aligned16(wq) || !aligned4(xs) || !aligned4(ws)) return FP8Q_ERR_ALIGN;
+  GemmArgs a{};
+  a.A = xq; a.B = wq; a.sa = xs; a.sb = ws; a.C = y;
+  a.lda = K; a.ldb = K; a.ld_sa = K / 128; a.sb_rs = K / 128; a.sb_cs = 1; a.ldc = ld_y;
+  a.M = M; a.N = N; a.K = K;
+  a.sb_mode = fp8q::kSbBlock; a.out_f32 = yt == FP8Q_F32; a.accumulate = 0; a.exact = exact;
+  return launched(fp8q::launch_gemm(a, stream));
+}
+
+static fp8q_status fp8q_gemm_dgrad_impl(int exact, const uint8_t* dyq, const float* dys, const uint8_t* wq_t, const float* ws,
+                            int64_t M, int64_t N, int64_t K, void* dx, fp8q_dtype dxt, int64_t ld_dx,
+                            hipStream_t stream) {
+  if (M < 0 || N < 0 || K < 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim) return FP8Q_ERR_SHAPE;
+  if (N % 128 != 0 || K % 128 != 0) return FP8Q_ERR_SHAPE;
+  if (!valid_dtype(dxt)) return FP8Q_ERR_DTYPE;
+  if (M == 0 || K == 0) return FP8Q_OK;
+  if (N == 0) return FP8Q_ERR_SHAPE;
+  if (!dyq || !dys || !wq_t || !ws) return FP8Q_ERR_NULL;
+  const fp8q_status c = check_gemm_out(dx, dxt, ld_dx, K);
+  if (c != FP8Q_OK) return c;
+  if (!aligned16(dyq) || !aligned16(wq_t) || !aligned4(dys) || !aligned4(ws)) return FP8Q_ERR_ALIGN;
+  // NT form over the contraction axis N: A = dY [M, N], B = W^T codes [K, N];
+  // the block scale of (output column k, chunk kb over N) is ws[kb, k/128].
+  GemmArgs a{};
+  a.A = dyq; a.B = wq_t; a.sa = dys; a.sb = ws; a.C = dx;
+  a.lda = N; a.ldb = N; a.ld_sa = N / 128; a.sb_rs = 1; a.sb_cs = K / 128; a.ldc = ld_dx;
+  a.M = M; a.N = K; a.K = N;
+  a.sb_mode = fp8q::kSbBlock; a.out_f32 = dxt == FP8Q_F32; a.accumulate = 0; a.exact = exact;
+  return launched(fp8q::launch_gemm(a, stream));
+}
+
+static fp8q_status fp8q_gemm_wgrad_impl(int exact, const uint8_t* dyq_t, const float* dys_t, const uint8_t* xq_t, const float* xs_t,
+                            int64_t T, int64_t N, int64_t K, float* dw, int64_t ld_dw, int accumulate,
+                            hipStream_t stream) {
+  if (T < 0 || N < 0 || K < 0 || T > kMaxDim || N > kMaxDim || K > kMaxDim) return FP8Q_ERR_SHAPE;
+  if (T % 128 != 0 || K % 128 != 0) return FP8Q_ERR_SHAPE;
+  if (accumulate != 0 && accumulate != 1) return FP8Q_ERR_SHAPE;
+  if (N == 0 || K == 0) return FP8Q_OK;
+  if (T == 0) return FP8Q_ERR_SHAPE;
+  if (!dyq_t || !dys_t || !xq_t || !xs_t) return FP8Q_ERR_NULL;
+  const fp8q_status c = check_gemm_out(dw, FP8Q_F32, ld_dw, K);
+  if (c != FP8Q_OK) return c;
+  if (!aligned16(dyq_t) || !aligned16(xq_t) || !aligned4(dys_t) || !aligned4(xs_t)) return FP8Q_ERR_ALIGN;
+  // NT form over the tokens: A = dY^T codes [N, T], B = X^T codes [K, T], one
+  // scale per row of each per 128 tokens.
+  GemmArgs a{};
+  a.A = dyq_t; a.B = xq_t; a.sa = dys_t; a.sb = xs_t; a.C = dw;
+  a.lda = T; a.ldb = T; a.ld_sa = T / 128; a.sb_rs = T / 128; a.sb_cs = 1; a.ldc = ld_dw;
+  a.M = N; a.N = K; a.K = T;
+  a.sb_mode = fp8q::kSbRow; a.out_f32 = 1; a.accumulate = accumulate; a.exact = exact;
+  return launched(fp8q::launch_gemm(a, stream));
+}
+
+static fp8q_status fp8q_grouped_gemm_impl(int exact, const uint8_t* xq, const float* xs, const uint8_t* wq, const float* ws,
+                              const int32_t* offsets, int64_t E, int64_t M_total, int64_t N, int64_t K,
+                              void* y, fp8q_dtype yt, int64_t ld_y, hipStream_t stream) {
+  if (E < 1 || E > 65536) return FP8Q_ERR_SHAPE;
+  if (M_total < 0 || N < 0 || K < 0 || M_total > kMaxDim || N > kMaxDim || K > kMaxDim) return FP8Q_ERR_SHAPE;
+  if (N % 128 != 0 || K % 128 != 0) return FP8Q_ERR_SHAPE;
+  if (!valid_dtype(yt)) return FP8Q_ERR_DTYPE;
+  if (M_total == 0 || N == 0) return FP8Q_OK;
+  if (K == 0) return FP8Q_ERR_SHAPE;
+  if (!xq || !xs || !wq || !ws || !offsets) return FP8Q_ERR_NULL;
+  const fp8q_status c = check_gemm_out(y, yt, ld_y, N);
+  if (c != FP8Q_OK) return c;
+  if (!aligned16(xq) || !aligned16(wq) || !aligned4(xs) || !aligned4(ws) || !aligned4(offsets))
+    return FP8Q_ERR_ALIGN;
+  if ((M_total / 256 + E) * (N / 128) > kMaxGroups) return FP8Q_ERR_SHAPE;
+  GemmArgs a{};
+  a.A = xq; a.B = wq; a.sa = xs; a.sb = ws; a.C = y;
+  a.lda = K; a.ldb = K; a.ld_sa = K / 128; a.sb_rs = K / 128; a.sb_cs = 1; a.ldc = ld_y;
+  a.M = M_total; a.N = N; a.K = K;
+  a.sb_mode = fp8q::kSbBlock; a.out_f32 = yt == FP8Q_F32; a.accumulate = 0; a.exact = exact;
+  a.offsets = offsets; a.E = E; a.b_estride = N * K; a.sb_estride = (N / 128) * (K / 128);
+  return launched(fp8q::launch_gemm(a, stream));
+}
+
+
+extern "C" {
+
+fp8q_status fp8q_gemm_fprop(const uint8_t* xq, const float* xs, const uint8_t* wq, const float* ws, int64_t M,
+                            int64_t N, int64_t K, void* y, fp8q_dtype yt, int64_t ld_y, hipStream_t stream) {
+  return fp8q_gemm_fprop_impl(0, xq, xs, wq, ws, M, N, K, y, yt, ld_y, stream);
+}
+fp8q_status fp8q_gemm_fprop_exact(const uint8_t* xq, const float* xs, const uint8_t* wq, const float* ws,
+                                  int64_t M, int64_t N, int64_t K, void* y, fp8q_dtype yt, int64_t ld_y,
+                                  hipStream_t stream) {
+  return fp8q_gemm_fprop_impl(1, xq, xs, wq, ws, M, N, K, y, yt, ld_y, stream);
+}
+fp8q_status fp8q_gemm_dgrad(const uint8_t* dyq, const float* dys, const uint8_t* wq_t, const float* ws, int64_t M,
+                            int64_t N, int64_t K, void* dx, fp8q_dtype dxt, int64_t ld_dx, hipStream_t stream) {
+  return fp8q_gemm_dgrad_impl(0, dyq, dys, wq_t, ws, M, N, K, dx, dxt, ld_dx, stream);
+}
+fp8q_status fp8q_gemm_dgrad_exact(const uint8_t* dyq, const float* dys, const uint8_t* wq_t, const float* ws,
+                                  int64_t M, int64_t N, int64_t K, void* dx, fp8q_dtype dxt, int64_t ld_dx,
+                                  hipStream_t stream) {
+  return fp8q_gemm_dgrad_impl(1, dyq, dys, wq_t, ws, M, N, K, dx, dxt, ld_dx, stream);
+}
+fp8q_status fp8q_gemm_wgrad(const uint8_t* dyq_t, const float* dys_t, const uint8_t* xq_t, const float* xs_t,
+                            int64_t T, int64_t N, int64_t K, float* dw, int64_t ld_dw, int accumulate,
+                            hipStream_t stream) {
+  return fp8q_gemm_wgrad_impl(0, dyq_t, dys_t, xq_t, xs_t, T, N, K, dw, ld_dw, accumulate, stream);
+}
+fp8q_status fp8q_gemm_wgrad_exact(const uint8_t* dyq_t, const float* dys_t, const uint8_t* xq_t, const float* xs_t,
+                                  int64_t T, int64_t N, int64_t K, float* dw, int64_t ld_dw, int accumulate,
+                                  hipStream_t stream) {
+  return fp8q_gemm_wgrad_impl(1, dyq_t, dys_t, xq_t, xs_t, T, N, K, dw, ld_dw, accumulate, stream);
+}
+fp8q_status fp8q_grouped_gemm(const uint8_t* xq, const float* xs, const uint8_t* wq, const float* ws,
+                              const int32_t* offsets, int64_t E, int64_t M_total, int64_t N, int64_t K, void* y,
+                              fp8q_dtype yt, int64_t ld_y, hipStream_t stream) {
+  return fp8q_grouped_gemm_impl(0, xq, xs, wq, ws, offsets, E, M_total, N, K, y, yt, ld_y, stream);
+}
+fp8q_status fp8q_grouped_gemm_exact(const uint8_t* xq, const float* xs, const uint8_t* wq, const float* ws,
+                                    const int32_t* offsets, int64_t E, int64_t M_total, int64_t N, int64_t K,
+                                    void* y, fp8q_dtype yt, int64_t ld_y, hipStream_t stream) {
+  return fp8q_grouped_gemm_impl(1, xq, xs, wq, ws, offsets, E, M_total, N, K, y, yt, ld_y, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,48 @@
+// Host-side launchers of the HIP kernels (internal to libfp8q; the C ABI in
+// include/fp8q.h validates arguments and calls these).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp8q {
+
+hipError_t launch_quant_act(const void* x, bool x_bf16, int64_t rows, int64_t cols, int64_t ld_x,
+                            uint8_t* q, int64_t ld_q, float* s, int64_t ld_s, hipStream_t st);
+
+hipError_t launch_quant_weight(const void* w, bool w_bf16, int64_t rows, int64_t cols, int64_t ld_w,
+                               uint8_t* q, int64_t ld_q, uint8_t* q_t, int64_t ld_qt,
+                               float* s, int64_t ld_s, hipStream_t st);
+
+hipError_t launch_quant_transpose(const void* x, bool x_bf16, int64_t rows, int64_t cols, int64_t ld_x,
+                                  uint8_t* q_t, int64_t ld_qt, float* s_t, int64_t ld_st, hipStream_t st);
+
+// How the scale of the B operand (rows = output columns) is indexed.
+enum SbMode : int {
+  kSbBlock = 0,  // one scale per 128 output columns per chunk: sb[(n/128)*sb_rs + kb*sb_cs]
+  kSbRow = 1     // one scale per output column per chunk:      sb[n*sb_rs + kb]
+};
+
+// C[m, n] = sum_kb P_kb[m, n] * sa[m*ld_sa + kb] * sB(n, kb), P_kb the FP8
+// product of the 128-long chunk kb of A[m, :] and B[n, :] (both row-major
+// with the contraction axis contiguous).
+struct GemmArgs {
+  const uint8_t* A;     // [M, K] codes, row stride lda bytes
+  const uint8_t* B;     // [N, K] codes, row stride ldb bytes
+  const float* sa;      // [M, K/128]
+  const float* sb;      // see SbMode
+  void* C;              // [M, N], BF16 or FP32, row stride ldc elements
+  int64_t lda, ldb, ld_sa, sb_rs, sb_cs, ldc;
+  int64_t M, N, K;
+  int sb_mode;          // SbMode
+  int out_f32;          // 0 = BF16 output, 1 = FP32 output
+  int accumulate;       // FP32 output only: C += result
+  int exact;            // 0: FP8 MFMA per chunk; 1: exact BF16 MFMA on the converted codes
+  // grouped: rows [offsets[e], offsets[e+1]) use B + e*b_estride, sb + e*sb_estride
+  const int32_t* offsets;  // NULL for a plain GEMM
+  int64_t E, b_estride, sb_estride;
+};
+
+hipError_t launch_gemm(const GemmArgs& a, hipStream_t st);
+
+}  // namespace fp8q

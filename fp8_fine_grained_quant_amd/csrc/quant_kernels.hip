@@ -1,0 +1,300 @@
+// Online fine-grained E4M3 quantizers for gfx950.
+//
+// Group rule ("How does the unified E4M3 format contribute to the efficiency
+// of DeepSeek-V3", sections "Fine-Grained Quantization Strategy" and "Dynamic
+// Scaling and Online Quantization"; innerforce.co.kr excerpt, paragraph on
+// Figure 7 (a)): amax = max |x| over the group, s = fl32(max(amax,2^-100)/448)
+// is stored, and each element becomes E4M3(fl32(x * fl32(448/max(amax,2^-100)))),
+// round-to-nearest-even, saturating, sign of zero kept.
+//
+// All three kernels are HBM-bound streaming kernels: every input byte is read
+// once and every code/scale written once, with 16-byte loads and coalesced
+// stores; reductions stay in registers, DPP and (for cross-wave) a few bytes of
+// LDS.
+
+#include "device_common.h"
+#include "launch.h"
+
+namespace fp8q {
+
+// ---------------------------------------------------------------------------
+// 1x128 activation tiles: 16 lanes (one DPP row) own one group, 8 elements per
+// lane; a wave covers 4 consecutive groups per step and U steps, so each lane
+// keeps U 16-byte loads in flight.
+constexpr int kActU = 4;
+
+template <class In>
+__global__ __launch_bounds__(256) void k_quant_act(const typename In::elem* __restrict__ x, int64_t ld_x,
+                                                   uint8_t* __restrict__ q, int64_t ld_q,
+                                                   float* __restrict__ s, int64_t ld_s,
+                                                   int cols, int ngr, int total) {
+  const int lane = threadIdx.x & 63;
+  const int wave = (int)((blockIdx.x * (uint32_t)blockDim.x + threadIdx.x) >> 6);
+  const int team = lane >> 4, lig = lane & 15;
+  float v[kActU][8];
+  int grow[kActU], gcol[kActU];
+#pragma unroll
+  for (int u = 0; u < kActU; ++u) {
+    const int g = (wave * kActU + u) * 4 + team;
+    grow[u] = -1;
+    gcol[u] = 0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[u][e] = 0.f;
+    if (g < total) {
+      const int r = g / ngr, j = g - r * ngr;
+      const int c0 = j * 128 + lig * 8;
+      grow[u] = r;
+      gcol[u] = c0;
+      const typename In::elem* p = x + (int64_t)r * ld_x + c0;
+      if (c0 + 8 <= cols) {
+        In::load8(p, v[u]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (c0 + e < cols) v[u][e] = In::load1(p + e);
+      }
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < kActU; ++u) {
+    uint32_t m = 0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) m = max(m, abs_bits(v[u][e]));
+    m = row16_max_u32(m);  // all 16 lanes of the team share one group
+    const int r = grow[u];
+    if (r < 0) continue;
+    float sc, inv;
+    group_scale(__uint_as_float(m), sc, inv);
+    const uint32_t w0 = pack4_e4m3(v[u][0] * inv, v[u][1] * inv, v[u][2] * inv, v[u][3] * inv);
+    const uint32_t w1 = pack4_e4m3(v[u][4] * inv, v[u][5] * inv, v[u][6] * inv, v[u][7] * inv);
+    const int c0 = gcol[u];
+    uint8_t* qp = q + (int64_t)r * ld_q + c0;
+    if (c0 + 8 <= cols) {
+      *reinterpret_cast<uint2*>(qp) = make_uint2(w0, w1);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (c0 + e < cols) qp[e] = (uint8_t)(((e < 4 ? w0 : w1) >> (8 * (e & 3))) & 0xFF);
+    }
+    if (lig == 0) s[(int64_t)r * ld_s + (c0 >> 7)] = sc;
+  }
+}
+
+hipError_t launch_quant_act(const void* x, bool x_bf16, int64_t rows, int64_t cols, int64_t ld_x,
+                            uint8_t* q, int64_t ld_q, float* s, int64_t ld_s, hipStream_t st) {
+  const int64_t ngr = (cols + 127) / 128;
+  const int64_t total = rows * ngr;
+  const int64_t waves = (total + 4 * kActU - 1) / (4 * kActU);
+  const int64_t blocks = (waves + 3) / 4;
+  if (x_bf16)
+    hipLaunchKernelGGL(k_quant_act<BF16In>, dim3((uint32_t)blocks), dim3(256), 0, st,
+                       (const uint16_t*)x, ld_x, q, ld_q, s, ld_s, (int)cols, (int)ngr, (int)total);
+  else
+    hipLaunchKernelGGL(k_quant_act<F32In>, dim3((uint32_t)blocks), dim3(256), 0, st,
+                       (const float*)x, ld_x, q, ld_q, s, ld_s, (int)cols, (int)ngr, (int)total);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// 128x128 weight blocks: one workgroup per block.  Thread t owns 16
+// consecutive rows (16*(t/32) ..) of 4 consecutive columns (4*(t%32) ..), so
+// row-wise codes go out as 128-byte row segments and the transposed codes as
+// 16-byte column segments without an LDS transpose.
+template <class In>
+__device__ __forceinline__ void load4(const typename In::elem* p, float v[4]);
+template <>
+__device__ __forceinline__ void load4<F32In>(const float* p, float v[4]) {
+  float4 a = *reinterpret_cast<const float4*>(p);
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+}
+template <>
+__device__ __forceinline__ void load4<BF16In>(const uint16_t* p, float v[4]) {
+  uint2 u = *reinterpret_cast<const uint2*>(p);
+  v[0] = bf16_to_f32(u.x & 0xFFFFu); v[1] = bf16_to_f32(u.x >> 16);
+  v[2] = bf16_to_f32(u.y & 0xFFFFu); v[3] = bf16_to_f32(u.y >> 16);
+}
+
+template <class In>
+__global__ __launch_bounds__(256) void k_quant_weight(const typename In::elem* __restrict__ w, int64_t ld_w,
+                                                      int rows, int cols,
+                                                      uint8_t* __restrict__ q, int64_t ld_q,
+                                                      uint8_t* __restrict__ qt, int64_t ld_qt,
+                                                      float* __restrict__ s, int64_t ld_s) {
+  __shared__ uint32_t red[4];
+  const int t = threadIdx.x;
+  const int c4 = t & 31, rb = t >> 5;
+  const int bi = blockIdx.y, bj = blockIdx.x;
+  const int r0 = bi * 128 + rb * 16;
+  const int c0 = bj * 128 + c4 * 4;
+  const bool full_c = c0 + 4 <= cols;
+  float v[16][4];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int r = r0 + i;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[i][e] = 0.f;
+    if (r < rows) {
+      const typename In::elem* p = w + (int64_t)r * ld_w + c0;
+      if (full_c) {
+        load4<In>(p, v[i]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (c0 + e < cols) v[i][e] = In::load1(p + e);
+      }
+    }
+  }
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) m = max(m, abs_bits(v[i][e]));
+  m = wave_max_u32(m);
+  if ((t & 63) == 0) red[t >> 6] = m;
+  __syncthreads();
+  m = max(max(red[0], red[1]), max(red[2], red[3]));
+  float sc, inv;
+  group_scale(__uint_as_float(m), sc, inv);
+  if (t == 0) s[(int64_t)bi * ld_s + bj] = sc;
+
+  // row-wise codes: one dword (4 columns) per row
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int r = r0 + i;
+    if (r >= rows) break;
+    const uint32_t wd = pack4_e4m3(v[i][0] * inv, v[i][1] * inv, v[i][2] * inv, v[i][3] * inv);
+    uint8_t* qp = q + (int64_t)r * ld_q + c0;
+    if (full_c) {
+      *reinterpret_cast<uint32_t*>(qp) = wd;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (c0 + e < cols) qp[e] = (uint8_t)((wd >> (8 * e)) & 0xFF);
+    }
+  }
+  if (qt == nullptr) return;
+  // transposed codes: 16 consecutive rows of one column -> 16 bytes of q_t
+  const bool full_r = r0 + 16 <= rows;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int c = c0 + e;
+    if (c >= cols) break;
+    uint32_t d[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      d[k] = pack4_e4m3(v[4 * k][e] * inv, v[4 * k + 1][e] * inv, v[4 * k + 2][e] * inv, v[4 * k + 3][e] * inv);
+    uint8_t* tp = qt + (int64_t)c * ld_qt + r0;
+    if (full_r) {
+      *reinterpret_cast<uint4*>(tp) = make_uint4(d[0], d[1], d[2], d[3]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (r0 + i < rows) tp[i] = (uint8_t)((d[i >> 2] >> (8 * (i & 3))) & 0xFF);
+    }
+  }
+}
+
+hipError_t launch_quant_weight(const void* w, bool w_bf16, int64_t rows, int64_t cols, int64_t ld_w,
+                               uint8_t* q, int64_t ld_q, uint8_t* q_t, int64_t ld_qt,
+                               float* s, int64_t ld_s, hipStream_t st) {
+  const dim3 grid((uint32_t)((cols + 127) / 128), (uint32_t)((rows + 127) / 128));
+  if (w_bf16)
+    hipLaunchKernelGGL(k_quant_weight<BF16In>, grid, dim3(256), 0, st, (const uint16_t*)w, ld_w, (int)rows,
+                       (int)cols, q, ld_q, q_t, ld_qt, s, ld_s);
+  else
+    hipLaunchKernelGGL(k_quant_weight<F32In>, grid, dim3(256), 0, st, (const float*)w, ld_w, (int)rows,
+                       (int)cols, q, ld_q, q_t, ld_qt, s, ld_s);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Fused quantize + transpose: one workgroup per 128-token x 128-channel tile.
+// Thread t owns 8 consecutive tokens (8*(t/16) ..) of 8 consecutive channels
+// (8*(t%16) ..): loads are 16-byte row segments, the per-channel max-abs is
+// reduced over the 16 threads of a channel (xor 16/32 inside the wave, LDS
+// across the 4 waves), and each channel's 8 codes are converted pairwise
+// down the column, so they leave as one 8-byte segment of the q_t row.
+template <class In>
+__global__ __launch_bounds__(256) void k_quant_transpose(const typename In::elem* __restrict__ x, int64_t ld_x,
+                                                         int rows, int cols,
+                                                         uint8_t* __restrict__ qt, int64_t ld_qt,
+                                                         float* __restrict__ st, int64_t ld_st) {
+  __shared__ uint32_t red[4][128];
+  const int t = threadIdx.x;
+  const int c8 = t & 15, rblk = t >> 4;
+  const int bi = blockIdx.y, bj = blockIdx.x;
+  const int r0 = bi * 128 + rblk * 8;
+  const int c0 = bj * 128 + c8 * 8;
+  float v[8][8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int r = r0 + i;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[i][e] = 0.f;
+    if (r < rows) {
+      const typename In::elem* p = x + (int64_t)r * ld_x + c0;
+      if (c0 + 8 <= cols) {
+        In::load8(p, v[i]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (c0 + e < cols) v[i][e] = In::load1(p + e);
+      }
+    }
+  }
+  uint32_t m[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    uint32_t a = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) a = max(a, abs_bits(v[i][e]));
+    a = max(a, (uint32_t)__shfl_xor((int)a, 16));
+    a = max(a, (uint32_t)__shfl_xor((int)a, 32));
+    m[e] = a;
+  }
+  const int wv = t >> 6;
+  if ((t & 63) < 16) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) red[wv][c8 * 8 + e] = m[e];
+  }
+  __syncthreads();
+  float inv[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int cl = c8 * 8 + e;
+    const uint32_t a = max(max(red[0][cl], red[1][cl]), max(red[2][cl], red[3][cl]));
+    float sc;
+    group_scale(__uint_as_float(a), sc, inv[e]);
+    if (rblk == 0 && c0 + e < cols) st[(int64_t)(c0 + e) * ld_st + bi] = sc;
+  }
+  const bool full_r = r0 + 8 <= rows;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int c = c0 + e;
+    if (c >= cols) break;
+    const uint32_t d0 = pack4_e4m3(v[0][e] * inv[e], v[1][e] * inv[e], v[2][e] * inv[e], v[3][e] * inv[e]);
+    const uint32_t d1 = pack4_e4m3(v[4][e] * inv[e], v[5][e] * inv[e], v[6][e] * inv[e], v[7][e] * inv[e]);
+    uint8_t* tp = qt + (int64_t)c * ld_qt + r0;
+    if (full_r) {
+      *reinterpret_cast<uint2*>(tp) = make_uint2(d0, d1);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        if (r0 + i < rows) tp[i] = (uint8_t)((((i < 4) ? d0 : d1) >> (8 * (i & 3))) & 0xFF);
+    }
+  }
+}
+
+hipError_t launch_quant_transpose(const void* x, bool x_bf16, int64_t rows, int64_t cols, int64_t ld_x,
+                                  uint8_t* q_t, int64_t ld_qt, float* s_t, int64_t ld_st, hipStream_t st) {
+  const dim3 grid((uint32_t)((cols + 127) / 128), (uint32_t)((rows + 127) / 128));
+  if (x_bf16)
+    hipLaunchKernelGGL(k_quant_transpose<BF16In>, grid, dim3(256), 0, st, (const uint16_t*)x, ld_x, (int)rows,
+                       (int)cols, q_t, ld_qt, s_t, ld_st);
+  else
+    hipLaunchKernelGGL(k_quant_transpose<F32In>, grid, dim3(256), 0, st, (const float*)x, ld_x, (int)rows,
+                       (int)cols, q_t, ld_qt, s_t, ld_st);
+  return hipGetLastError();
+}
+
+}  // namespace fp8q

@@ -1,0 +1,207 @@
+/*
+ * fp8q -- fine-grained E4M3 quantization and the block-scaled FP8 GEMM that
+ * consumes it, for AMD Instinct MI355X (gfx950).
+ *
+ * The method (sources are cited by page title and section):
+ *   - "How does the unified E4M3 format contribute to the efficiency of
+ *     DeepSeek-V3" (codingmall.com), "Fine-Grained Quantization Strategy":
+ *     one E4M3 format for every tensor; activations scaled per 1x128 tile,
+ *     weights per 128x128 block.  "Dynamic Scaling and Online Quantization":
+ *     each scale is computed from the group's current values.  "Enhanced
+ *     Numerical Stability": FP8 partial results are promoted to FP32 at
+ *     intervals during accumulation.
+ *   - The innerforce.co.kr excerpt of the DeepSeek-V3 report, paragraph on
+ *     Figure 7 (a): a group's max-abs is mapped to the largest FP8 value;
+ *     1x128 = per token per 128 channels, 128x128 = per 128 input channels
+ *     per 128 output channels.  The next paragraph: dequantization is folded
+ *     into the FP32 accumulation of the GEMM.
+ *   - "DeepSeek FP8 Training" (arcalunar.github.io), the Fprop pipeline, the
+ *     weight-gradient list and the input-gradient list: the three products
+ *     and their output precisions (BF16 Y and dX, FP32 dW).
+ *
+ * Numeric conventions (the pages leave these open; the readings taken):
+ *   amax' = max(amax, 2^-100); scale s = fl32(amax'/448) is stored; codes are
+ *   E4M3FN(fl32(x * fl32(448/amax'))) with round-to-nearest-even, saturation
+ *   to +-448 and the sign of zero kept.  Dequantized value = decode(q) * s.
+ *   GEMM: for every 128-long chunk kb of the contraction axis an FP8 matrix-
+ *   core partial P is formed and added as acc += P * sA(row,kb) * sB(col,kb)
+ *   into FP32 registers; the result is stored as BF16 (round-to-nearest-even)
+ *   or FP32.  Accuracy of the FP8 variants: within each group of 8 consecutive
+ *   K of a chunk the matrix instruction keeps 14 bits below the largest
+ *   product's exponent (truncating), so |C - exact| <= 2^-10 * sum|a*b| plus
+ *   FP32 rounding; the _exact variants (end of this file) stay within FP32
+ *   rounding of the exact contraction.
+ *
+ * Conventions of every entry point:
+ *   - All pointers are DEVICE pointers owned by the caller.  The library
+ *     allocates nothing, keeps no pointer after returning and has no global
+ *     state: calls are re-entrant and thread-safe.  Buffers must stay valid
+ *     until the work enqueued on `stream` has completed.
+ *   - Work is enqueued asynchronously on `stream` (NULL = the default
+ *     stream).  Results are deterministic (no atomics, no split-K).
+ *   - Arguments are validated on the host before anything is enqueued; a bad
+ *     argument returns its status and enqueues nothing.  A zero-size call is
+ *     a no-op returning FP8Q_OK.  A launch failure reported by the HIP runtime
+ *     returns FP8Q_ERR_LAUNCH.  No exception crosses this interface and the
+ *     library never aborts or prints.
+ *   - Matrices are row-major; `ld_*` is the distance between rows in
+ *     ELEMENTS of that matrix.  Quantizer inputs and code outputs must start on
+ *     16-byte boundaries and have row strides that are multiples of 16 bytes
+ *     (vector access), else FP8Q_ERR_ALIGN.  Scale arrays need 4-byte alignment.
+ *   - Inputs must be finite; NaN or Inf inputs give unspecified codes.
+ *   - Work is sized for one GPU's share; every size must fit in int64 and the
+ *     number of 128-groups of one call must stay below 2^31.
+ */
+#ifndef FP8Q_H
+#define FP8Q_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FP8Q_OK = 0,
+  FP8Q_ERR_NULL = 1,   /* a required pointer is NULL while its size is non-zero */
+  FP8Q_ERR_SHAPE = 2,  /* negative size, or a size rule of the entry point broken */
+  FP8Q_ERR_STRIDE = 3, /* a leading dimension smaller than the row length */
+  FP8Q_ERR_ALIGN = 4,  /* pointer or row stride not aligned as required */
+  FP8Q_ERR_DTYPE = 5,  /* unsupported element type */
+  FP8Q_ERR_LAUNCH = 6  /* the HIP runtime refused a launch */
+} fp8q_status;
+
+typedef enum { FP8Q_BF16 = 0, FP8Q_F32 = 1 } fp8q_dtype;
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char* fp8q_status_string(fp8q_status s);
+
+/*
+ * 1x128 activation quantization ("unified E4M3" page, "Fine-Grained
+ * Quantization Strategy"; innerforce.co.kr excerpt, Figure 7 (a) item (1)).
+ *   x     : [rows, cols] BF16 or FP32 (xt), row stride ld_x >= cols elements
+ *   q     : [rows, cols] E4M3 codes (uint8), row stride ld_q >= cols bytes
+ *   scale : [rows, ceil(cols/128)] FP32, row stride ld_s >= ceil(cols/128)
+ * Group (r, j) = x[r, 128j : min(128j+128, cols)); a trailing partial group
+ * uses only the elements present.  Any rows, cols >= 0.
+ */
+fp8q_status fp8q_quant_act_1x128(const void* x, fp8q_dtype xt, int64_t rows, int64_t cols, int64_t ld_x,
+                                 uint8_t* q, int64_t ld_q, float* scale, int64_t ld_s, hipStream_t stream);
+
+/*
+ * 128x128 weight quantization (same page and section; innerforce.co.kr
+ * excerpt, Figure 7 (a) item (2)).
+ *   w     : [rows, cols] FP32 (master weights) or BF16 (wt), stride ld_w
+ *   q     : [rows, cols] E4M3 codes, stride ld_q
+ *   q_t   : optional [cols, rows] E4M3 codes, the exact transpose of q
+ *           (stride ld_qt >= rows), or NULL to skip.  A block's scale does not
+ *           change under transposition, so q_t with the same scale array is
+ *           the weight operand of the input-gradient GEMM.
+ *   scale : [ceil(rows/128), ceil(cols/128)] FP32, stride ld_s
+ * Block (i, j) = rows [128i, 128i+128) x cols [128j, 128j+128), clipped.
+ */
+fp8q_status fp8q_quant_weight_128x128(const void* w, fp8q_dtype wt, int64_t rows, int64_t cols, int64_t ld_w,
+                                      uint8_t* q, int64_t ld_q, uint8_t* q_t, int64_t ld_qt,
+                                      float* scale, int64_t ld_s, hipStream_t stream);
+
+/*
+ * Fused quantize + transpose for the weight-gradient operands ("DeepSeek FP8
+ * Training", weight-gradient list: both dY and the activation are quantized
+ * for the Wgrad GEMM).  The 1x128 rule applied to x^T: a group is 128
+ * consecutive rows (tokens) of one column (channel).
+ *   x       : [rows, cols] BF16 or FP32, stride ld_x
+ *   q_t     : [cols, rows] E4M3 codes, q_t[c, r] = code of x[r, c]; stride ld_qt >= rows
+ *   scale_t : [cols, ceil(rows/128)] FP32, stride ld_st
+ * The result equals fp8q_quant_act_1x128 applied to the transposed matrix.
+ */
+fp8q_status fp8q_quant_transpose(const void* x, fp8q_dtype xt, int64_t rows, int64_t cols, int64_t ld_x,
+                                 uint8_t* q_t, int64_t ld_qt, float* scale_t, int64_t ld_st, hipStream_t stream);
+
+/*
+ * Fprop: Y[M,N] = X[M,K] . W[N,K]^T ("DeepSeek FP8 Training", Fprop pipeline:
+ * FP8 GEMM with FP32 accumulation, result stored as BF16).
+ *   xq : [M, K] codes, contiguous;  xs : [M, K/128] FP32, contiguous
+ *   wq : [N, K] codes, contiguous;  ws : [N/128, K/128] FP32, contiguous
+ *   y  : [M, N] of type yt (BF16 or FP32), row stride ld_y >= N elements,
+ *        ld_y * element size a multiple of 16 bytes, y 16-byte aligned
+ * Rules: K % 128 == 0, N % 128 == 0, any M >= 0; xq, wq 16-byte aligned.
+ */
+fp8q_status fp8q_gemm_fprop(const uint8_t* xq, const float* xs, const uint8_t* wq, const float* ws,
+                            int64_t M, int64_t N, int64_t K, void* y, fp8q_dtype yt, int64_t ld_y,
+                            hipStream_t stream);
+
+/*
+ * Dgrad: dX[M,K] = dY[M,N] . W[N,K] ("DeepSeek FP8 Training", input-gradient
+ * list: FP8 weight and FP8 output gradient, FP32 accumulation, BF16 dX).
+ *   dyq  : [M, N] codes (1x128 groups along N), dys : [M, N/128] FP32
+ *   wq_t : [K, N] codes = the q_t output of fp8q_quant_weight_128x128
+ *   ws   : the SAME [N/128, K/128] block-scale array of that call
+ *   dx   : [M, K] of type dxt, row stride ld_dx (rules as y above)
+ * Rules: N % 128 == 0 (contraction), K % 128 == 0, any M >= 0.
+ */
+fp8q_status fp8q_gemm_dgrad(const uint8_t* dyq, const float* dys, const uint8_t* wq_t, const float* ws,
+                            int64_t M, int64_t N, int64_t K, void* dx, fp8q_dtype dxt, int64_t ld_dx,
+                            hipStream_t stream);
+
+/*
+ * Wgrad: dW[N,K] (= or +=) dY^T . X over T tokens ("DeepSeek FP8 Training",
+ * weight-gradient list: FP32 accumulation, dW stored in FP32).
+ *   dyq_t : [N, T] codes, dys_t : [N, T/128]  (fp8q_quant_transpose of dY[T,N])
+ *   xq_t  : [K, T] codes, xs_t  : [K, T/128]  (fp8q_quant_transpose of X[T,K])
+ *   dw    : [N, K] FP32, row stride ld_dw (multiple of 4 elements)
+ *   accumulate : 0 stores the product, 1 adds it to dw
+ * Rules: T % 128 == 0, K % 128 == 0, any N >= 0.
+ */
+fp8q_status fp8q_gemm_wgrad(const uint8_t* dyq_t, const float* dys_t, const uint8_t* xq_t, const float* xs_t,
+                            int64_t T, int64_t N, int64_t K, float* dw, int64_t ld_dw, int accumulate,
+                            hipStream_t stream);
+
+/*
+ * Grouped (MoE) Fprop: for every expert e, rows [o_e, o_{e+1}) of Y are
+ * X[o_e:o_{e+1}, :] . W_e^T (the FP8 GEMMs of MoE layers; the expert layout
+ * is this library's own, the pages give no grouped algorithm).
+ *   xq : [M_total, K] codes, xs : [M_total, K/128]
+ *   wq : [E, N, K] codes,    ws : [E, N/128, K/128]
+ *   offsets : DEVICE int32 [E+1]; offsets[0] = 0, non-decreasing,
+ *             offsets[E] = M_total (not checked on the host: it stays on the
+ *             device; malformed offsets are undefined behaviour)
+ *   y  : [M_total, N] of type yt, row stride ld_y
+ * Rules: K % 128 == 0, N % 128 == 0, 1 <= E <= 65536, any M_total >= 0.
+ * Experts with no rows are skipped; no host synchronisation happens.
+ */
+fp8q_status fp8q_grouped_gemm(const uint8_t* xq, const float* xs, const uint8_t* wq, const float* ws,
+                              const int32_t* offsets, int64_t E, int64_t M_total, int64_t N, int64_t K,
+                              void* y, fp8q_dtype yt, int64_t ld_y, hipStream_t stream);
+
+/*
+ * Exact-accumulation variants.  Same arguments, rules, layouts and results
+ * definition as the four GEMMs above; only the in-chunk arithmetic differs.
+ * gfx950's FP8 matrix instruction adds the 8 products of each group of 8
+ * consecutive K after aligning them to the largest one and truncating the
+ * others 13 bits below its exponent (the counterpart of the limited FP8 tensor-
+ * core accumulation the innerforce.co.kr excerpt reports for H800, paragraph
+ * after Figure 7 (a)).  These variants convert every code exactly to BF16 and
+ * use the BF16 matrix instruction, whose products are exact and whose sums are
+ * FP32, then promote every 128-K chunk exactly like the FP8 variants.  They
+ * run at the BF16 matrix rate (half the FP8 rate) and serve callers who need
+ * the result within 1e-5 * sum|a*b| of the exact contraction.
+ */
+fp8q_status fp8q_gemm_fprop_exact(const uint8_t* xq, const float* xs, const uint8_t* wq, const float* ws,
+                                  int64_t M, int64_t N, int64_t K, void* y, fp8q_dtype yt, int64_t ld_y,
+                                  hipStream_t stream);
+fp8q_status fp8q_gemm_dgrad_exact(const uint8_t* dyq, const float* dys, const uint8_t* wq_t, const float* ws,
+                                  int64_t M, int64_t N, int64_t K, void* dx, fp8q_dtype dxt, int64_t ld_dx,
+                                  hipStream_t stream);
+fp8q_status fp8q_gemm_wgrad_exact(const uint8_t* dyq_t, const float* dys_t, const uint8_t* xq_t,
+                                  const float* xs_t, int64_t T, int64_t N, int64_t K, float* dw, int64_t ld_dw,
+                                  int accumulate, hipStream_t stream);
+fp8q_status fp8q_grouped_gemm_exact(const uint8_t* xq, const float* xs, const uint8_t* wq, const float* ws,
+                                    const int32_t* offsets, int64_t E, int64_t M_total, int64_t N, int64_t K,
+                                    void* y, fp8q_dtype yt, int64_t ld_y, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP8Q_H */

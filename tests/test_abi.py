@@ -1,0 +1,103 @@
+"""C-ABI checks that need no GPU: the library loads, exports every entry point
+the header declares, and rejects bad arguments on the host (validation happens
+before any launch, so these calls never reach the device)."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import fp8_fine_grained_quant_amd as fq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp8q.h")
+
+OK, NULL, SHAPE, STRIDE, ALIGN, DTYPE = 0, 1, 2, 3, 4, 5
+A16 = 1 << 20          # a fake, 16-byte-aligned address (never dereferenced)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(fp8q_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(fq.LIB_PATH):
+        pytest.fail("libfp8q.so is not built: run __graft_entry__.build()")
+    return fq.load_library()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert set(names) == set(fq.EXPORTS)
+    out = subprocess.run(["nm", "-D", "--defined-only", fq.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (fp8q_\w+)", out))
+    for n in names:
+        assert n in exported, n
+        assert getattr(lib, n) is not None
+
+
+def test_status_strings(lib):
+    for code, name in enumerate(fq._STATUS):
+        assert fq.status_string(code).startswith(name)
+    assert "unknown" in fq.status_string(99)
+
+
+def test_quantizer_argument_errors(lib):
+    f = lib.fp8q_quant_act_1x128
+    assert f(A16, 0, -1, 128, 128, A16, 128, A16, 1, None) == SHAPE
+    assert f(A16, 7, 4, 128, 128, A16, 128, A16, 1, None) == DTYPE
+    assert f(None, 0, 4, 128, 128, A16, 128, A16, 1, None) == NULL
+    assert f(A16, 0, 4, 128, 100, A16, 128, A16, 1, None) == STRIDE       # ld_x < cols
+    assert f(A16, 0, 4, 128, 128, A16, 128, A16, 0, None) == STRIDE       # ld_s < groups
+    assert f(A16 + 2, 0, 4, 128, 128, A16, 128, A16, 1, None) == ALIGN
+    assert f(A16, 0, 4, 100, 100, A16, 112, A16, 1, None) == ALIGN        # 200-byte rows
+    assert f(A16, 0, 0, 128, 128, None, 128, None, 1, None) == OK         # empty: no-op
+    g = lib.fp8q_quant_weight_128x128
+    assert g(A16, 1, 256, 256, 256, A16, 256, A16, 100, A16, 2, None) == STRIDE  # ld_qt < rows
+    assert g(A16, 1, 256, 256, 256, A16, 256, A16 + 4, 256, A16, 2, None) == ALIGN
+    assert g(A16, 1, 256, 256, 256, A16, 256, None, 0, A16, 1, None) == STRIDE   # ld_s < 2
+    h = lib.fp8q_quant_transpose
+    assert h(A16, 0, 300, 64, 64, A16, 256, A16, 3, None) == STRIDE      # ld_qt < rows
+    assert h(A16, 0, 300, 64, 64, A16, 304, A16, 2, None) == STRIDE      # ld_st < 3
+
+
+def test_gemm_argument_errors(lib):
+    fp = lib.fp8q_gemm_fprop
+    assert fp(A16, A16, A16, A16, 64, 128, 200, A16, 0, 128, None) == SHAPE  # K % 128
+    assert fp(A16, A16, A16, A16, 64, 100, 256, A16, 0, 128, None) == SHAPE  # N % 128
+    assert fp(A16, A16, A16, A16, 64, 128, 256, A16, 3, 128, None) == DTYPE
+    assert fp(A16, None, A16, A16, 64, 128, 256, A16, 0, 128, None) == NULL
+    assert fp(A16, A16, A16, A16, 64, 128, 256, A16, 0, 120, None) == STRIDE
+    assert fp(A16, A16, A16, A16, 64, 128, 256, A16, 0, 132, None) == ALIGN  # 264-byte rows
+    assert fp(A16 + 8, A16, A16, A16, 64, 128, 256, A16, 0, 128, None) == ALIGN
+    assert fp(A16, A16, A16, A16, 0, 128, 256, None, 0, 128, None) == OK     # M = 0
+    dg = lib.fp8q_gemm_dgrad
+    assert dg(A16, A16, A16, A16, 64, 200, 256, A16, 0, 256, None) == SHAPE  # contraction % 128
+    wg = lib.fp8q_gemm_wgrad
+    assert wg(A16, A16, A16, A16, 200, 64, 256, A16, 256, 0, None) == SHAPE  # T % 128
+    assert wg(A16, A16, A16, A16, 256, 64, 256, A16, 256, 2, None) == SHAPE  # accumulate flag
+    assert wg(A16, A16, A16, A16, 256, 64, 256, A16, 254, 0, None) == STRIDE
+    gg = lib.fp8q_grouped_gemm
+    assert gg(A16, A16, A16, A16, A16, 0, 64, 128, 256, A16, 0, 128, None) == SHAPE  # E = 0
+    assert gg(A16, A16, A16, A16, None, 4, 64, 128, 256, A16, 0, 128, None) == NULL
+    assert gg(A16, A16, A16, A16, A16 + 2, 4, 64, 128, 256, A16, 0, 128, None) == ALIGN
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    x = torch.zeros(4, 128, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        fq.quant_act_1x128(x)
+
+
+def test_header_compiles_as_c(tmp_path):
+    src = tmp_path / "t.c"
+    src.write_text('#include "fp8q.h"\nint main(void){ return (int)FP8Q_OK; }\n')
+    res = subprocess.run(["gcc", "-std=c99", "-fsyntax-only", "-I", os.path.join(ROOT, "include"),
+                          "-I", "/opt/rocm/include", "-D__HIP_PLATFORM_AMD__", str(src)],
+                         capture_output=True, text=True)
+    assert res.returncode == 0, res.stderr
