@@ -23,6 +23,8 @@ FLAGS = [
     f"--offload-arch={ARCH}",
     "-fhip-fp32-correctly-rounded-divide-sqrt",
     "-fno-gpu-flush-denormals-to-zero",
+    # private staging arrays must stay in registers, never in LDS
+    "-mllvm", "-disable-promote-alloca-to-lds",
     "-ffp-contract=off",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function",

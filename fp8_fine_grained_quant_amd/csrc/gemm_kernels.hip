@@ -13,15 +13,18 @@
 // one promotion interval), and the scale-and-add runs as FP32 FMAs on the
 // vector ALU into accumulators kept in architectural VGPRs.
 //
-// Tiling (MI355X-first: 256 CUs, 64-wide waves, 160 KB LDS per CU):
-//   * workgroup tile 256 x 128, 512 threads = 8 waves in a 4 x 2 grid, each
-//     wave 64 x 64 (4 x 4 MFMA sub-tiles, 64 FP32 accumulators per lane);
-//     two waves per SIMD so one wave's promotion FMAs issue under the other's
-//     MFMAs;
-//   * B (the operand every wave of a column shares) is staged through a
-//     double-buffered LDS tile with a 144-byte row pitch (conflict-free 16-byte
-//     reads across 16 rows); A goes from global memory straight into the MFMA
-//     register layout, one chunk ahead;
+// Tiling (MI355X-first: 256 CUs, 64-wide waves, 160 KB LDS per CU), set by a
+// compile-time configuration (waves in M x N, MFMA sub-tiles per wave):
+//   * default workgroup tile 256 x 128 with 4 waves, one per SIMD, each wave a
+//     64 x 128 strip (4 x 8 MFMA sub-tiles, 128 FP32 accumulators per lane in
+//     architectural VGPRs, which leaves room for double-buffered operands and
+//     MFMA results so a wave's promotion FMAs issue under its next MFMAs);
+//   * B (the operand every wave shares) is staged through a double-buffered
+//     LDS tile with a 144-byte row pitch (conflict-free 16-byte reads across
+//     16 rows); A, private to a wave, goes from global memory straight into
+//     the MFMA register layout one chunk ahead;
+//   * the main loop is branch-free (clamped addresses instead of conditional
+//     loads) so the compiler's wait counts only cover the chunk in use;
 //   * the chunk's A-row scales (and per-column B scales for Wgrad) are staged
 //     in LDS beside the tile;
 //   * the epilogue stages the tile through LDS so every global store is a full
@@ -54,26 +57,52 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 
-constexpr int BM = 256, BN = 128, BK = 128;
-constexpr int NWAVES = 8, NTHREADS = 512;
-constexpr int WM = 64, WN = 64;      // wave tile
-constexpr int BPITCH = 144;          // LDS row pitch of the B tile (bytes)
-constexpr int GROUP_M = 4;           // m-tiles per band in the tile order
+constexpr int BK = 128;          // one chunk = one promotion interval
+constexpr int BPITCH_X = 272;    // LDS row pitch of the BF16 B tile (exact variant)
+[[maybe_unused]] constexpr int GROUP_M = 4;  // m-tiles per band in the tile order
 
-constexpr int BPITCH_X = BK * 2 + 16;  // row pitch of the BF16 B tile (exact variant)
+// Tile configuration: WAVES_M x WAVES_N waves, each TM x TN MFMA sub-tiles of 16 x 16.
+template <int WAVES_M_, int WAVES_N_, int TM_, int TN_>
+struct Cfg {
+  static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_, TM = TM_, TN = TN_;
+  static constexpr int NWAVES = WAVES_M * WAVES_N, NT = 64 * NWAVES;
+  static constexpr int WM = 16 * TM, WN = 16 * TN;
+  static constexpr int BM = WAVES_M * WM, BN = WAVES_N * WN;
+  static_assert(NT >= BM, "one A-scale load per thread");
+  static_assert(NT >= BN, "one B-scale load per thread");
+  static_assert((BN * 8) % NT == 0, "B tile loads split evenly");
+  static_assert(BN <= 128 && 128 % BN == 0, "a tile's columns share one 128-block");
+};
 
-constexpr int kEpiPitchBF16 = WN * 2 + 16;              // 144
-constexpr int kEpiPitchF32 = WN * 4 + 16;               // 272
+#ifndef FP8Q_GEMM_CFG
+#define FP8Q_GEMM_CFG 1
+#endif
+#if FP8Q_GEMM_CFG == 0
+typedef Cfg<4, 2, 4, 4> DefaultCfg;   // 256 x 128, 8 waves of 64 x 64
+#elif FP8Q_GEMM_CFG == 1
+typedef Cfg<4, 1, 4, 8> DefaultCfg;   // 256 x 128, 4 waves of 64 x 128
+#elif FP8Q_GEMM_CFG == 2
+typedef Cfg<2, 2, 8, 4> DefaultCfg;   // 256 x 128, 4 waves of 128 x 64
+#elif FP8Q_GEMM_CFG == 3
+typedef Cfg<2, 1, 8, 8> DefaultCfg;   // 256 x 128, 2 waves of 128 x 128
+#endif
 
-template <int OUT_F32, bool EXACT>
+// LDS of one workgroup.  Each pipeline stage has its own arrays (B tile, A
+// scales, B scales) so the compiler can tell a stage being read from the one
+// being filled by direct loads and does not wait for the latter; the epilogue
+// has its own staging area (FP32 tiles go out in two passes of half the rows).
+template <class C, int OUT_F32, bool EXACT>
 struct Lds {
-  static constexpr int stage_b = BN * (EXACT ? BPITCH_X : BPITCH);
-  static constexpr int b = 2 * stage_b;
-  static constexpr int sa = 2 * BM * 4;
-  static constexpr int sb = 2 * BN * 4;
-  static constexpr int main = b + sa + sb;
-  static constexpr int epi = NWAVES * WM * (OUT_F32 ? kEpiPitchF32 : kEpiPitchBF16);
-  static constexpr int total = epi > main ? epi : main;
+  // FP8 tiles arrive by direct global->LDS loads: 128-byte rows, 16-byte
+  // chunks XOR-swizzled by (row & 7); BF16 tiles (exact variant) are written
+  // from registers with a padded pitch.
+  static constexpr int stage_b = C::BN * (EXACT ? BPITCH_X : BK);
+  static constexpr int epi_pitch = C::WN * (OUT_F32 ? 4 : 2) + 16;
+  static constexpr int epi_passes = OUT_F32 ? 2 : 1;
+  static constexpr int epi_rows = C::WM / epi_passes;
+  static constexpr int epi = C::NWAVES * epi_rows * epi_pitch;
+  static constexpr int total = 2 * stage_b + 2 * 4 * (C::BM + 4) + 2 * 4 * (C::BN + 4) + epi;
+  static_assert(total <= 160 * 1024, "LDS budget of one CU");
 };
 
 // 8 E4M3 codes (two dwords) -> 8 BF16 values, exactly (scale 1.0).
@@ -95,18 +124,27 @@ __device__ __forceinline__ v8i make_frag(uint4 lo, uint4 hi) {
   return f;
 }
 
-template <int SB_MODE, int OUT_F32, bool GROUPED, bool EXACT>
-__global__ __launch_bounds__(NTHREADS) void k_gemm(GemmArgs p) {
-  typedef Lds<OUT_F32, EXACT> L;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[L::total];
-  uint8_t* ldsB = lds;
-  float* ldsSa = reinterpret_cast<float*>(lds + L::b);
-  float* ldsSb = reinterpret_cast<float*>(lds + L::b + L::sa);
-  constexpr int kPitchB = EXACT ? BPITCH_X : BPITCH;
+template <class C, int SB_MODE, int OUT_F32, bool GROUPED, bool EXACT>
+__global__ __launch_bounds__(C::NT) void k_gemm(GemmArgs p) {
+#if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
+  constexpr int BM = C::BM, BN = C::BN, WM = C::WM, WN = C::WN, TM = C::TM, TN = C::TN, NT = C::NT;
+  constexpr int UB = BN * 8 / NT;  // 16-byte B units per thread per chunk
+  typedef Lds<C, OUT_F32, EXACT> L;
+  __shared__ __attribute__((aligned(16))) uint8_t ldsB0[L::stage_b];
+  __shared__ __attribute__((aligned(16))) uint8_t ldsB1[L::stage_b];
+  __shared__ __attribute__((aligned(16))) float ldsSa0[BM + 4];  // [BM]: parking slot
+  __shared__ __attribute__((aligned(16))) float ldsSa1[BM + 4];
+  __shared__ __attribute__((aligned(16))) float ldsSb0[BN + 4];
+  __shared__ __attribute__((aligned(16))) float ldsSb1[BN + 4];
+  __shared__ __attribute__((aligned(16))) uint8_t ldsE[L::epi];
+  auto stB = [&](int stage) { return stage ? ldsB1 : ldsB0; };
+  auto stSa = [&](int stage) { return stage ? ldsSa1 : ldsSa0; };
+  auto stSb = [&](int stage) { return stage ? ldsSb1 : ldsSb0; };
+  constexpr int kPitchB = EXACT ? BPITCH_X : BK;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
-  const int wm = w >> 1, wn = w & 1;
+  const int wm = w / C::WAVES_N, wn = w % C::WAVES_N;
   const int l16 = lane & 15, g = lane >> 4;
 
   // ---- which output tile: XCD-aware renumbering of the workgroup id
@@ -157,80 +195,114 @@ __global__ __launch_bounds__(NTHREADS) void k_gemm(GemmArgs p) {
 
   // ---- per-lane A row pointers (rows beyond the tile's end are clamped to the
   // last valid row: they are loaded but never stored)
-  const uint8_t* pa[4];
+  const uint8_t* pa[TM];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < TM; ++i) {
     int64_t row = m0 + wm * WM + 16 * i + l16;
     row = row < mend ? row : mend - 1;
     pa[i] = p.A + row * p.lda + 16 * g;
   }
-  // ---- B loader: thread -> (row, 16-byte column chunk), two rows 64 apart
-  const int bl_row = tid >> 3, bl_c = tid & 7;
-  const uint8_t* pb0 = B + (int64_t)(n0 + bl_row) * p.ldb + 16 * bl_c;
-  const uint8_t* pb1 = pb0 + 64 * p.ldb;
-  const int lds_b0 = bl_row * kPitchB + (EXACT ? 32 : 16) * bl_c;
-  const int lds_b1 = lds_b0 + 64 * kPitchB;
-  // ---- scale loaders
-  const float* psa = nullptr;
-  if (tid < BM) {
-    int64_t row = m0 + tid;
-    row = row < mend ? row : mend - 1;
-    psa = p.sa + row * p.ld_sa;
+  // ---- B loader.  FP8 path: direct global->LDS (no registers): wave w's
+  // q-th 16-byte load lands at LDS unit (w*IB + q)*64 + lane, i.e. row
+  // unit/8, physical chunk lane%8, which holds logical chunk (lane%8)^(row&7).
+  // Exact path: unit u = tid + NT*q -> (row u/8, chunk u%8) through registers.
+  constexpr int IB = BN / (8 * C::NWAVES);   // DMA instructions per wave per chunk
+  const uint8_t* pb[UB];
+  int lds_b[UB];
+#pragma unroll
+  for (int q = 0; q < UB; ++q) {
+    if (EXACT) {
+      const int u = tid + NT * q, row = u >> 3, c = u & 7;
+      pb[q] = B + (int64_t)(n0 + row) * p.ldb + 16 * c;
+      lds_b[q] = row * kPitchB + 32 * c;
+    } else if (q < IB) {
+      const int row = (w * IB + q) * 8 + (lane >> 3);
+      const int c = (lane & 7) ^ (row & 7);
+      pb[q] = B + (int64_t)(n0 + row) * p.ldb + 16 * c;
+      lds_b[q] = (w * IB + q) * 1024;      // wave-uniform LDS base of the instruction
+    }
   }
-  const float* psb_row = nullptr;
-  if (SB_MODE == kSbRow && tid >= BM && tid < BM + BN) psb_row = sb + (int64_t)(n0 + tid - BM) * p.sb_rs;
+  // ---- scale loaders.  Every thread issues the same loads (threads without a
+  // scale of their own read a clamped, valid address and park the value in a
+  // spare LDS slot), so the main loop has no divergent branches and the
+  // compiler can track the prefetch loads across iterations.  FP8 path: the
+  // A scales go global->LDS with 4-byte direct loads, one per lane, by the
+  // first BM/64 waves.
+  int64_t sa_row = m0 + (EXACT ? (tid & (BM - 1)) : ((w * 64 + lane) & (BM - 1)));
+  sa_row = sa_row < mend ? sa_row : mend - 1;
+  const float* psa = p.sa + sa_row * p.ld_sa;
+  const int lds_sa_slot = tid < BM ? tid : BM;  // BM: parking slot (never read)
+  const float* psb_row = sb + (int64_t)(n0 + (tid & (BN - 1))) * p.sb_rs;
+  const int lds_sb_slot = tid < BN ? tid : BN;
   const float* psb_blk = sb + (int64_t)(n0 / 128) * p.sb_rs;  // block mode: + kb * sb_cs
+  typedef __attribute__((address_space(3))) void* lds_ptr;
 
-  float acc[4][4][4];
+  float acc[TM][TN][4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < TM; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < TN; ++j)
 #pragma unroll
       for (int r = 0; r < 4; ++r) acc[i][j][r] = 0.f;
 
-  v8i a0[4], a1[4];
-  uint4 bst0, bst1;
+  v8i a0[TM], a1[TM];
+  uint4 bst[UB];
   float sav = 0.f, sbv = 0.f, sbk_next = 0.f;
 
-  auto load_a = [&](v8i (&a)[4], int kb) {
+  auto load_a = [&](v8i (&a)[TM], int kb) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < TM; ++i) {
       const uint8_t* q = pa[i] + (int64_t)kb * BK;
-      uint4 lo = *reinterpret_cast<const uint4*>(q);
-      uint4 hi = *reinterpret_cast<const uint4*>(q + 64);
+      const uint4 lo = *reinterpret_cast<const uint4*>(q);
+      const uint4 hi = *reinterpret_cast<const uint4*>(q + 64);
       a[i] = make_frag(lo, hi);
     }
   };
-  auto load_stage = [&](int kb) {
-    bst0 = *reinterpret_cast<const uint4*>(pb0 + (int64_t)kb * BK);
-    bst1 = *reinterpret_cast<const uint4*>(pb1 + (int64_t)kb * BK);
-    if (psa) sav = psa[kb];
-    if (SB_MODE == kSbRow && psb_row) sbv = psb_row[kb];
+  // FP8 path: issue the direct loads of chunk kb into LDS stage `stage`.
+  // Exact path: load chunk kb into registers (store_stage writes them).
+  auto load_stage = [&](int kb, int stage) {
+    if (!EXACT) {
+      uint8_t* dst = stB(stage);
+#pragma unroll
+      for (int q = 0; q < IB; ++q)
+        __builtin_amdgcn_global_load_lds(pb[q] + (int64_t)kb * BK, (lds_ptr)(dst + lds_b[q]), 16, 0, 0);
+      if (w * 64 < BM)
+        __builtin_amdgcn_global_load_lds(psa + kb, (lds_ptr)(stSa(stage) + w * 64), 4, 0, 0);
+      if (SB_MODE == kSbRow && w * 64 < BN)
+        __builtin_amdgcn_global_load_lds(sb + (int64_t)(n0 + w * 64 + lane) * p.sb_rs + kb,
+                                         (lds_ptr)(stSb(stage) + w * 64), 4, 0, 0);
+    } else {
+#pragma unroll
+      for (int q = 0; q < UB; ++q) bst[q] = *reinterpret_cast<const uint4*>(pb[q] + (int64_t)kb * BK);
+      sav = psa[kb];
+      if (SB_MODE == kSbRow) sbv = psb_row[kb];
+    }
     if (SB_MODE == kSbBlock) sbk_next = psb_blk[(int64_t)kb * p.sb_cs];
   };
   auto store_stage = [&](int stage) {
-    if (EXACT) {
-      const v8bf c0 = fp8x8_to_bf16(bst0.x, bst0.y), c1 = fp8x8_to_bf16(bst0.z, bst0.w);
-      const v8bf c2 = fp8x8_to_bf16(bst1.x, bst1.y), c3 = fp8x8_to_bf16(bst1.z, bst1.w);
-      *reinterpret_cast<v8bf*>(ldsB + stage * L::stage_b + lds_b0) = c0;
-      *reinterpret_cast<v8bf*>(ldsB + stage * L::stage_b + lds_b0 + 16) = c1;
-      *reinterpret_cast<v8bf*>(ldsB + stage * L::stage_b + lds_b1) = c2;
-      *reinterpret_cast<v8bf*>(ldsB + stage * L::stage_b + lds_b1 + 16) = c3;
-    } else {
-      *reinterpret_cast<uint4*>(ldsB + stage * L::stage_b + lds_b0) = bst0;
-      *reinterpret_cast<uint4*>(ldsB + stage * L::stage_b + lds_b1) = bst1;
+    if (!EXACT) {
+      // the direct loads of this wave must have landed before the barrier
+      // that publishes the stage; the A loads issued after them may stay in
+      // flight (vmcnt counts in issue order)
+      __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * TM));  // vmcnt(2*TM), expcnt/lgkmcnt: no wait
+      return;
     }
-    if (psa) ldsSa[stage * BM + tid] = sav;
-    if (SB_MODE == kSbRow && psb_row) ldsSb[stage * BN + tid - BM] = sbv;
+    uint8_t* dst = stB(stage);
+#pragma unroll
+    for (int q = 0; q < UB; ++q) {
+      *reinterpret_cast<v8bf*>(dst + lds_b[q]) = fp8x8_to_bf16(bst[q].x, bst[q].y);
+      *reinterpret_cast<v8bf*>(dst + lds_b[q] + 16) = fp8x8_to_bf16(bst[q].z, bst[q].w);
+    }
+    stSa(stage)[lds_sa_slot] = sav;  // parked values land in the spare slot
+    if (SB_MODE == kSbRow) stSb(stage)[lds_sb_slot] = sbv;
   };
 
-  auto compute = [&](const v8i (&a)[4], int stage, float sbk) {
-    const uint8_t* bs = ldsB + stage * L::stage_b;
-    float sc[4][4];
+  auto compute = [&](const v8i (&a)[TM], int stage, float sbk) {
+    const uint8_t* bs = stB(stage);
+    float sc[TM][4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float4 s4 = *reinterpret_cast<const float4*>(ldsSa + stage * BM + wm * WM + 16 * i + 4 * g);
+    for (int i = 0; i < TM; ++i) {
+      const float4 s4 = *reinterpret_cast<const float4*>(stSa(stage) + wm * WM + 16 * i + 4 * g);
       if (SB_MODE == kSbBlock) {
         sc[i][0] = s4.x * sbk; sc[i][1] = s4.y * sbk; sc[i][2] = s4.z * sbk; sc[i][3] = s4.w * sbk;
       } else {
@@ -238,161 +310,196 @@ __global__ __launch_bounds__(NTHREADS) void k_gemm(GemmArgs p) {
       }
     }
     // exact variant: the wave's A fragments as BF16, four quarters of 8 K each
-    v8bf ax[4][4];
+    v8bf ax[TM][4];
     if (EXACT) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int qq = 0; qq < 4; ++qq) ax[i][qq] = fp8x8_to_bf16((uint32_t)a[i][2 * qq], (uint32_t)a[i][2 * qq + 1]);
     }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    // Software pipeline over the TN column sub-tiles: the TM MFMAs of column
+    // j+1 are issued before the promotion FMAs of column j, so the matrix core
+    // works while the vector ALU scales and accumulates the previous partials.
+    auto mfma_col = [&](int j, v4f (&pp)[TM]) {
       const int brow = wn * WN + 16 * j + l16;
-      v8i b;
-      v8bf bx[4];
       if (EXACT) {
         // quarter qq of lane group g covers K [16g + 8qq, +8) for qq < 2 and
         // [64 + 16g + 8(qq-2), +8) for qq >= 2, matching the A fragment order
+        v8bf bx[4];
 #pragma unroll
         for (int qq = 0; qq < 4; ++qq) {
           const int k0 = (qq < 2 ? 0 : 64) + 16 * g + 8 * (qq & 1);
           bx[qq] = *reinterpret_cast<const v8bf*>(bs + brow * BPITCH_X + 2 * k0);
         }
-      } else {
-        const uint4 lo = *reinterpret_cast<const uint4*>(bs + brow * BPITCH + 16 * g);
-        const uint4 hi = *reinterpret_cast<const uint4*>(bs + brow * BPITCH + 64 + 16 * g);
-        b = make_frag(lo, hi);
-      }
-      float sbj = 1.f;
-      if (SB_MODE == kSbRow) sbj = ldsSb[stage * BN + brow];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        v4f pp = {0.f, 0.f, 0.f, 0.f};
-        if (EXACT) {
+        for (int i = 0; i < TM; ++i) {
+          pp[i] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int qq = 0; qq < 4; ++qq) pp = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ax[i][qq], bx[qq], pp, 0, 0, 0);
-        } else {
-          pp = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[i], b, pp, 0, 0, 0, 0, 0, 0);
+          for (int qq = 0; qq < 4; ++qq) pp[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ax[i][qq], bx[qq], pp[i], 0, 0, 0);
         }
+      } else {
+        const int sw = l16 & 7;               // == brow & 7
+        const uint4 lo = *reinterpret_cast<const uint4*>(bs + brow * BK + 16 * (g ^ sw));
+        const uint4 hi = *reinterpret_cast<const uint4*>(bs + brow * BK + 16 * ((4 + g) ^ sw));
+        const v8i b = make_frag(lo, hi);
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+          pp[i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[i], b, v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
+      }
+    };
+    auto promote_col = [&](int j, const v4f (&pp)[TM]) {
+      float sbj = 1.f;
+      if (SB_MODE == kSbRow) sbj = stSb(stage)[wn * WN + 16 * j + l16];
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const float s = SB_MODE == kSbRow ? sc[i][r] * sbj : sc[i][r];
-          acc[i][j][r] = __builtin_fmaf(pp[r], s, acc[i][j][r]);
+          acc[i][j][r] = __builtin_fmaf(pp[i][r], s, acc[i][j][r]);
         }
+    };
+    v4f pa0[TM], pa1[TM];
+    mfma_col(0, pa0);
+#pragma unroll
+    for (int j = 1; j < TN; ++j) {
+      if (j & 1) {
+        mfma_col(j, pa1);
+        promote_col(j - 1, pa0);
+      } else {
+        mfma_col(j, pa0);
+        promote_col(j - 1, pa1);
       }
     }
+    if (TN & 1) promote_col(TN - 1, pa0); else promote_col(TN - 1, pa1);
   };
 
   // ---- prologue
-  load_stage(0);
+  load_stage(0, 0);
   load_a(a0, 0);
   store_stage(0);
   float sbk_cur = sbk_next;
   __syncthreads();
 
-  // ---- main loop, unrolled by two so the A register sets alternate
-  for (int kb = 0; kb < nk; kb += 2) {
-    {
-      const bool more = kb + 1 < nk;
-      if (more) {
-        load_stage(kb + 1);
-        load_a(a1, kb + 1);
-      }
-      compute(a0, 0, sbk_cur);
-      if (more) store_stage(1);
-      sbk_cur = sbk_next;
-      __syncthreads();
-      if (!more) break;
-    }
-    {
-      const bool more = kb + 2 < nk;
-      if (more) {
-        load_stage(kb + 2);
-        load_a(a0, kb + 2);
-      }
-      compute(a1, 1, sbk_cur);
-      if (more) store_stage(0);
-      sbk_cur = sbk_next;
-      __syncthreads();
-    }
+  // ---- main loop: unrolled by two so the A register sets alternate, with no
+  // branch inside; the chunk after the last one is never prefetched (peeled
+  // tail below)
+  // The empty asm memory barriers stop the IR optimizers from sinking the
+  // prefetch loads of the B tile down to their LDS stores, and sched_barrier(0)
+  // stops the machine scheduler from hoisting the stores up to the loads;
+  // either would expose the full memory latency every chunk.  With both, the
+  // loads stay in flight during the compute.
+  int kb = 0;
+  for (; kb + 2 < nk; kb += 2) {
+    load_stage(kb + 1, 1);
+    load_a(a1, kb + 1);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    compute(a0, 0, sbk_cur);
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" ::: "memory");
+    store_stage(1);
+    sbk_cur = sbk_next;
+    __syncthreads();
+    load_stage(kb + 2, 0);
+    load_a(a0, kb + 2);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    compute(a1, 1, sbk_cur);
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" ::: "memory");
+    store_stage(0);
+    sbk_cur = sbk_next;
+    __syncthreads();
+  }
+  if (kb + 1 < nk) {
+    load_stage(kb + 1, 1);
+    load_a(a1, kb + 1);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    compute(a0, 0, sbk_cur);
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" ::: "memory");
+    store_stage(1);
+    sbk_cur = sbk_next;
+    __syncthreads();
+    compute(a1, 1, sbk_cur);
+  } else {
+    compute(a0, 0, sbk_cur);
   }
 
-  // ---- epilogue: stage this wave's 64x64 tile in LDS, then 16-byte row stores
-  if (!OUT_F32) {
-    uint8_t* ep = lds + w * (WM * kEpiPitchBF16);
+  // ---- epilogue: stage this wave's tile in LDS (in passes of epi_rows rows),
+  // then write full 16-byte row segments
+  constexpr int ES = OUT_F32 ? 4 : 2;
+  constexpr int P = L::epi_pitch;
+  constexpr int ER = L::epi_rows;
+  constexpr int CPR = WN * ES / 16;     // 16-byte chunks per row
+  constexpr int RPI = 64 / CPR;         // rows per store instruction
+  static_assert(64 % CPR == 0 && ER % RPI == 0 && ER % 16 == 0, "epilogue store shape");
+  uint8_t* ep = ldsE + w * (ER * P);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int rl = 16 * i + 4 * g + r, cl = 16 * j + l16;
-          *reinterpret_cast<uint16_t*>(ep + rl * kEpiPitchBF16 + 2 * cl) = (uint16_t)f32_to_bf16_rne(acc[i][j][r]);
-        }
-    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes done
-    __builtin_amdgcn_wave_barrier();
-    uint16_t* C = reinterpret_cast<uint16_t*>(p.C);
-#pragma unroll
-    for (int it = 0; it < 8; ++it) {
-      const int rl = it * 8 + (lane >> 3), ch = lane & 7;
-      const int64_t row = m0 + wm * WM + rl;
-      const uint4 v = *reinterpret_cast<const uint4*>(ep + rl * kEpiPitchBF16 + 16 * ch);
-      if (row < mend) *reinterpret_cast<uint4*>(C + row * p.ldc + n0 + wn * WN + 8 * ch) = v;
+  for (int pass = 0; pass < L::epi_passes; ++pass) {
+    if (pass) {
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): previous pass's LDS reads done
+      __builtin_amdgcn_wave_barrier();
     }
-  } else {
-    uint8_t* ep = lds + w * (WM * kEpiPitchF32);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = pass * (TM / L::epi_passes); i < (pass + 1) * (TM / L::epi_passes); ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < TN; ++j)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int rl = 16 * i + 4 * g + r, cl = 16 * j + l16;
-          *reinterpret_cast<float*>(ep + rl * kEpiPitchF32 + 4 * cl) = acc[i][j][r];
+          const int rl = 16 * i + 4 * g + r - pass * ER, cl = 16 * j + l16;
+          if (OUT_F32)
+            *reinterpret_cast<float*>(ep + rl * P + 4 * cl) = acc[i][j][r];
+          else
+            *reinterpret_cast<uint16_t*>(ep + rl * P + 2 * cl) = (uint16_t)f32_to_bf16_rne(acc[i][j][r]);
         }
-    __builtin_amdgcn_s_waitcnt(0xc07f);
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes are done
     __builtin_amdgcn_wave_barrier();
-    float* C = reinterpret_cast<float*>(p.C);
 #pragma unroll
-    for (int it = 0; it < 16; ++it) {
-      const int rl = it * 4 + (lane >> 4), ch = lane & 15;
-      const int64_t row = m0 + wm * WM + rl;
-      float4 v = *reinterpret_cast<const float4*>(ep + rl * kEpiPitchF32 + 16 * ch);
-      if (row < mend) {
-        float4* dst = reinterpret_cast<float4*>(C + row * p.ldc + n0 + wn * WN + 4 * ch);
-        if (p.accumulate) {
-          const float4 o = *dst;
-          v.x += o.x; v.y += o.y; v.z += o.z; v.w += o.w;
-        }
-        *dst = v;
+    for (int it = 0; it < ER / RPI; ++it) {
+      const int rl = it * RPI + lane / CPR, ch = lane % CPR;
+      const int64_t row = m0 + wm * WM + pass * ER + rl;
+      if (row >= mend) continue;
+      const uint4 v = *reinterpret_cast<const uint4*>(ep + rl * P + 16 * ch);
+      uint8_t* dst = reinterpret_cast<uint8_t*>(p.C) + (row * p.ldc + n0 + wn * WN) * ES + 16 * ch;
+      if (OUT_F32 && p.accumulate) {
+        const float4 o = *reinterpret_cast<const float4*>(dst);
+        float4 f = *reinterpret_cast<const float4*>(&v);
+        f.x += o.x; f.y += o.y; f.z += o.z; f.w += o.w;
+        *reinterpret_cast<float4*>(dst) = f;
+      } else {
+        *reinterpret_cast<uint4*>(dst) = v;
       }
     }
   }
+#endif  // __HIP_DEVICE_COMPILE__
 }
 
-template <int SB_MODE, int OUT_F32, bool GROUPED, bool EXACT>
+template <class C, int SB_MODE, int OUT_F32, bool GROUPED, bool EXACT>
 static hipError_t launch_one(const GemmArgs& a, hipStream_t st) {
   int64_t tiles;
-  const int64_t tiles_n = a.N / BN;
+  const int64_t tiles_n = a.N / C::BN;
   if (!GROUPED)
-    tiles = ((a.M + BM - 1) / BM) * tiles_n;
+    tiles = ((a.M + C::BM - 1) / C::BM) * tiles_n;
   else
-    tiles = ((a.M + BM - 1) / BM + a.E) * tiles_n;  // upper bound: one partial tile per expert
+    tiles = ((a.M + C::BM - 1) / C::BM + a.E) * tiles_n;  // upper bound: one partial tile per expert
   if (tiles <= 0) return hipSuccess;
-  hipLaunchKernelGGL((k_gemm<SB_MODE, OUT_F32, GROUPED, EXACT>), dim3((uint32_t)tiles), dim3(NTHREADS), 0, st, a);
+  hipLaunchKernelGGL((k_gemm<C, SB_MODE, OUT_F32, GROUPED, EXACT>), dim3((uint32_t)tiles), dim3(C::NT), 0, st, a);
   return hipGetLastError();
 }
 
 template <bool EXACT>
 static hipError_t launch_mode(const GemmArgs& a, hipStream_t st) {
+  typedef DefaultCfg C;
   const bool grouped = a.offsets != nullptr;
   if (a.sb_mode == kSbRow) {
     // per-column B scales: the weight-gradient product, FP32 output
-    return launch_one<kSbRow, 1, false, EXACT>(a, st);
+    return launch_one<C, kSbRow, 1, false, EXACT>(a, st);
   }
   if (grouped)
-    return a.out_f32 ? launch_one<kSbBlock, 1, true, EXACT>(a, st) : launch_one<kSbBlock, 0, true, EXACT>(a, st);
-  return a.out_f32 ? launch_one<kSbBlock, 1, false, EXACT>(a, st) : launch_one<kSbBlock, 0, false, EXACT>(a, st);
+    return a.out_f32 ? launch_one<C, kSbBlock, 1, true, EXACT>(a, st) : launch_one<C, kSbBlock, 0, true, EXACT>(a, st);
+  return a.out_f32 ? launch_one<C, kSbBlock, 1, false, EXACT>(a, st) : launch_one<C, kSbBlock, 0, false, EXACT>(a, st);
 }
 
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t st) {

@@ -40,6 +40,15 @@ def test_exports_every_declared_symbol(lib):
         assert getattr(lib, n) is not None
 
 
+def test_every_kernel_launch_stub_is_defined(lib):
+    """A kernel whose host-side launch stub is missing makes dlopen fail on the
+    GPU machine only; catch it here."""
+    out = subprocess.run(["nm", "-D", fq.LIB_PATH], capture_output=True, text=True).stdout
+    undefined = [l for l in out.splitlines() if " U " in l and "__device_stub__" in l]
+    assert not undefined, undefined[:3]
+    assert sum(1 for l in out.splitlines() if "__device_stub__" in l) >= 16
+
+
 def test_status_strings(lib):
     for code, name in enumerate(fq._STATUS):
         assert fq.status_string(code).startswith(name)
