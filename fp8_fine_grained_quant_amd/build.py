@@ -13,7 +13,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libfp8q.so")
-SOURCES = ["quant_kernels.hip", "gemm_kernels.hip", "api.cpp"]
+SOURCES = ["quant_kernels.hip", "gemm_kernels.hip", "gemm_fp8.hip", "api.cpp"]
 ARCH = os.environ.get("FP8Q_ARCH", "gfx950")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -25,6 +25,8 @@ FLAGS = [
     "-fno-gpu-flush-denormals-to-zero",
     # private staging arrays must stay in registers, never in LDS
     "-mllvm", "-disable-promote-alloca-to-lds",
+    # MFMA results in architectural VGPRs: the promotion FMAs read them directly
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-ffp-contract=off",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function",

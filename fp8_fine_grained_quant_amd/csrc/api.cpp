@@ -21,6 +21,7 @@ inline fp8q_status launched(hipError_t e) { return e == hipSuccess ? FP8Q_OK : F
 
 constexpr int64_t kMaxGroups = (int64_t(1) << 31) - 1;
 constexpr int64_t kMaxDim = (int64_t(1) << 31) - 1;
+constexpr int64_t kMaxContraction = 1024 * 128;  // the GEMM keeps one scale per chunk in LDS
 
 // Checks shared by the three quantizers: input [rows, cols] with stride ld_in
 // (elements of size in_es), code output with stride ld_out bytes covering
@@ -104,7 +105,7 @@ static fp8q_status fp8q_gemm_fprop_impl(int exact, const uint8_t* xq, const floa
                             int64_t M, int64_t N, int64_t K, void* y, fp8q_dtype yt, int64_t ld_y,
                             hipStream_t stream) {
   if (M < 0 || N < 0 || K < 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim) return FP8Q_ERR_SHAPE;
-  if (N % 128 != 0 || K % 128 != 0) return FP8Q_ERR_SHAPE;
+  if (N % 128 != 0 || K % 128 != 0 || K > kMaxContraction) return FP8Q_ERR_SHAPE;
   if (!valid_dtype(yt)) return FP8Q_ERR_DTYPE;
   if (M == 0 || N == 0) return FP8Q_OK;
   if (K == 0) return FP8Q_ERR_SHAPE;  // an empty contraction would leave Y undefined
@@ -124,7 +125,7 @@ static fp8q_status fp8q_gemm_dgrad_impl(int exact, const uint8_t* dyq, const flo
                             int64_t M, int64_t N, int64_t K, void* dx, fp8q_dtype dxt, int64_t ld_dx,
                             hipStream_t stream) {
   if (M < 0 || N < 0 || K < 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim) return FP8Q_ERR_SHAPE;
-  if (N % 128 != 0 || K % 128 != 0) return FP8Q_ERR_SHAPE;
+  if (N % 128 != 0 || K % 128 != 0 || N > kMaxContraction) return FP8Q_ERR_SHAPE;
   if (!valid_dtype(dxt)) return FP8Q_ERR_DTYPE;
   if (M == 0 || K == 0) return FP8Q_OK;
   if (N == 0) return FP8Q_ERR_SHAPE;
@@ -146,7 +147,7 @@ static fp8q_status fp8q_gemm_wgrad_impl(int exact, const uint8_t* dyq_t, const f
                             int64_t T, int64_t N, int64_t K, float* dw, int64_t ld_dw, int accumulate,
                             hipStream_t stream) {
   if (T < 0 || N < 0 || K < 0 || T > kMaxDim || N > kMaxDim || K > kMaxDim) return FP8Q_ERR_SHAPE;
-  if (T % 128 != 0 || K % 128 != 0) return FP8Q_ERR_SHAPE;
+  if (T % 128 != 0 || K % 128 != 0 || T > kMaxContraction) return FP8Q_ERR_SHAPE;
   if (accumulate != 0 && accumulate != 1) return FP8Q_ERR_SHAPE;
   if (N == 0 || K == 0) return FP8Q_OK;
   if (T == 0) return FP8Q_ERR_SHAPE;

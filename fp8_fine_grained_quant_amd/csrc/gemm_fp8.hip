@@ -1,0 +1,353 @@
+// FP8 GEMM with FP32 promotion after every 128-long K chunk, gfx950.
+//
+// What is computed ("DeepSeek FP8 Training", the Fprop pipeline and the
+// weight- and input-gradient lists; the innerforce.co.kr excerpt of the
+// DeepSeek-V3 report, the paragraph after Figure 7 (a): dequantization folded
+// into the increased-precision accumulation; the "unified E4M3 format" page,
+// "Enhanced Numerical Stability": partial results promoted to FP32 registers
+// at a fixed interval of 128 elements):
+//
+//     C[m, n] = sum_kb  P_kb[m, n] * sA(m, kb) * sB(n, kb)
+//
+// P_kb is the FP8 x FP8 product over the 128 K of chunk kb, one
+// v_mfma_f32_16x16x128_f8f6f4 per 16x16 sub-tile, so one MFMA is exactly one
+// promotion interval; the scale-and-add runs as FP32 FMAs on the vector ALU
+// into accumulators held in architectural VGPRs.
+//
+// Design (MI355X: 256 CUs, one 4-SIMD CU per workgroup, 160 KB LDS):
+//   * workgroup tile 256 x 128, four waves (one per SIMD), each wave a
+//     64 x 128 strip of 4 x 8 sub-tiles (128 FP32 accumulators per lane);
+//   * every operand byte reaches LDS by direct buffer loads (global -> LDS,
+//     no registers): A tile 32 KB, B tile 16 KB and the chunk's scales per
+//     stage, three stages, 16-byte chunks XOR-swizzled by (row & 7) so the
+//     fragment reads of 16 rows hit distinct banks;
+//   * each stage is one LDS object, so the compiler can tell the stage being
+//     read from the one being filled and never waits for the latter;
+//   * one chunk = 32 matrix "slots"; slot t issues one MFMA and the promotion
+//     of slot t-3, whose result is then complete, so the matrix core and the
+//     vector ALU work side by side; the skew runs across chunk boundaries
+//     (the last three promotions of a chunk are issued under the first MFMAs
+//     of the next), and the next chunk's fragments are read under the last
+//     column's MFMAs;
+//   * two barriers per chunk: after the first column (every wave is done with
+//     the previous chunk, whose stage is then refilled with chunk c+2), and
+//     before the last column (chunk c+1 has landed), giving each chunk's
+//     loads about one chunk time to arrive;
+//   * buffer loads range-check the A rows: rows past the tile's last valid
+//     row read nothing and are never stored;
+//   * the epilogue stages each wave's strip through LDS so every global store
+//     is a full 16-byte row segment.
+//
+// MFMA operand layout (the same permutation of the 128 K positions for A and
+// B, which leaves every dot product unchanged): lane l supplies row l%16 of
+// the 16-row slice, bytes [16g, 16g+16) and [64+16g, 64+16g+16) of the chunk,
+// g = l/16.  Result: lane l holds C[4g + r][l%16], r = 0..3.
+
+#include "device_common.h"
+#include "gemm_tile.h"
+#include "launch.h"
+
+namespace fp8q {
+namespace {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void* lds_ptr;
+
+constexpr int kBM = 256, kBN = 128, kBK = 128;
+constexpr int kNT = 256;                          // four waves
+constexpr int kTM = 4, kTN = 8;                   // sub-tiles per wave: 64 x 128
+constexpr int kIA = kBM * kBK / (16 * kNT);       // 16-byte A loads per lane per chunk
+constexpr int kIB = kBN * kBK / (16 * kNT);       // 16-byte B loads per lane per chunk
+constexpr int kMaxChunks = 1024;
+constexpr int kSkew = 3;                          // promotion trails its MFMA by 3 slots
+static_assert(kTM == 4 && kSkew == kTM - 1, "the slot schedule below assumes 4 row sub-tiles");
+
+template <int SB_MODE>
+struct Stage {
+  static constexpr int a = 0;                     // [256 rows][128 B], swizzled
+  static constexpr int b = kBM * kBK;             // [128 rows][128 B], swizzled
+  static constexpr int sa = b + kBN * kBK;        // 256 row scales
+  static constexpr int sb = sa + 4 * kNT;         // row mode: 128 column scales (+128 spare)
+  static constexpr int bytes = sb + (SB_MODE == kSbRow ? 4 * kNT : 0);
+  static constexpr int sbk_len = SB_MODE == kSbBlock ? kMaxChunks : 4;
+  static_assert(3 * bytes + 4 * sbk_len <= 160 * 1024, "LDS of one CU");
+  static_assert(4 * 12288 <= bytes, "epilogue staging fits in one stage");
+};
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  // raw buffer: stride 0, range `bytes`, default data format for gfx9
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+__device__ __forceinline__ v8i make_frag(uint4 lo, uint4 hi) {
+  v8i f;
+  f[0] = (int)lo.x; f[1] = (int)lo.y; f[2] = (int)lo.z; f[3] = (int)lo.w;
+  f[4] = (int)hi.x; f[5] = (int)hi.y; f[6] = (int)hi.z; f[7] = (int)hi.w;
+  return f;
+}
+
+template <int V>
+struct IC {
+  static constexpr int value = V;
+};
+
+}  // namespace
+
+template <int SB_MODE, int OUT_F32, bool GROUPED>
+__global__ __launch_bounds__(kNT) void k_gemm_fp8(GemmArgs p) {
+#if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
+  typedef Stage<SB_MODE> S;
+  constexpr bool ROW = SB_MODE == kSbRow;
+  __shared__ __attribute__((aligned(16))) uint8_t st0[S::bytes];
+  __shared__ __attribute__((aligned(16))) uint8_t st1[S::bytes];
+  __shared__ __attribute__((aligned(16))) uint8_t st2[S::bytes];
+  __shared__ __attribute__((aligned(16))) float sbk_all[S::sbk_len];  // block mode: B scale per chunk
+
+  TileCoord tc;
+  if (!tile_coord<kBM, kBN, GROUPED>(p, tc)) return;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l16 = lane & 15, g = lane >> 4;
+  const int nk = (int)(p.K / kBK);
+  const uint8_t* Bp = p.B + (GROUPED ? (int64_t)tc.e * p.b_estride : 0);
+  const float* sbp = p.sb + (GROUPED ? (int64_t)tc.e * p.sb_estride : 0);
+  const int rows = (int)min(tc.mend - tc.m0, (int64_t)kBM);  // valid rows of the tile, >= 1
+
+  // ---- direct-load sources.  Buffer ranges: A covers exactly the tile's valid
+  // rows (a row past them is out of range: nothing is read), B the tile's 128
+  // columns, the scale vectors their rows.
+  const __amdgpu_buffer_rsrc_t rA = make_rsrc(p.A + tc.m0 * p.lda, (uint32_t)(rows * p.lda));
+  const __amdgpu_buffer_rsrc_t rB = make_rsrc(Bp + (int64_t)tc.n0 * p.ldb, (uint32_t)(kBN * p.ldb));
+  const __amdgpu_buffer_rsrc_t rSa = make_rsrc(p.sa + tc.m0 * p.ld_sa, (uint32_t)(rows * p.ld_sa * 4));
+  const __amdgpu_buffer_rsrc_t rSb = make_rsrc(sbp + (int64_t)tc.n0 * p.sb_rs, (uint32_t)(kBN * p.sb_rs * 4));
+  // Wave w's q-th 16-byte load of a tile writes LDS bytes [(w*I + q)*1024, +1024):
+  // rows (w*I + q)*8 + lane/8, physical chunk lane%8, which holds the logical
+  // chunk (lane%8) ^ (row%8); row%8 == lane/8.
+  const int r8 = lane >> 3, lc = (lane & 7) ^ r8;
+  const uint32_t voffA = (uint32_t)((w * kIA * 8 + r8) * p.lda + 16 * lc);
+  const uint32_t voffB = (uint32_t)((w * kIB * 8 + r8) * p.ldb + 16 * lc);
+  const uint32_t stepA = (uint32_t)(8 * p.lda), stepB = (uint32_t)(8 * p.ldb);
+  // scales: lane (w, l) fetches row 64w + l (clamped to a valid row) and, in
+  // row mode, column (64w + l) % 128 (waves 2, 3 fill spare slots)
+  const uint32_t voffSa = (uint32_t)(min(w * 64 + lane, rows - 1) * p.ld_sa * 4);
+  const uint32_t voffSb = (uint32_t)(((w * 64 + lane) & (kBN - 1)) * p.sb_rs * 4);
+
+  auto issue = [&](int kb, uint8_t* st) {
+    const uint32_t ka = (uint32_t)kb * kBK;
+#pragma unroll
+    for (int q = 0; q < kIA; ++q)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, (lds_ptr)(st + S::a + (w * kIA + q) * 1024), 16, voffA + q * stepA,
+                                               ka, 0, 0);
+#pragma unroll
+    for (int q = 0; q < kIB; ++q)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, (lds_ptr)(st + S::b + (w * kIB + q) * 1024), 16, voffB + q * stepB,
+                                               ka, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rSa, (lds_ptr)(st + S::sa + w * 256), 4, voffSa, (uint32_t)kb * 4, 0, 0);
+    if (ROW)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rSb, (lds_ptr)(st + S::sb + w * 256), 4, voffSb, (uint32_t)kb * 4, 0, 0);
+  };
+  // direct loads one wave issues per chunk; vmcnt counts them in issue order
+  constexpr int kDma = kIA + kIB + 1 + (ROW ? 1 : 0);
+  static_assert(kDma < 64, "vmcnt range");
+  constexpr int kWaitPrev = 0x0F70 | (kDma & 15) | ((kDma >> 4) << 14);  // vmcnt(kDma) only
+
+  // ---- LDS fragment reads
+  const int sw = l16 & 7;
+  const int offLo = l16 * kBK + 16 * (g ^ sw);
+  const int offHi = l16 * kBK + 16 * ((4 + g) ^ sw);
+  auto rdA = [&](const uint8_t* st, int i) -> v8i {
+    const uint8_t* base = st + S::a + (w * 64 + 16 * i) * kBK;
+    return make_frag(*reinterpret_cast<const uint4*>(base + offLo), *reinterpret_cast<const uint4*>(base + offHi));
+  };
+  auto rdB = [&](const uint8_t* st, int j) -> v8i {
+    const uint8_t* base = st + S::b + 16 * j * kBK;
+    return make_frag(*reinterpret_cast<const uint4*>(base + offLo), *reinterpret_cast<const uint4*>(base + offHi));
+  };
+  auto rdSa = [&](const uint8_t* st, int i) -> float4 {
+    return *reinterpret_cast<const float4*>(st + S::sa + 4 * (w * 64 + 16 * i + 4 * g));
+  };
+  auto rdSb = [&](const uint8_t* st, int j) -> float {
+    return *reinterpret_cast<const float*>(st + S::sb + 4 * (16 * j + l16));
+  };
+
+  float acc[kTM][kTN][4];
+#pragma unroll
+  for (int i = 0; i < kTM; ++i)
+#pragma unroll
+    for (int j = 0; j < kTN; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[i][j][r] = 0.f;
+
+  // state carried from chunk to chunk
+  v8i a[kTM];           // A fragments of the current chunk
+  v8i bfirst;           // B fragment of the current chunk's column 0
+  v4f pp[kTM];          // MFMA partials, ring indexed by slot % 4
+  float sc[kTM][4];     // row scales (times the block's B scale) in use
+  float4 sa_nx[kTM];    // the next chunk's row scales, as read
+  float sbk_nx = 1.f;   // the next chunk's block B scale
+  float sbc_prev = 0.f; // row mode: scale of the previous chunk's last column
+  float sbc_first = 0.f;  // row mode: scale of the current chunk's column 0
+
+  auto promote = [&](int i, int j, float sbc) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float s = ROW ? sc[i][r] * sbc : sc[i][r];
+      acc[i][j][r] = __builtin_fmaf(pp[i][r], s, acc[i][j][r]);
+    }
+  };
+  auto load_sc = [&](int i) {
+    const float4 v = sa_nx[i];
+    const float k = ROW ? 1.f : sbk_nx;
+    sc[i][0] = v.x * k; sc[i][1] = v.y * k; sc[i][2] = v.z * k; sc[i][3] = v.w * k;
+  };
+  auto mfma = [&](const v8i& x, const v8i& y) -> v4f {
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(x, y, v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
+  };
+  auto fence = [] { asm volatile("" ::: "memory"); };
+
+  // ---- prologue: block B scales of every chunk to LDS, chunks 0 and 1 in
+  // flight, chunk 0 published, its fragments and scales in registers
+  if (!ROW) {
+    const float* psb = sbp + (int64_t)(tc.n0 / 128) * p.sb_rs;
+    for (int q = tid; q < nk; q += kNT) sbk_all[q] = psb[(int64_t)q * p.sb_cs];
+  }
+  fence();
+  issue(0, st0);
+  issue(min(1, nk - 1), st1);
+  __builtin_amdgcn_s_waitcnt(kWaitPrev);
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the block scales are written
+  __builtin_amdgcn_s_barrier();
+  fence();
+#pragma unroll
+  for (int i = 0; i < kTM; ++i) {
+    a[i] = rdA(st0, i);
+    sa_nx[i] = rdSa(st0, i);
+    pp[i] = v4f{0.f, 0.f, 0.f, 0.f};
+  }
+  bfirst = rdB(st0, 0);
+  if (ROW) sbc_first = rdSb(st0, 0);
+  else sbk_nx = sbk_all[0];
+#pragma unroll
+  for (int i = 0; i < kTM; ++i) load_sc(i);
+
+  // ---- one chunk.  Stage u holds chunk c; stage (u+1)%3 receives or holds
+  // chunk c+1; stage (u+2)%3 held chunk c-1 and is refilled with chunk c+2.
+  auto step = [&](int c, auto U) {
+    constexpr int u = decltype(U)::value;
+    uint8_t* const cur = u == 0 ? st0 : u == 1 ? st1 : st2;
+    uint8_t* const nxt = u == 0 ? st1 : u == 1 ? st2 : st0;
+    uint8_t* const fut = u == 0 ? st2 : u == 1 ? st0 : st1;
+    v8i bcur = bfirst, bnext;
+    float sbc[kTN + 1];  // row mode: column scales of this chunk, [kTN] = next chunk's column 0
+    sbc[0] = sbc_first;
+#pragma unroll
+    for (int j = 0; j < kTN; ++j) {
+      // the B fragment (and column scale) of the next column: this chunk's
+      // column j+1, or the next chunk's column 0 (published by the barrier
+      // before the last column)
+      if (j + 1 < kTN) {
+        bnext = rdB(cur, j + 1);
+        if (ROW) sbc[j + 1] = rdSb(cur, j + 1);
+      } else {
+        bnext = rdB(nxt, 0);
+        if (ROW) sbc[kTN] = rdSb(nxt, 0);
+      }
+      fence();
+#pragma unroll
+      for (int i = 0; i < kTM; ++i) {
+        const int t = kTM * j + i;
+        pp[i] = mfma(a[i], bcur);
+        if (t >= kSkew) {
+          const int tp = t - kSkew;
+          promote(tp % kTM, tp / kTM, sbc[tp / kTM]);
+        } else {
+          // the previous chunk's last column, rows t+1; then this chunk's
+          // scales for those rows (row 0's were set at the previous chunk end)
+          promote(t + 1, kTN - 1, sbc_prev);
+          load_sc(t + 1);
+        }
+        if (j == kTN - 1) {
+          // a[i] is no longer needed for this chunk: fetch the next chunk's
+          a[i] = rdA(nxt, i);
+          if (i == 0) {
+            sa_nx[0] = rdSa(nxt, 0);
+            sa_nx[1] = rdSa(nxt, 1);
+            if (!ROW) sbk_nx = sbk_all[min(c + 1, nk - 1)];
+          } else if (i == 1) {
+            sa_nx[2] = rdSa(nxt, 2);
+            sa_nx[3] = rdSa(nxt, 3);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (j == 0) {
+        // every wave has finished reading chunk c-1: refill its stage with
+        // chunk c+2 (past the end, the last chunk again, so every chunk
+        // issues the same loads and the wait counts stay exact)
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+        __builtin_amdgcn_s_barrier();
+        fence();
+        issue(min(c + 2, nk - 1), fut);
+        fence();
+      }
+      if (j == kTN - 2) {
+        // chunk c+1 has landed: only the loads of chunk c+2 may be in flight
+        __builtin_amdgcn_s_waitcnt(kWaitPrev);
+        __builtin_amdgcn_s_barrier();
+        fence();
+      }
+      bcur = bnext;
+    }
+    // slot 31 promoted row 0 of the last column: row 0 takes the next
+    // chunk's scales now, rows 1-3 after their last promotion
+    load_sc(0);
+    bfirst = bcur;
+    sbc_prev = sbc[kTN - 1];
+    sbc_first = sbc[kTN];
+  };
+
+  int c = 0;
+  for (; c + 3 <= nk; c += 3) {
+    step(c, IC<0>());
+    step(c + 1, IC<1>());
+    step(c + 2, IC<2>());
+  }
+  if (c < nk) step(c, IC<0>());
+  if (c + 1 < nk) step(c + 1, IC<1>());
+  // the last chunk's last column, rows 1-3 (load_sc(0) above only touched row 0)
+#pragma unroll
+  for (int i = 1; i < kTM; ++i) promote(i, kTN - 1, sbc_prev);
+
+  // ---- epilogue: no direct load may still target LDS, and every wave is done
+  // reading; each wave then stages its strip in its own 12 KB of stage 0
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  fence();
+  store_tile<kTM, kTN, OUT_F32, OUT_F32 ? 16 : 32>(acc, st0 + w * 12288, p, tc.m0 + w * 64, tc.mend, tc.n0, lane);
+#endif  // __HIP_DEVICE_COMPILE__
+}
+
+namespace {
+
+template <int SB_MODE, int OUT_F32, bool GROUPED>
+hipError_t launch_one(const GemmArgs& a, hipStream_t st) {
+  const int64_t tiles_n = a.N / kBN;
+  const int64_t tiles = GROUPED ? ((a.M + kBM - 1) / kBM + a.E) * tiles_n  // upper bound: a partial tile per expert
+                                : ((a.M + kBM - 1) / kBM) * tiles_n;
+  if (tiles <= 0) return hipSuccess;
+  hipLaunchKernelGGL((k_gemm_fp8<SB_MODE, OUT_F32, GROUPED>), dim3((uint32_t)tiles), dim3(kNT), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gemm_fp8(const GemmArgs& a, hipStream_t st) {
+  if (a.sb_mode == kSbRow) return launch_one<kSbRow, 1, false>(a, st);  // weight gradient: FP32 out
+  if (a.offsets != nullptr)
+    return a.out_f32 ? launch_one<kSbBlock, 1, true>(a, st) : launch_one<kSbBlock, 0, true>(a, st);
+  return a.out_f32 ? launch_one<kSbBlock, 1, false>(a, st) : launch_one<kSbBlock, 0, false>(a, st);
+}
+
+}  // namespace fp8q

@@ -58,6 +58,7 @@ typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 
 constexpr int BK = 128;          // one chunk = one promotion interval
+constexpr int kMaxChunks = 1024; // contraction length limit: 1024 chunks of 128
 constexpr int BPITCH_X = 272;    // LDS row pitch of the BF16 B tile (exact variant)
 [[maybe_unused]] constexpr int GROUP_M = 4;  // m-tiles per band in the tile order
 
@@ -97,11 +98,16 @@ struct Lds {
   // chunks XOR-swizzled by (row & 7); BF16 tiles (exact variant) are written
   // from registers with a padded pitch.
   static constexpr int stage_b = C::BN * (EXACT ? BPITCH_X : BK);
+  static constexpr int stages = EXACT ? 2 : 3;  // pipeline depth (chunks in flight + 1)
   static constexpr int epi_pitch = C::WN * (OUT_F32 ? 4 : 2) + 16;
   static constexpr int epi_passes = OUT_F32 ? 2 : 1;
   static constexpr int epi_rows = C::WM / epi_passes;
   static constexpr int epi = C::NWAVES * epi_rows * epi_pitch;
-  static constexpr int total = 2 * stage_b + 2 * 4 * (C::BM + 4) + 2 * 4 * (C::BN + 4) + epi;
+  // scale arrays: every wave's 64 lanes write one slot each (spare slots park
+  // the values of lanes without a row/column of their own)
+  static constexpr int sa_len = (C::BM > C::NWAVES * 64 ? C::BM : C::NWAVES * 64) + 4;
+  static constexpr int sb_len = (C::BN > C::NWAVES * 64 ? C::BN : C::NWAVES * 64) + 4;
+  static constexpr int total = stages * (stage_b + 4 * sa_len + 4 * sb_len) + epi;
   static_assert(total <= 160 * 1024, "LDS budget of one CU");
 };
 
@@ -130,20 +136,27 @@ __global__ __launch_bounds__(C::NT) void k_gemm(GemmArgs p) {
   constexpr int BM = C::BM, BN = C::BN, WM = C::WM, WN = C::WN, TM = C::TM, TN = C::TN, NT = C::NT;
   constexpr int UB = BN * 8 / NT;  // 16-byte B units per thread per chunk
   typedef Lds<C, OUT_F32, EXACT> L;
+  constexpr int NS = L::stages, D = NS - 1;  // stages, prefetch distance in chunks
+  constexpr int S2 = NS > 2 ? 1 : 0;           // third stage present
   __shared__ __attribute__((aligned(16))) uint8_t ldsB0[L::stage_b];
   __shared__ __attribute__((aligned(16))) uint8_t ldsB1[L::stage_b];
-  __shared__ __attribute__((aligned(16))) float ldsSa0[BM + 4];  // [BM]: parking slot
-  __shared__ __attribute__((aligned(16))) float ldsSa1[BM + 4];
-  __shared__ __attribute__((aligned(16))) float ldsSb0[BN + 4];
-  __shared__ __attribute__((aligned(16))) float ldsSb1[BN + 4];
+  __shared__ __attribute__((aligned(16))) uint8_t ldsB2[S2 ? L::stage_b : 16];
+  __shared__ __attribute__((aligned(16))) float ldsSa0[L::sa_len];  // [BM..]: parking slots
+  __shared__ __attribute__((aligned(16))) float ldsSa1[L::sa_len];
+  __shared__ __attribute__((aligned(16))) float ldsSa2[S2 ? L::sa_len : 4];
+  __shared__ __attribute__((aligned(16))) float ldsSb0[L::sb_len];
+  __shared__ __attribute__((aligned(16))) float ldsSb1[L::sb_len];
+  __shared__ __attribute__((aligned(16))) float ldsSb2[S2 ? L::sb_len : 4];
   __shared__ __attribute__((aligned(16))) uint8_t ldsE[L::epi];
-  auto stB = [&](int stage) { return stage ? ldsB1 : ldsB0; };
-  auto stSa = [&](int stage) { return stage ? ldsSa1 : ldsSa0; };
-  auto stSb = [&](int stage) { return stage ? ldsSb1 : ldsSb0; };
+  __shared__ float ldsSbk[kMaxChunks];  // block mode: the tile's B scale of every chunk
+  auto stB = [&](int stage) { return stage == 0 ? ldsB0 : stage == 1 ? ldsB1 : ldsB2; };
+  auto stSa = [&](int stage) { return stage == 0 ? ldsSa0 : stage == 1 ? ldsSa1 : ldsSa2; };
+  auto stSb = [&](int stage) { return stage == 0 ? ldsSb0 : stage == 1 ? ldsSb1 : ldsSb2; };
   constexpr int kPitchB = EXACT ? BPITCH_X : BK;
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, w = tid >> 6;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, provably uniform
   const int wm = w / C::WAVES_N, wn = w % C::WAVES_N;
   const int l16 = lane & 15, g = lane >> 4;
 
@@ -228,13 +241,14 @@ __global__ __launch_bounds__(C::NT) void k_gemm(GemmArgs p) {
   // compiler can track the prefetch loads across iterations.  FP8 path: the
   // A scales go global->LDS with 4-byte direct loads, one per lane, by the
   // first BM/64 waves.
-  int64_t sa_row = m0 + (EXACT ? (tid & (BM - 1)) : ((w * 64 + lane) & (BM - 1)));
+  int64_t sa_row = m0 + ((EXACT ? tid : w * 64 + lane) & (BM - 1));
   sa_row = sa_row < mend ? sa_row : mend - 1;
   const float* psa = p.sa + sa_row * p.ld_sa;
   const int lds_sa_slot = tid < BM ? tid : BM;  // BM: parking slot (never read)
   const float* psb_row = sb + (int64_t)(n0 + (tid & (BN - 1))) * p.sb_rs;
   const int lds_sb_slot = tid < BN ? tid : BN;
   const float* psb_blk = sb + (int64_t)(n0 / 128) * p.sb_rs;  // block mode: + kb * sb_cs
+  const float* psb_row_dma = sb + (int64_t)(n0 + ((w * 64 + lane) & (BN - 1))) * p.sb_rs;
   typedef __attribute__((address_space(3))) void* lds_ptr;
 
   float acc[TM][TN][4];
@@ -245,9 +259,9 @@ __global__ __launch_bounds__(C::NT) void k_gemm(GemmArgs p) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) acc[i][j][r] = 0.f;
 
-  v8i a0[TM], a1[TM];
-  uint4 bst[UB];
-  float sav = 0.f, sbv = 0.f, sbk_next = 0.f;
+  v8i abuf[NS][TM];     // A fragments of the chunks in flight, one set per stage
+  uint4 bst[UB];        // exact path: B staging registers
+  float sav = 0.f, sbv = 0.f;
 
   auto load_a = [&](v8i (&a)[TM], int kb) {
 #pragma unroll
@@ -266,27 +280,20 @@ __global__ __launch_bounds__(C::NT) void k_gemm(GemmArgs p) {
 #pragma unroll
       for (int q = 0; q < IB; ++q)
         __builtin_amdgcn_global_load_lds(pb[q] + (int64_t)kb * BK, (lds_ptr)(dst + lds_b[q]), 16, 0, 0);
-      if (w * 64 < BM)
-        __builtin_amdgcn_global_load_lds(psa + kb, (lds_ptr)(stSa(stage) + w * 64), 4, 0, 0);
-      if (SB_MODE == kSbRow && w * 64 < BN)
-        __builtin_amdgcn_global_load_lds(sb + (int64_t)(n0 + w * 64 + lane) * p.sb_rs + kb,
-                                         (lds_ptr)(stSb(stage) + w * 64), 4, 0, 0);
+      // every wave issues one scale load per lane (no branch): waves past BM
+      // (or BN) re-read valid rows into parking slots
+      __builtin_amdgcn_global_load_lds(psa + kb, (lds_ptr)(stSa(stage) + w * 64), 4, 0, 0);
+      if (SB_MODE == kSbRow)
+        __builtin_amdgcn_global_load_lds(psb_row_dma + kb, (lds_ptr)(stSb(stage) + w * 64), 4, 0, 0);
     } else {
 #pragma unroll
       for (int q = 0; q < UB; ++q) bst[q] = *reinterpret_cast<const uint4*>(pb[q] + (int64_t)kb * BK);
       sav = psa[kb];
       if (SB_MODE == kSbRow) sbv = psb_row[kb];
     }
-    if (SB_MODE == kSbBlock) sbk_next = psb_blk[(int64_t)kb * p.sb_cs];
   };
   auto store_stage = [&](int stage) {
-    if (!EXACT) {
-      // the direct loads of this wave must have landed before the barrier
-      // that publishes the stage; the A loads issued after them may stay in
-      // flight (vmcnt counts in issue order)
-      __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * TM));  // vmcnt(2*TM), expcnt/lgkmcnt: no wait
-      return;
-    }
+    if (!EXACT) return;  // the direct loads already target the stage
     uint8_t* dst = stB(stage);
 #pragma unroll
     for (int q = 0; q < UB; ++q) {
@@ -297,7 +304,8 @@ __global__ __launch_bounds__(C::NT) void k_gemm(GemmArgs p) {
     if (SB_MODE == kSbRow) stSb(stage)[lds_sb_slot] = sbv;
   };
 
-  auto compute = [&](const v8i (&a)[TM], int stage, float sbk) {
+  auto compute = [&](const v8i (&a)[TM], int stage, int c) {
+    const float sbk = SB_MODE == kSbBlock ? ldsSbk[c] : 1.f;
     const uint8_t* bs = stB(stage);
     float sc[TM][4];
 #pragma unroll
@@ -371,61 +379,91 @@ __global__ __launch_bounds__(C::NT) void k_gemm(GemmArgs p) {
       }
     }
     if (TN & 1) promote_col(TN - 1, pa0); else promote_col(TN - 1, pa1);
+    // Interleave: each MFMA (32 cycles on the matrix core) is followed by four
+    // promotion instructions of the previous column, so the vector ALU works
+    // while the matrix core does; B fragment reads are spread between columns.
+    if (!EXACT) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);   // scale + first B fragment reads
+      __builtin_amdgcn_sched_group_barrier(0x002, 4 * TM, 0);  // scale products
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+          __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);   // four VALU
+          if (i == 1) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // next B fragment
+        }
+      }
+      __builtin_amdgcn_sched_group_barrier(0x002, 4 * TM, 0);  // last column's promotion
+    }
   };
 
-  // ---- prologue
-  load_stage(0, 0);
-  load_a(a0, 0);
-  store_stage(0);
-  float sbk_cur = sbk_next;
-  __syncthreads();
+  // ---- pipeline.  Chunk c lives in stage c % NS.  Iteration c issues the
+  // loads of chunk c + D (direct LDS loads for B and the scales, register
+  // loads for A), computes chunk c, waits until the direct loads of chunk c+1
+  // have landed and synchronises the workgroup.  The barrier is a bare
+  // s_barrier with compiler memory fences: __syncthreads() would also wait
+  // for every outstanding global load, i.e. drain the prefetch.
+  // Every iteration issues the same loads (past the last chunk the index is
+  // clamped, which re-reads the last chunk into a stage nobody reads again),
+  // so the instruction stream is branch-free and the wait counts are exact.
+  // VMEM instructions one iteration issues (direct loads counted only where
+  // every wave issues them): waiting for vmcnt <= kVm after an iteration's
+  // issue leaves exactly the previous chunk's A loads and this issue in flight.
+  constexpr int kVm = 4 * TM + IB + 1 + (SB_MODE == kSbRow ? 1 : 0);
+  static_assert(kVm < 64, "vmcnt range");
+  auto wait_stage = [&]() {
+    if (!EXACT) __builtin_amdgcn_s_waitcnt(0x0F70 | (kVm & 15) | ((kVm >> 4) << 14));
+  };
+  auto block_sync = [&]() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS stores are done
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+  auto issue = [&](int c, int stage) {
+    load_stage(c, stage);
+    load_a(abuf[stage], c);
+  };
 
-  // ---- main loop: unrolled by two so the A register sets alternate, with no
-  // branch inside; the chunk after the last one is never prefetched (peeled
-  // tail below)
-  // The empty asm memory barriers stop the IR optimizers from sinking the
-  // prefetch loads of the B tile down to their LDS stores, and sched_barrier(0)
-  // stops the machine scheduler from hoisting the stores up to the loads;
-  // either would expose the full memory latency every chunk.  With both, the
-  // loads stay in flight during the compute.
+  // prologue: the tile's block-mode B scales of all chunks go to LDS once;
+  // chunks 0 .. D-1 in flight, chunk 0 published
+  if (SB_MODE == kSbBlock)
+    for (int q = tid; q < nk; q += NT) ldsSbk[q] = psb_blk[(int64_t)q * p.sb_cs];
+#pragma unroll
+  for (int c = 0; c < D; ++c) issue(min(c, nk - 1), c);
+  if (EXACT) store_stage(0);
+  if (!EXACT) {
+    constexpr int v0 = kVm - 2 * TM;  // chunk 1's loads may stay in flight
+    __builtin_amdgcn_s_waitcnt(0x0F70 | (v0 & 15) | ((v0 >> 4) << 14));
+  }
+  block_sync();
+
+  // The empty asm memory barriers stop the IR optimizers from moving loads of
+  // the next chunks down to their uses, and sched_barrier(0) stops the
+  // machine scheduler from pulling those uses up; either would expose the full
+  // memory latency every chunk.
+  auto step = [&](int c, int u) {  // u = c % NS, a compile-time constant at every call
+    issue(min(c + D, nk - 1), (u + D) % NS);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    compute(abuf[u], u, c);
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" ::: "memory");
+    if (EXACT) store_stage((u + 1) % NS);
+    wait_stage();
+    block_sync();
+  };
   int kb = 0;
-  for (; kb + 2 < nk; kb += 2) {
-    load_stage(kb + 1, 1);
-    load_a(a1, kb + 1);
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_sched_barrier(0);
-    compute(a0, 0, sbk_cur);
-    __builtin_amdgcn_sched_barrier(0);
-    asm volatile("" ::: "memory");
-    store_stage(1);
-    sbk_cur = sbk_next;
-    __syncthreads();
-    load_stage(kb + 2, 0);
-    load_a(a0, kb + 2);
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_sched_barrier(0);
-    compute(a1, 1, sbk_cur);
-    __builtin_amdgcn_sched_barrier(0);
-    asm volatile("" ::: "memory");
-    store_stage(0);
-    sbk_cur = sbk_next;
-    __syncthreads();
+  for (; kb + NS <= nk; kb += NS) {
+#pragma unroll
+    for (int u = 0; u < NS; ++u) step(kb + u, u);
   }
-  if (kb + 1 < nk) {
-    load_stage(kb + 1, 1);
-    load_a(a1, kb + 1);
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_sched_barrier(0);
-    compute(a0, 0, sbk_cur);
-    __builtin_amdgcn_sched_barrier(0);
-    asm volatile("" ::: "memory");
-    store_stage(1);
-    sbk_cur = sbk_next;
-    __syncthreads();
-    compute(a1, 1, sbk_cur);
-  } else {
-    compute(a0, 0, sbk_cur);
-  }
+#pragma unroll
+  for (int u = 0; u < NS - 1; ++u)
+    if (kb + u < nk) step(kb + u, u);
+  // no direct load may still target LDS when the workgroup retires
+  __builtin_amdgcn_s_waitcnt(0x0F70);
 
   // ---- epilogue: stage this wave's tile in LDS (in passes of epi_rows rows),
   // then write full 16-byte row segments
@@ -503,7 +541,7 @@ static hipError_t launch_mode(const GemmArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t st) {
-  return a.exact ? launch_mode<true>(a, st) : launch_mode<false>(a, st);
+  return a.exact ? launch_mode<true>(a, st) : launch_gemm_fp8(a, st);
 }
 
 }  // namespace fp8q

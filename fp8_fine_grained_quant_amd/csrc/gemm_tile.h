@@ -1,0 +1,119 @@
+// Output-tile assignment and LDS-staged epilogue shared by the GEMM kernels.
+#pragma once
+
+#include "device_common.h"
+#include "launch.h"
+
+namespace fp8q {
+
+constexpr int kGroupM = 4;  // m-tiles per band of the tile order
+
+struct TileCoord {
+  int64_t m0;    // first output row of the tile
+  int64_t mend;  // end of the rows this tile may write (M, or the expert's end)
+  int n0;        // first output column
+  int e;         // expert (grouped launches), else 0
+};
+
+// Maps this workgroup to an output tile; false when it has none (grouped
+// launches size the grid for the worst case).
+//
+// Dispatch hands consecutive workgroup ids to the 8 XCDs in turn, so the ids
+// are first renumbered to give each XCD one contiguous run of tile numbers;
+// tile numbers then walk bands of kGroupM m-tiles column by column.  The
+// workgroups of one XCD thus cover a compact block of the output and share
+// their A rows and B columns in that XCD's L2.
+template <int BM, int BN, bool GROUPED>
+__device__ __forceinline__ bool tile_coord(const GemmArgs& p, TileCoord& tc) {
+  const int G = gridDim.x, bid = blockIdx.x;
+  const int xcd = bid & 7, q8 = G >> 3, r8 = G & 7;
+  const int t = xcd * q8 + min(xcd, r8) + (bid >> 3);
+  const int tiles_n = (int)(p.N / BN);
+  if (!GROUPED) {
+    const int tiles_m = (int)((p.M + BM - 1) / BM);
+    const int band = kGroupM * tiles_n;
+    const int b = t / band, first_m = b * kGroupM;
+    const int gm = min(tiles_m - first_m, kGroupM);
+    const int in_band = t - b * band;
+    tc.m0 = (int64_t)(first_m + in_band % gm) * BM;
+    tc.n0 = (in_band / gm) * BN;
+    tc.mend = p.M;
+    tc.e = 0;
+    return true;
+  }
+  // grouped: walk the experts' tile counts; tiles never straddle experts
+  int64_t base = 0, lo = 0, hi = 0, mt = 0;
+  int e = 0;
+  for (; e < (int)p.E; ++e) {
+    lo = p.offsets[e];
+    hi = p.offsets[e + 1];
+    mt = (hi - lo + BM - 1) / BM;
+    const int64_t cnt = mt * tiles_n;
+    if (t < base + cnt) break;
+    base += cnt;
+  }
+  if (e >= (int)p.E) return false;
+  const int64_t local = t - base;
+  tc.m0 = lo + (local % mt) * BM;
+  tc.n0 = (int)(local / mt) * BN;
+  tc.mend = hi;
+  tc.e = e;
+  return true;
+}
+
+// Writes one wave's WM x WN accumulator block (MFMA 16x16 result layout:
+// lane l holds rows 4*(l/16) + r, column l%16 of each sub-tile) to C, staged
+// through the wave's private LDS region `ep` in passes of ER rows so that
+// every global access is a full 16-byte row segment.  Rows at or beyond
+// `mend` are not written.
+template <int TM, int TN, int OUT_F32, int ER>
+__device__ __forceinline__ void store_tile(const float (&acc)[TM][TN][4], uint8_t* ep, const GemmArgs& p,
+                                           int64_t row0, int64_t mend, int col0, int lane) {
+  constexpr int WM = 16 * TM, WN = 16 * TN;
+  constexpr int ES = OUT_F32 ? 4 : 2;
+  constexpr int P = WN * ES + 16;       // padded LDS row pitch
+  constexpr int CPR = WN * ES / 16;     // 16-byte chunks per row
+  constexpr int RPI = 64 / CPR;         // rows per store instruction
+  constexpr int PASSES = WM / ER;
+  static_assert(64 % CPR == 0 && ER % RPI == 0 && ER % 16 == 0 && WM % ER == 0, "epilogue store shape");
+  const int g = lane >> 4, l16 = lane & 15;
+#pragma unroll
+  for (int pass = 0; pass < PASSES; ++pass) {
+    if (pass) {
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the previous pass's LDS reads are done
+      __builtin_amdgcn_wave_barrier();
+    }
+#pragma unroll
+    for (int i = pass * (ER / 16); i < (pass + 1) * (ER / 16); ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int rl = 16 * i + 4 * g + r - pass * ER, cl = 16 * j + l16;
+          if (OUT_F32)
+            *reinterpret_cast<float*>(ep + rl * P + 4 * cl) = acc[i][j][r];
+          else
+            *reinterpret_cast<uint16_t*>(ep + rl * P + 2 * cl) = (uint16_t)f32_to_bf16_rne(acc[i][j][r]);
+        }
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS writes are done
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int it = 0; it < ER / RPI; ++it) {
+      const int rl = it * RPI + lane / CPR, ch = lane % CPR;
+      const int64_t row = row0 + pass * ER + rl;
+      if (row >= mend) continue;
+      const uint4 v = *reinterpret_cast<const uint4*>(ep + rl * P + 16 * ch);
+      uint8_t* dst = reinterpret_cast<uint8_t*>(p.C) + (row * p.ldc + col0) * ES + 16 * ch;
+      if (OUT_F32 && p.accumulate) {
+        const float4 o = *reinterpret_cast<const float4*>(dst);
+        float4 f = *reinterpret_cast<const float4*>(&v);
+        f.x += o.x; f.y += o.y; f.z += o.z; f.w += o.w;
+        *reinterpret_cast<float4*>(dst) = f;
+      } else {
+        *reinterpret_cast<uint4*>(dst) = v;
+      }
+    }
+  }
+}
+
+}  // namespace fp8q

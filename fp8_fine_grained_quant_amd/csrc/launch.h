@@ -44,5 +44,7 @@ struct GemmArgs {
 };
 
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t st);
+// the FP8 matrix-instruction kernel (a.exact == 0)
+hipError_t launch_gemm_fp8(const GemmArgs& a, hipStream_t st);
 
 }  // namespace fp8q

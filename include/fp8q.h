@@ -50,7 +50,8 @@
  *     (vector access), else FP8Q_ERR_ALIGN.  Scale arrays need 4-byte alignment.
  *   - Inputs must be finite; NaN or Inf inputs give unspecified codes.
  *   - Work is sized for one GPU's share; every size must fit in int64 and the
- *     number of 128-groups of one call must stay below 2^31.
+ *     number of 128-groups of one call must stay below 2^31.  A GEMM's
+ *     contraction length is at most 131072 (1024 chunks of 128).
  */
 #ifndef FP8Q_H
 #define FP8Q_H

@@ -46,7 +46,8 @@ def test_every_kernel_launch_stub_is_defined(lib):
     out = subprocess.run(["nm", "-D", fq.LIB_PATH], capture_output=True, text=True).stdout
     undefined = [l for l in out.splitlines() if " U " in l and "__device_stub__" in l]
     assert not undefined, undefined[:3]
-    assert sum(1 for l in out.splitlines() if "__device_stub__" in l) >= 16
+    # 3 quantizers + 5 FP8 GEMM and 5 exact GEMM instantiations
+    assert sum(1 for l in out.splitlines() if "__device_stub__" in l) >= 13
 
 
 def test_status_strings(lib):
