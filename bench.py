@@ -15,6 +15,7 @@ Prints one JSON line on stdout; progress goes to stderr.
 """
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -26,6 +27,8 @@ if ROOT not in sys.path:
 
 PEAK_FP8_TFLOPS = 5000.0      # MI355X dense FP8 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = ["quant_kernels.hip", "gemm_fp8.hip", "gemm_kernels.hip", "gemm_tile.h", "device_common.h"]
 
 
 def log(msg):
@@ -36,19 +39,22 @@ def cdiv(a, b):
     return (a + b - 1) // b
 
 
-def build_workload(dev):
-    import torch
+def host_inputs():
+    """The step's seeded synthetic inputs on the host (CPU tensors)."""
     import synth
 
     t0 = time.time()
     x, w = synth.linear_x_w()
     dy = synth.linear_dy()
     xm, wm, off = synth.moe_fprop()
-    log(f"inputs generated in {time.time() - t0:.1f}s; moving to {dev}")
+    log(f"inputs generated in {time.time() - t0:.1f}s")
+    return dict(x=x, w=w, dy=dy, xm=xm, wm=wm, off=off)
+
+
+def build_workload(H, dev):
     g = lambda t: t.to(dev)
-    L = dict(x=g(x), w=g(w), dy=g(dy), xm=g(xm), wm=g(wm).reshape(-1, wm.shape[2]), off=g(off))
-    del x, w, dy, xm, wm
-    return L
+    return dict(x=g(H["x"]), w=g(H["w"]), dy=g(H["dy"]), xm=g(H["xm"]),
+                wm=g(H["wm"]).reshape(-1, H["wm"].shape[2]), off=g(H["off"]))
 
 
 def make_ops(L, dev):
@@ -96,46 +102,90 @@ def make_ops(L, dev):
     return ops, O
 
 
-def cpu_baseline(frac):
-    """The CPU oracle, as it stands, on a row sample (fraction `frac`) of
-    every op of one step; returns its GEMM throughput."""
+def cpu_baseline(H, frac):
+    """The CPU oracle, as it stands, on a token sample of one step: the first
+    `frac` of the tokens (rounded to 128) of the linear layer (quantizers,
+    Fprop, Dgrad, and Wgrad over those tokens) and of the MoE layer (its
+    quantizer over those tokens, the weights of the experts they reach, the
+    grouped Fprop).  Returns its GEMM throughput in the bench's unit."""
     import numpy as np
     import oracle
-    import synth
     try:
         from threadpoolctl import threadpool_info
         blas_threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"]
                            or [1])
     except Exception:  # pragma: no cover
         blas_threads = 1
-    x, w = synth.linear_x_w()
-    dy = synth.linear_dy()
+    x, w, dy, xm, wm, off = H["x"], H["w"], H["dy"], H["xm"], H["wm"], H["off"]
     M, K = x.shape
     N = w.shape[0]
-    rs = max(1, int(M * frac))
-    ns = max(128, int(N * frac) // 128 * 128)
-    xs_ = x[:rs].float().numpy()
-    dys_ = dy[:rs].float().numpy()
-    wf = w.numpy()
+    rs = max(128, int(M * frac) // 128 * 128)
+    ts = max(128, int(xm.shape[0] * frac) // 128 * 128)
+    x_s = x[:rs].float().numpy()
+    dy_s = dy[:rs].float().numpy()
+    xm_s = xm[:ts].float().numpy()
+    offs = np.minimum(off.numpy().astype(np.int64), ts)
+    experts = [e for e in range(len(offs) - 1) if offs[e + 1] > offs[e]]
     flops = 0.0
     t0 = time.perf_counter()
-    xq, xsc = oracle.quant_act_1x128(xs_)
-    wq, wsc, _ = oracle.quant_weight_128x128(wf[:ns])            # a slice of the weight rows
-    wq_full, wsc_full, _ = oracle.quant_weight_128x128(wf)        # the GEMMs need all of W
-    y, _ = oracle.fprop_ref(xq, xsc, wq_full, wsc_full)
-    flops += 2.0 * rs * N * K
-    dyq, dysc = oracle.quant_act_1x128(dys_)
-    dx, _ = oracle.dgrad_ref(dyq, dysc, wq_full, wsc_full)
-    flops += 2.0 * rs * N * K
-    xq_t, xs_t = oracle.quant_transpose(x.float().numpy()[:, : max(128, int(K * frac))])
-    dq_t, ds_t = oracle.quant_transpose(dy.float().numpy()[:, :ns])
-    dw, _ = oracle.wgrad_ref(dq_t, ds_t, xq_t, xs_t)
-    flops += 2.0 * ns * xq_t.shape[0] * M
+    xq, xsc = oracle.quant_act_1x128(x_s)
+    wq, wsc, _ = oracle.quant_weight_128x128(w.numpy())
+    oracle.fprop_ref(xq, xsc, wq, wsc)
+    dyq, dysc = oracle.quant_act_1x128(dy_s)
+    oracle.dgrad_ref(dyq, dysc, wq, wsc)
+    xq_t, xs_t = oracle.quant_transpose(x_s)
+    dq_t, ds_t = oracle.quant_transpose(dy_s)
+    oracle.wgrad_ref(dq_t, ds_t, xq_t, xs_t)
+    flops += 3 * 2.0 * rs * N * K
+    xmq, xmsc = oracle.quant_act_1x128(xm_s)
+    wmq = np.zeros(wm.shape, dtype=np.uint8)
+    wms = np.zeros((wm.shape[0], N // 128, K // 128), dtype=np.float32)
+    for e in experts:
+        wmq[e], wms[e], _ = oracle.quant_weight_128x128(wm[e].numpy())
+    oracle.grouped_ref(xmq, xmsc, wmq, wms, offs)
+    flops += 2.0 * ts * N * K
     dt = time.perf_counter() - t0
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(blas_threads), "kind": "oracle",
-            "sample": f"linear-layer step on a {frac:g} row sample (X/dY rows {rs}, W rows {ns} quantized "
-                      f"plus full W for the GEMM operands, Wgrad {ns}x{xq_t.shape[0]} outputs over {M} tokens); "
-                      f"{dt:.1f}s wall, FP64 BLAS GEMMs + NumPy quantizers"}
+            "sample": f"one step on a token sample: linear layer on the first {rs} of {M} tokens (all three "
+                      f"GEMMs, all quantizers, full W), MoE layer on the first {ts} of {xm.shape[0]} tokens "
+                      f"({len(experts)} experts reached, their weights quantized); {dt:.1f}s wall; FP64 BLAS "
+                      f"GEMMs on {blas_threads} threads, NumPy quantizers on one"}
+
+
+def kernel_source_hash():
+    """SHA-256 over the kernel sources: measured HBM traffic is reported only
+    while the kernels are the ones the counters were taken on."""
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "fp8_fine_grained_quant_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed counter summary
+    (FETCH_SIZE + WRITE_SIZE, scaled by the copy-kernel calibration), or None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_sha") != kernel_source_hash():
+        return None
+    k = t.get("kernels", {}).get(kernel)
+    return None if k is None else k.get("bytes_per_launch")
+
+
+def copy_calibration(mbytes, reps):
+    """A plain device copy of known size, for scaling the HBM byte counters."""
+    import torch
+    n = int(mbytes * 1e6) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4, "reps": reps}), flush=True)
 
 
 def main():
@@ -143,20 +193,29 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--cpu-frac", type=float, default=1 / 32)
+    ap.add_argument("--cpu-frac", type=float, default=1 / 2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=float, default=0.0, metavar="MB",
+                    help="only run a plain device copy of MB megabytes (counter calibration) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: the path is built and timed on a single MI355X; "
               "multi-GPU runs are not part of this library", file=sys.stderr)
         sys.exit(2)
 
+    if args.copy_calibration > 0:
+        copy_calibration(args.copy_calibration, 5)
+        return
+
     import torch
     import fp8_fine_grained_quant_amd as fq
 
     fq.load_library()
     dev = "cuda:0"
-    L = build_workload(dev)
+    H = host_inputs()
+    L = build_workload(H, dev)
+    if args.no_cpu_baseline:
+        del H
     ops, O = make_ops(L, dev)
     names = [o[0] for o in ops]
 
@@ -204,17 +263,18 @@ def main():
     dom = max(range(len(ops)), key=lambda i: kernels[names[i]]["avg_us"])
     dname, _, dkind, dwork = ops[dom]
     dk = kernels[dname]
+    traffic = measured_traffic(dname)
     if dkind == "mfma":
         roof = {"kernel": dname, "bound": "mfma", "achieved": dk["tflops"], "peak": PEAK_FP8_TFLOPS,
-                "unit": "TFLOP/s", "frac": dk["frac_peak"], "traffic": None}
+                "unit": "TFLOP/s", "frac": dk["frac_peak"], "traffic": traffic}
     else:
         roof = {"kernel": dname, "bound": "hbm", "achieved": dk["gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": dk["frac_peak"], "traffic": None}
+                "frac": dk["frac_peak"], "traffic": traffic}
 
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
-        cpu = cpu_baseline(args.cpu_frac)
+        cpu = cpu_baseline(H, args.cpu_frac)
         log(f"cpu baseline {cpu}")
 
     out = {
@@ -231,12 +291,14 @@ def main():
         "dtype": "fp8e4m3 x fp8e4m3 -> f32 (bf16/f32 out)",
         "data": "synthetic",
         "config": {
-            "workload": "fp8 linear-layer fwd+dgrad+wgrad (M=4096 tokens, K=7168, N=2048) + MoE grouped fprop "
-                        "(16384 tokens, 32 experts, 2048x7168), incl. all online quantization",
+            "workload": "FP8 linear layer Fprop+Dgrad+Wgrad (X [4096,7168] bf16, W [2048,7168] fp32, dY [4096,2048] "
+                        "bf16) + MoE grouped Fprop (X [16384,7168] bf16, 32 experts of [2048,7168] fp32, Zipf "
+                        "token counts), each with its online 1x128 / 128x128 E4M3 quantization",
             "gemm_gflop_per_step": round(gemm_flops / 1e9, 2),
             "value_definition": "useful GEMM FLOPs of the step / step time (quantizers inside the timed step)",
         },
         "roofline": roof,
+        "kernel_source_sha": kernel_source_hash(),
         "kernels": kernels,
         "cpu_baseline": cpu,
     }

@@ -30,12 +30,14 @@ description; no code was taken from anywhere):
   pattern, no infinities, largest value 448) are those of the OCP FP8 E4M3FN
   encoding.
 
-Readings taken where the pages are silent (each one is listed with its reason
-in the design notes of the repository):
+Readings taken where the pages are silent:
 
 * scale s = fl32(amax'/448) is stored; values are multiplied by
-  inv = fl32(448/amax'), amax' = max(amax, 2^-100)        -- parity unpinned by
-  the pages (they do not say divide-by-s or multiply-by-inverse); fixed here.
+  inv = fl32(448/amax'), amax' = max(amax, 2^-100).  The pages do not say
+  whether a value is divided by s or multiplied by 1/s; the two conventions
+  give different codes for some values, and the tests pin the one chosen here
+  (an exact rational re-derivation of every code, and a planted switch to the
+  other convention that the tests must catch).
 * round-to-nearest-even, saturation to +-448, the sign of zero kept.
 * Wgrad operands are grouped 1x128 along the token (contraction) axis.
 * the GEMM result is defined as the exact contraction of the dequantized
