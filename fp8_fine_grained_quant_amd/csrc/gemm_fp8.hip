@@ -134,22 +134,36 @@ __global__ __launch_bounds__(kNT) void k_gemm_fp8(GemmArgs p) {
   const uint32_t voffSa = (uint32_t)(min(w * 64 + lane, rows - 1) * p.ld_sa * 4);
   const uint32_t voffSb = (uint32_t)(((w * 64 + lane) & (kBN - 1)) * p.sb_rs * 4);
 
-  auto issue = [&](int kb, uint8_t* st) {
-    const uint32_t ka = (uint32_t)kb * kBK;
-#pragma unroll
-    for (int q = 0; q < kIA; ++q)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, (lds_ptr)(st + S::a + (w * kIA + q) * 1024), 16, voffA + q * stepA,
-                                               ka, 0, 0);
-#pragma unroll
-    for (int q = 0; q < kIB; ++q)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, (lds_ptr)(st + S::b + (w * kIB + q) * 1024), 16, voffB + q * stepB,
-                                               ka, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rSa, (lds_ptr)(st + S::sa + w * 256), 4, voffSa, (uint32_t)kb * 4, 0, 0);
-    if (ROW)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rSb, (lds_ptr)(st + S::sb + w * 256), 4, voffSb, (uint32_t)kb * 4, 0, 0);
-  };
   // direct loads one wave issues per chunk; vmcnt counts them in issue order
   constexpr int kDma = kIA + kIB + 1 + (ROW ? 1 : 0);
+  // the d-th direct load of chunk kb into stage st
+  auto issue_one = [&](int kb, uint8_t* st, int d) {
+    const uint32_t ka = (uint32_t)kb * kBK;
+    if (d < kIA) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, (lds_ptr)(st + S::a + (w * kIA + d) * 1024), 16,
+                                               voffA + d * stepA, ka, 0, 0);
+    } else if (d < kIA + kIB) {
+      const int q = d - kIA;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, (lds_ptr)(st + S::b + (w * kIB + q) * 1024), 16,
+                                               voffB + q * stepB, ka, 0, 0);
+    } else if (d == kIA + kIB) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rSa, (lds_ptr)(st + S::sa + w * 256), 4, voffSa, (uint32_t)kb * 4, 0,
+                                               0);
+    } else {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rSb, (lds_ptr)(st + S::sb + w * 256), 4, voffSb, (uint32_t)kb * 4, 0,
+                                               0);
+    }
+  };
+  auto issue = [&](int kb, uint8_t* st) {
+#pragma unroll
+    for (int d = 0; d < kDma; ++d) issue_one(kb, st, d);
+  };
+  // Inside a chunk the loads of chunk c+2 are spread over the slots between
+  // the two barriers (a burst of them fills the memory pipeline's queue and
+  // stalls the issuing wave, MFMAs included): load d goes out in slot
+  // kFirstDmaSlot + (d * kDmaSlots) / kDma.
+  constexpr int kFirstDmaSlot = kTM, kDmaSlots = kTM * (kTN - 2);
+  static_assert(kDma <= kDmaSlots, "one direct load per slot at most");
   static_assert(kDma < 64, "vmcnt range");
   constexpr int kWaitPrev = 0x0F70 | (kDma & 15) | ((kDma >> 4) << 14);  // vmcnt(kDma) only
 
@@ -268,6 +282,11 @@ __global__ __launch_bounds__(kNT) void k_gemm_fp8(GemmArgs p) {
           promote(t + 1, kTN - 1, sbc_prev);
           load_sc(t + 1);
         }
+        if (t >= kFirstDmaSlot && t < kFirstDmaSlot + kDmaSlots) {
+#pragma unroll
+          for (int d = 0; d < kDma; ++d)
+            if (kFirstDmaSlot + (d * kDmaSlots) / kDma == t) issue_one(min(c + 2, nk - 1), fut, d);
+        }
         if (j == kTN - 1) {
           // a[i] is no longer needed for this chunk: fetch the next chunk's
           a[i] = rdA(nxt, i);
@@ -283,13 +302,11 @@ __global__ __launch_bounds__(kNT) void k_gemm_fp8(GemmArgs p) {
         __builtin_amdgcn_sched_barrier(0);
       }
       if (j == 0) {
-        // every wave has finished reading chunk c-1: refill its stage with
-        // chunk c+2 (past the end, the last chunk again, so every chunk
+        // every wave has finished reading chunk c-1: its stage may be refilled
+        // with chunk c+2 (past the end, the last chunk again, so every chunk
         // issues the same loads and the wait counts stay exact)
         __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
         __builtin_amdgcn_s_barrier();
-        fence();
-        issue(min(c + 2, nk - 1), fut);
         fence();
       }
       if (j == kTN - 2) {
