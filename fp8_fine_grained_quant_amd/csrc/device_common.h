@@ -72,15 +72,46 @@ __device__ __forceinline__ uint32_t abs_bits(float f) { return __float_as_uint(f
 
 // Element loaders: 8 consecutive elements of type T from a 16-byte-aligned
 // address (full), or element by element (n < 8 valid).
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+// Streaming accesses: every input byte is read once and every output byte
+// written once.
+// NT = 1 marks the access non-temporal.  Measured on MI355X: it pays for
+// long streams written or read in full 64-byte-plus segments (the stacked
+// expert weights), and loses for tensors that fit the 256 MB MALL or for
+// scattered short stores, so each kernel picks per access.
+template <int NT>
+__device__ __forceinline__ u32x4 ld_stream16(const void* p) {
+  if (NT) return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return *reinterpret_cast<const u32x4*>(p);
+}
+template <int NT>
+__device__ __forceinline__ void st_stream8(void* p, uint32_t a, uint32_t b) {
+  if (NT) __builtin_nontemporal_store(u32x2{a, b}, reinterpret_cast<u32x2*>(p));
+  else *reinterpret_cast<u32x2*>(p) = u32x2{a, b};
+}
+template <int NT>
+__device__ __forceinline__ void st_stream16(void* p, uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  if (NT) __builtin_nontemporal_store(u32x4{a, b, c, d}, reinterpret_cast<u32x4*>(p));
+  else *reinterpret_cast<u32x4*>(p) = u32x4{a, b, c, d};
+}
+template <int NT>
+__device__ __forceinline__ void st_stream4(void* p, uint32_t a) {
+  if (NT) __builtin_nontemporal_store(a, reinterpret_cast<uint32_t*>(p));
+  else *reinterpret_cast<uint32_t*>(p) = a;
+}
+
 struct BF16In {
   typedef uint16_t elem;
   static constexpr int kBytes = 2;
+  template <int NT = 0>
   __device__ __forceinline__ static void load8(const elem* p, float v[8]) {
-    uint4 u = *reinterpret_cast<const uint4*>(p);
-    v[0] = bf16_to_f32(u.x & 0xFFFFu); v[1] = bf16_to_f32(u.x >> 16);
-    v[2] = bf16_to_f32(u.y & 0xFFFFu); v[3] = bf16_to_f32(u.y >> 16);
-    v[4] = bf16_to_f32(u.z & 0xFFFFu); v[5] = bf16_to_f32(u.z >> 16);
-    v[6] = bf16_to_f32(u.w & 0xFFFFu); v[7] = bf16_to_f32(u.w >> 16);
+    const u32x4 u = ld_stream16<NT>(p);
+    v[0] = bf16_to_f32(u[0] & 0xFFFFu); v[1] = bf16_to_f32(u[0] >> 16);
+    v[2] = bf16_to_f32(u[1] & 0xFFFFu); v[3] = bf16_to_f32(u[1] >> 16);
+    v[4] = bf16_to_f32(u[2] & 0xFFFFu); v[5] = bf16_to_f32(u[2] >> 16);
+    v[6] = bf16_to_f32(u[3] & 0xFFFFu); v[7] = bf16_to_f32(u[3] >> 16);
   }
   __device__ __forceinline__ static float load1(const elem* p) { return bf16_to_f32(*p); }
 };
@@ -88,11 +119,11 @@ struct BF16In {
 struct F32In {
   typedef float elem;
   static constexpr int kBytes = 4;
+  template <int NT = 0>
   __device__ __forceinline__ static void load8(const elem* p, float v[8]) {
-    float4 a = *reinterpret_cast<const float4*>(p);
-    float4 b = *reinterpret_cast<const float4*>(p + 4);
-    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    const u32x4 a = ld_stream16<NT>(p), b = ld_stream16<NT>(p + 4);
+    v[0] = __uint_as_float(a[0]); v[1] = __uint_as_float(a[1]); v[2] = __uint_as_float(a[2]); v[3] = __uint_as_float(a[3]);
+    v[4] = __uint_as_float(b[0]); v[5] = __uint_as_float(b[1]); v[6] = __uint_as_float(b[2]); v[7] = __uint_as_float(b[3]);
   }
   __device__ __forceinline__ static float load1(const elem* p) { return *p; }
 };
