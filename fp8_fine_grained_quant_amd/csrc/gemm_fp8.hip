@@ -92,6 +92,21 @@ struct IC {
   static constexpr int value = V;
 };
 
+// Lane L of every 16-lane row, broadcast to the whole row (DPP row_newbcast).
+template <int L>
+__device__ __forceinline__ float row_bcast(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x150 + L, 0xF, 0xF, false));
+}
+
+// The four row scales of sub-tile I held by lanes 4I .. 4I+3 of each row.
+template <int I>
+__device__ __forceinline__ void row_scales(float v, float k, float (&out)[4]) {
+  out[0] = row_bcast<4 * I + 0>(v) * k;
+  out[1] = row_bcast<4 * I + 1>(v) * k;
+  out[2] = row_bcast<4 * I + 2>(v) * k;
+  out[3] = row_bcast<4 * I + 3>(v) * k;
+}
+
 }  // namespace
 
 template <int SB_MODE, int OUT_F32, bool GROUPED>
@@ -179,9 +194,16 @@ __global__ __launch_bounds__(kNT) void k_gemm_fp8(GemmArgs p) {
     const uint8_t* base = st + S::b + 16 * j * kBK;
     return make_frag(*reinterpret_cast<const uint4*>(base + offLo), *reinterpret_cast<const uint4*>(base + offHi));
   };
-  auto rdSa = [&](const uint8_t* st, int i) -> float4 {
-    return *reinterpret_cast<const float4*>(st + S::sa + 4 * (w * 64 + 16 * i + 4 * g));
+  // Row scales: lane (l16, g) reads the scale of row 16*(l16/4) + 4g + l16%4
+  // of its wave's strip, i.e. the (i, r) = (l16/4, l16%4) entry of its lane
+  // group's 16 values; row_scales hands every lane of the group entry (i, r)
+  // (DPP row_newbcast): one 4-byte LDS read per chunk instead of four
+  // 16-byte ones.
+  const int offSa = 4 * (w * 64 + 16 * (l16 >> 2) + 4 * g + (l16 & 3));
+  auto rdSa = [&](const uint8_t* st) -> float {
+    return *reinterpret_cast<const float*>(st + S::sa + offSa);
   };
+
   auto rdSb = [&](const uint8_t* st, int j) -> float {
     return *reinterpret_cast<const float*>(st + S::sb + 4 * (16 * j + l16));
   };
@@ -199,7 +221,7 @@ __global__ __launch_bounds__(kNT) void k_gemm_fp8(GemmArgs p) {
   v8i bfirst;           // B fragment of the current chunk's column 0
   v4f pp[kTM];          // MFMA partials, ring indexed by slot % 4
   float sc[kTM][4];     // row scales (times the block's B scale) in use
-  float4 sa_nx[kTM];    // the next chunk's row scales, as read
+  float sa_nx = 0.f;    // the next chunk's row scales, as read (one per lane)
   float sbk_nx = 1.f;   // the next chunk's block B scale
   float sbc_prev = 0.f; // row mode: scale of the previous chunk's last column
   float sbc_first = 0.f;  // row mode: scale of the current chunk's column 0
@@ -212,9 +234,13 @@ __global__ __launch_bounds__(kNT) void k_gemm_fp8(GemmArgs p) {
     }
   };
   auto load_sc = [&](int i) {
-    const float4 v = sa_nx[i];
     const float k = ROW ? 1.f : sbk_nx;
-    sc[i][0] = v.x * k; sc[i][1] = v.y * k; sc[i][2] = v.z * k; sc[i][3] = v.w * k;
+    switch (i) {
+      case 0: row_scales<0>(sa_nx, k, sc[0]); break;
+      case 1: row_scales<1>(sa_nx, k, sc[1]); break;
+      case 2: row_scales<2>(sa_nx, k, sc[2]); break;
+      default: row_scales<3>(sa_nx, k, sc[3]); break;
+    }
   };
   auto mfma = [&](const v8i& x, const v8i& y) -> v4f {
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(x, y, v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
@@ -237,7 +263,7 @@ __global__ __launch_bounds__(kNT) void k_gemm_fp8(GemmArgs p) {
 #pragma unroll
   for (int i = 0; i < kTM; ++i) {
     a[i] = rdA(st0, i);
-    sa_nx[i] = rdSa(st0, i);
+    if (i == 0) sa_nx = rdSa(st0);
     pp[i] = v4f{0.f, 0.f, 0.f, 0.f};
   }
   bfirst = rdB(st0, 0);
@@ -291,12 +317,8 @@ __global__ __launch_bounds__(kNT) void k_gemm_fp8(GemmArgs p) {
           // a[i] is no longer needed for this chunk: fetch the next chunk's
           a[i] = rdA(nxt, i);
           if (i == 0) {
-            sa_nx[0] = rdSa(nxt, 0);
-            sa_nx[1] = rdSa(nxt, 1);
+            sa_nx = rdSa(nxt);
             if (!ROW) sbk_nx = sbk_all[min(c + 1, nk - 1)];
-          } else if (i == 1) {
-            sa_nx[2] = rdSa(nxt, 2);
-            sa_nx[3] = rdSa(nxt, 3);
           }
         }
         __builtin_amdgcn_sched_barrier(0);
