@@ -18,26 +18,30 @@
 namespace fp8q {
 
 // Non-temporal choices per access (see ld_stream16): the weight loads and
-// row codes (long streams of full segments) are non-temporal; activation
-// codes and the transposed codes (short scattered segments) stay cached so
-// that neighbouring segments merge in L2.
-constexpr int kNtActStore = 0, kNtWeightLoad = 1, kNtWeightStore = 1, kNtWeightTStore = 0, kNtTransStore = 0;
+// row codes (long streams of full segments) are non-temporal; the transposed
+// codes (short scattered segments) stay cached so that neighbouring segments
+// merge in L2; the activation quantizer uses plain accesses throughout.
+constexpr int kNtWeightLoad = 1, kNtWeightStore = 1, kNtWeightTStore = 0, kNtTransStore = 0;
 
 // ---------------------------------------------------------------------------
 // 1x128 activation tiles: 16 lanes (one DPP row) own one group, 8 elements per
-// lane; a wave covers a batch of 4 x kActU consecutive groups (kActU 16-byte
-// loads per lane) and walks the batches with a grid stride, the next batch's
-// loads issued before the current batch is converted.  The grid is sized to a
-// few workgroups per CU, all resident, so no tail round of workgroups is left.
+// lane; a wave covers 4 consecutive groups per step and U steps, so each lane
+// keeps U 16-byte loads in flight.
 constexpr int kActU = 4;
 
 template <class In>
-__device__ __forceinline__ void act_load(const typename In::elem* __restrict__ x, int64_t ld_x, int cols, int ngr,
-                                         int total, int batch, int team, int lig, float (&v)[kActU][8],
-                                         int (&grow)[kActU], int (&gcol)[kActU]) {
+__global__ __launch_bounds__(256) void k_quant_act(const typename In::elem* __restrict__ x, int64_t ld_x,
+                                                   uint8_t* __restrict__ q, int64_t ld_q,
+                                                   float* __restrict__ s, int64_t ld_s,
+                                                   int cols, int ngr, int total) {
+  const int lane = threadIdx.x & 63;
+  const int wave = (int)((blockIdx.x * (uint32_t)blockDim.x + threadIdx.x) >> 6);
+  const int team = lane >> 4, lig = lane & 15;
+  float v[kActU][8];
+  int grow[kActU], gcol[kActU];
 #pragma unroll
   for (int u = 0; u < kActU; ++u) {
-    const int g = (batch * kActU + u) * 4 + team;
+    const int g = (wave * kActU + u) * 4 + team;
     grow[u] = -1;
     gcol[u] = 0;
 #pragma unroll
@@ -57,56 +61,28 @@ __device__ __forceinline__ void act_load(const typename In::elem* __restrict__ x
       }
     }
   }
-}
-
-template <class In>
-__global__ __launch_bounds__(256) void k_quant_act(const typename In::elem* __restrict__ x, int64_t ld_x,
-                                                   uint8_t* __restrict__ q, int64_t ld_q,
-                                                   float* __restrict__ s, int64_t ld_s,
-                                                   int cols, int ngr, int total, int nbatch) {
-  const int lane = threadIdx.x & 63;
-  const int wave = (int)((blockIdx.x * (uint32_t)blockDim.x + threadIdx.x) >> 6);
-  const int nwaves = (int)(gridDim.x * (blockDim.x >> 6));
-  const int team = lane >> 4, lig = lane & 15;
-  float v[kActU][8], vn[kActU][8];
-  int grow[kActU], gcol[kActU], grown[kActU], gcoln[kActU];
-  int b = wave;
-  if (b < nbatch) act_load<In>(x, ld_x, cols, ngr, total, b, team, lig, v, grow, gcol);
-  for (; b < nbatch; b += nwaves) {
-    const bool more = b + nwaves < nbatch;
-    if (more) act_load<In>(x, ld_x, cols, ngr, total, b + nwaves, team, lig, vn, grown, gcoln);
 #pragma unroll
-    for (int u = 0; u < kActU; ++u) {
-      uint32_t m = 0;
+  for (int u = 0; u < kActU; ++u) {
+    uint32_t m = 0;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) m = max(m, abs_bits(v[u][e]));
-      m = row16_max_u32(m);  // all 16 lanes of the team share one group
-      const int r = grow[u];
-      if (r < 0) continue;
-      float sc, inv;
-      group_scale(__uint_as_float(m), sc, inv);
-      const uint32_t w0 = pack4_e4m3(v[u][0] * inv, v[u][1] * inv, v[u][2] * inv, v[u][3] * inv);
-      const uint32_t w1 = pack4_e4m3(v[u][4] * inv, v[u][5] * inv, v[u][6] * inv, v[u][7] * inv);
-      const int c0 = gcol[u];
-      uint8_t* qp = q + (int64_t)r * ld_q + c0;
-      if (c0 + 8 <= cols) {
-        st_stream8<kNtActStore>(qp, w0, w1);
-      } else {
+    for (int e = 0; e < 8; ++e) m = max(m, abs_bits(v[u][e]));
+    m = row16_max_u32(m);  // all 16 lanes of the team share one group
+    const int r = grow[u];
+    if (r < 0) continue;
+    float sc, inv;
+    group_scale(__uint_as_float(m), sc, inv);
+    const uint32_t w0 = pack4_e4m3(v[u][0] * inv, v[u][1] * inv, v[u][2] * inv, v[u][3] * inv);
+    const uint32_t w1 = pack4_e4m3(v[u][4] * inv, v[u][5] * inv, v[u][6] * inv, v[u][7] * inv);
+    const int c0 = gcol[u];
+    uint8_t* qp = q + (int64_t)r * ld_q + c0;
+    if (c0 + 8 <= cols) {
+      *reinterpret_cast<uint2*>(qp) = make_uint2(w0, w1);
+    } else {
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-          if (c0 + e < cols) qp[e] = (uint8_t)(((e < 4 ? w0 : w1) >> (8 * (e & 3))) & 0xFF);
-      }
-      if (lig == 0) s[(int64_t)r * ld_s + (c0 >> 7)] = sc;
+      for (int e = 0; e < 8; ++e)
+        if (c0 + e < cols) qp[e] = (uint8_t)(((e < 4 ? w0 : w1) >> (8 * (e & 3))) & 0xFF);
     }
-    if (more) {
-#pragma unroll
-      for (int u = 0; u < kActU; ++u) {
-        grow[u] = grown[u];
-        gcol[u] = gcoln[u];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) v[u][e] = vn[u][e];
-      }
-    }
+    if (lig == 0) s[(int64_t)r * ld_s + (c0 >> 7)] = sc;
   }
 }
 
@@ -114,19 +90,14 @@ hipError_t launch_quant_act(const void* x, bool x_bf16, int64_t rows, int64_t co
                             uint8_t* q, int64_t ld_q, float* s, int64_t ld_s, hipStream_t st) {
   const int64_t ngr = (cols + 127) / 128;
   const int64_t total = rows * ngr;
-  const int64_t nbatch = (total + 4 * kActU - 1) / (4 * kActU);
-  // one batch per wave up to 2^20 waves (measured faster than a persistent
-  // grid at these sizes); beyond, every wave walks the same number of batches
-  const int64_t max_waves = int64_t(1) << 20;
-  const int64_t per_wave = (nbatch + max_waves - 1) / max_waves;
-  const int64_t waves = (nbatch + per_wave - 1) / per_wave;
+  const int64_t waves = (total + 4 * kActU - 1) / (4 * kActU);
   const int64_t blocks = (waves + 3) / 4;
   if (x_bf16)
     hipLaunchKernelGGL(k_quant_act<BF16In>, dim3((uint32_t)blocks), dim3(256), 0, st,
-                       (const uint16_t*)x, ld_x, q, ld_q, s, ld_s, (int)cols, (int)ngr, (int)total, (int)nbatch);
+                       (const uint16_t*)x, ld_x, q, ld_q, s, ld_s, (int)cols, (int)ngr, (int)total);
   else
     hipLaunchKernelGGL(k_quant_act<F32In>, dim3((uint32_t)blocks), dim3(256), 0, st,
-                       (const float*)x, ld_x, q, ld_q, s, ld_s, (int)cols, (int)ngr, (int)total, (int)nbatch);
+                       (const float*)x, ld_x, q, ld_q, s, ld_s, (int)cols, (int)ngr, (int)total);
   return hipGetLastError();
 }
 
