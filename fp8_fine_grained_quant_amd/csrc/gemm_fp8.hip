@@ -218,7 +218,7 @@ __global__ __launch_bounds__(kNT) void k_gemm_fp8(GemmArgs p) {
 
   // state carried from chunk to chunk
   v8i a[kTM];           // A fragments of the current chunk
-  v8i bfirst;           // B fragment of the current chunk's column 0
+  v8i bring[3];         // B fragments, ring over the global column index 8c + j
   v4f pp[kTM];          // MFMA partials, ring indexed by slot % 4
   float sc[kTM][4];     // row scales (times the block's B scale) in use
   float sa_nx = 0.f;    // the next chunk's row scales, as read (one per lane)
@@ -266,7 +266,8 @@ __global__ __launch_bounds__(kNT) void k_gemm_fp8(GemmArgs p) {
     if (i == 0) sa_nx = rdSa(st0);
     pp[i] = v4f{0.f, 0.f, 0.f, 0.f};
   }
-  bfirst = rdB(st0, 0);
+  bring[0] = rdB(st0, 0);
+  bring[1] = rdB(st0, 1);
   if (ROW) sbc_first = rdSb(st0, 0);
   else sbk_nx = sbk_all[0];
 #pragma unroll
@@ -279,7 +280,7 @@ __global__ __launch_bounds__(kNT) void k_gemm_fp8(GemmArgs p) {
     uint8_t* const cur = u == 0 ? st0 : u == 1 ? st1 : st2;
     uint8_t* const nxt = u == 0 ? st1 : u == 1 ? st2 : st0;
     uint8_t* const fut = u == 0 ? st2 : u == 1 ? st0 : st1;
-    v8i bcur = bfirst, bnext;
+
     float sbc[kTN + 1];  // row mode: column scales of this chunk, [kTN] = next chunk's column 0
     sbc[0] = sbc_first;
 #pragma unroll
@@ -287,11 +288,19 @@ __global__ __launch_bounds__(kNT) void k_gemm_fp8(GemmArgs p) {
       // the B fragment (and column scale) of the next column: this chunk's
       // column j+1, or the next chunk's column 0 (published by the barrier
       // before the last column)
+      // B two columns ahead: this chunk's columns 2..7 at columns 0..5; the
+      // next chunk's columns 0 and 1 at column 7, after the barrier that
+      // publishes it (column 6 reads none)
+      const v8i bcur = bring[(2 * u + j) % 3];
+      if (j + 2 < kTN) {
+        bring[(2 * u + j + 2) % 3] = rdB(cur, j + 2);
+      } else if (j == kTN - 1) {
+        bring[(2 * u + kTN) % 3] = rdB(nxt, 0);
+        bring[(2 * u + kTN + 1) % 3] = rdB(nxt, 1);
+      }
       if (j + 1 < kTN) {
-        bnext = rdB(cur, j + 1);
         if (ROW) sbc[j + 1] = rdSb(cur, j + 1);
       } else {
-        bnext = rdB(nxt, 0);
         if (ROW) sbc[kTN] = rdSb(nxt, 0);
       }
       fence();
@@ -337,12 +346,10 @@ __global__ __launch_bounds__(kNT) void k_gemm_fp8(GemmArgs p) {
         __builtin_amdgcn_s_barrier();
         fence();
       }
-      bcur = bnext;
     }
     // slot 31 promoted row 0 of the last column: row 0 takes the next
     // chunk's scales now, rows 1-3 after their last promotion
     load_sc(0);
-    bfirst = bcur;
     sbc_prev = sbc[kTN - 1];
     sbc_first = sbc[kTN];
   };
