@@ -42,11 +42,16 @@ Readings taken where the pages are silent:
 * Wgrad operands are grouped 1x128 along the token (contraction) axis.
 * the GEMM result is defined as the exact contraction of the dequantized
   operands; the FP32 promotion every 128 K is how a kernel approaches it.
+* MoE backward (``grouped``): an expert's tokens are quantized on their own
+  for the weight gradient (no 128-token group mixes two experts), placed in
+  a token-padded layout whose chunks each belong to one expert.
 """
 
-from . import e4m3, quant, gemm  # noqa: F401
+from . import e4m3, quant, gemm, grouped  # noqa: F401
 from .e4m3 import decode, encode  # noqa: F401
 from .quant import (quant_act_1x128, quant_weight_128x128,  # noqa: F401
                     quant_transpose)
 from .gemm import (fprop_ref, dgrad_ref, wgrad_ref, grouped_ref,  # noqa: F401
                    exact_outputs)
+from .grouped import (quant_transpose_grouped, grouped_dgrad_ref,  # noqa: F401
+                      grouped_wgrad_ref, padded_starts, token_capacity)

@@ -22,6 +22,9 @@ projection and a 32-expert MoE layer):
   5 MoE Fprop      W_e [32,2048,7168] N(0,0.02); X [16384,7168] N(0,1) sorted
                    by expert; counts: 4 dead experts, Zipf(1.1) over the other
                    28, no non-zero count a multiple of 128
+  6 MoE backward   dY [16384,2048] Student-t(3), 164 token rows x100 (config 3's
+                   recipe at config 5's token count); the expert offsets,
+                   weights and X are config 5's
 """
 
 import numpy as np
@@ -72,6 +75,16 @@ def linear_dy(m=4096, n=2048):
     rng = rng_for(3)
     dy = rng.standard_t(3.0, size=(m, n))
     rows = rng.choice(m, size=round(0.01 * m), replace=False)
+    dy[rows, :] *= 100.0
+    return to_bf16(dy)
+
+
+def moe_dy(tokens=16384, n=2048):
+    """Config 6: dY bf16 [tokens, n] of the MoE layer, Student-t(3) with 1% of
+    the token rows x100."""
+    rng = rng_for(6)
+    dy = rng.standard_t(3.0, size=(tokens, n))
+    rows = rng.choice(tokens, size=round(0.01 * tokens), replace=False)
     dy[rows, :] *= 100.0
     return to_bf16(dy)
 

@@ -113,3 +113,59 @@ def test_sign_error_in_grouped_is_caught(monkeypatch):
         return -y, s
     monkeypatch.setattr(oracle, "grouped_ref", flipped)
     _fails(gemm_pins.check_grouped_pow2)
+
+
+# ----------------------------------------------------- grouped (MoE) backward
+import test_oracle_grouped as grouped_pins  # noqa: E402
+from oracle import grouped  # noqa: E402
+
+
+def test_overlapping_padded_layout_is_caught(monkeypatch):
+    """Padded starts without the per-expert extra chunk overlap."""
+    monkeypatch.setattr(grouped, "padded_starts",
+                        lambda off: 128 * (np.asarray(off, np.int64)[:-1] // 128))
+    monkeypatch.setattr(oracle, "padded_starts", grouped.padded_starts)
+    _fails(grouped_pins.test_padded_layout_never_overlaps)
+
+
+def test_groups_straddling_experts_are_caught(monkeypatch):
+    """Quantizing the concatenated tokens in global 128-token groups (a group
+    may mix two experts) instead of each expert on its own."""
+    def straddling(x, offsets):
+        q_all, s_all = quant.quant_transpose(x)
+        off = np.asarray(offsets, np.int64)
+        cap = grouped.token_capacity(off[-1], len(off) - 1)
+        q_t = np.zeros((x.shape[1], cap), np.uint8)
+        s_t = np.zeros((x.shape[1], cap // 128), np.float32)
+        for e, p in enumerate(grouped.padded_starts(off)):
+            lo, hi = int(off[e]), int(off[e + 1])
+            q_t[:, p:p + hi - lo] = q_all[:, lo:hi]
+            for j in range(-(-(hi - lo) // 128)):
+                s_t[:, p // 128 + j] = s_all[:, min((lo + 128 * j) // 128, s_all.shape[1] - 1)]
+        return q_t, s_t, np.ones(cap, bool), np.ones(cap // 128, bool)
+
+    monkeypatch.setattr(oracle, "quant_transpose_grouped", straddling)
+    _fails(grouped_pins.test_grouped_transpose_matches_exact_rederivation)
+
+
+def test_dgrad_with_first_expert_scales_is_caught(monkeypatch):
+    """Using expert 0's block scales for every expert."""
+    real = oracle.grouped_dgrad_ref
+
+    def wrong(dyq, dys, wq_t, ws, offsets):
+        n = dyq.shape[1]
+        return real(dyq, dys, wq_t, np.tile(ws[:n // 128], (len(offsets) - 1, 1)), offsets)
+
+    monkeypatch.setattr(oracle, "grouped_dgrad_ref", wrong)
+    _fails(grouped_pins.test_grouped_dgrad_closed_form)
+
+
+def test_wgrad_chunk_offset_error_is_caught(monkeypatch):
+    """Reading an expert's token scales one chunk late."""
+    real = oracle.grouped_wgrad_ref
+
+    def shifted(dyq_t, dys_t, xq_t, xs_t, offsets):
+        return real(dyq_t, np.roll(dys_t, 1, axis=1), xq_t, xs_t, offsets)
+
+    monkeypatch.setattr(oracle, "grouped_wgrad_ref", shifted)
+    _fails(grouped_pins.test_grouped_wgrad_closed_form)
