@@ -38,7 +38,8 @@ _STATUS = ["FP8Q_OK", "FP8Q_ERR_NULL", "FP8Q_ERR_SHAPE", "FP8Q_ERR_STRIDE",
 EXPORTS = ["fp8q_status_string", "fp8q_quant_act_1x128", "fp8q_quant_weight_128x128",
            "fp8q_quant_transpose", "fp8q_gemm_fprop", "fp8q_gemm_dgrad", "fp8q_gemm_wgrad",
            "fp8q_grouped_gemm", "fp8q_gemm_fprop_exact", "fp8q_gemm_dgrad_exact", "fp8q_gemm_wgrad_exact",
-           "fp8q_grouped_gemm_exact"]
+           "fp8q_grouped_gemm_exact", "fp8q_quant_transpose_grouped", "fp8q_grouped_gemm_dgrad",
+           "fp8q_grouped_gemm_wgrad"]
 
 
 class Fp8qError(RuntimeError):
@@ -68,6 +69,9 @@ def load_library(path=LIB_PATH):
         "fp8q_gemm_dgrad": ([P, P, P, P, I64, I64, I64, P, I32, I64, P], I32),
         "fp8q_gemm_wgrad": ([P, P, P, P, I64, I64, I64, P, I64, I32, P], I32),
         "fp8q_grouped_gemm": ([P, P, P, P, P, I64, I64, I64, I64, P, I32, I64, P], I32),
+        "fp8q_quant_transpose_grouped": ([P, I32, I64, I64, I64, P, I64, P, I64, P, I64, P], I32),
+        "fp8q_grouped_gemm_dgrad": ([P, P, P, P, P, I64, I64, I64, I64, P, I32, I64, P], I32),
+        "fp8q_grouped_gemm_wgrad": ([P, P, P, P, P, I64, I64, I64, I64, I64, P, I32, P], I32),
     }
     for name in ["fp8q_gemm_fprop", "fp8q_gemm_dgrad", "fp8q_gemm_wgrad", "fp8q_grouped_gemm"]:
         sig[name + "_exact"] = sig[name]
@@ -200,6 +204,53 @@ def fp8q_grouped_gemm(xq, xs, wq, ws, offsets, y, stream=None, exact=False):
            "fp8q_grouped_gemm")
 
 
+def fp8q_quant_transpose_grouped(x, offsets, q_t, scale_t, stream=None):
+    _on_gpu(x, offsets, q_t, scale_t)
+    _contig(offsets)
+    if offsets.dtype != torch.int32:
+        raise TypeError("offsets are int32")
+    rows, cols = x.shape
+    e = offsets.shape[0] - 1
+    _check(load_library().fp8q_quant_transpose_grouped(_ptr(x), _dtype_code(x), rows, cols, _ld(x),
+                                                        _ptr(offsets), e, _ptr(q_t), _ld(q_t), _ptr(scale_t),
+                                                        _ld(scale_t), _stream(stream)),
+           "fp8q_quant_transpose_grouped")
+
+
+def fp8q_grouped_gemm_dgrad(dyq, dys, wq_t, ws, offsets, dx, stream=None):
+    """wq_t [K, E*N], ws [E*N/128, K/128] (quant_weight_128x128 of the stacked
+    weights [E*N, K])."""
+    _on_gpu(dyq, dys, wq_t, ws, offsets, dx)
+    _contig(dyq, dys, wq_t, ws, offsets)
+    if offsets.dtype != torch.int32:
+        raise TypeError("offsets are int32")
+    m_total, n = dyq.shape
+    k = wq_t.shape[0]
+    e = offsets.shape[0] - 1
+    _check(load_library().fp8q_grouped_gemm_dgrad(_ptr(dyq), _ptr(dys), _ptr(wq_t), _ptr(ws), _ptr(offsets), e,
+                                                   m_total, n, k, _ptr(dx), _dtype_code(dx), _ld(dx),
+                                                   _stream(stream)),
+           "fp8q_grouped_gemm_dgrad")
+
+
+def fp8q_grouped_gemm_wgrad(dyq_t, dys_t, xq_t, xs_t, offsets, m_total, dw, accumulate=False, stream=None):
+    """Token-padded operands [N, ld_t] / [K, ld_t] (quant_transpose_grouped);
+    dw [E, N, K] FP32 contiguous."""
+    _on_gpu(dyq_t, dys_t, xq_t, xs_t, offsets, dw)
+    _contig(dyq_t, dys_t, xq_t, xs_t, offsets, dw)
+    if offsets.dtype != torch.int32 or dw.dtype != torch.float32:
+        raise TypeError("offsets are int32 and dW is FP32")
+    n, ld_t = dyq_t.shape
+    k = xq_t.shape[0]
+    e = offsets.shape[0] - 1
+    if xq_t.shape[1] != ld_t or dys_t.shape[1] * 128 != ld_t or xs_t.shape[1] * 128 != ld_t:
+        raise ValueError("the four operands share one padded token stride")
+    _check(load_library().fp8q_grouped_gemm_wgrad(_ptr(dyq_t), _ptr(dys_t), _ptr(xq_t), _ptr(xs_t), _ptr(offsets),
+                                                   e, m_total, n, k, ld_t, _ptr(dw), int(bool(accumulate)),
+                                                   _stream(stream)),
+           "fp8q_grouped_gemm_wgrad")
+
+
 # ---------------------------------------------------------------- convenience
 def _cdiv(a, b):
     return (a + b - 1) // b
@@ -254,3 +305,32 @@ def grouped_gemm(xq, xs, wq, ws, offsets, out_dtype=torch.bfloat16, stream=None,
     y = torch.empty((xq.shape[0], wq.shape[1]), dtype=out_dtype, device=xq.device)
     fp8q_grouped_gemm(xq, xs, wq, ws, offsets, y, stream, exact)
     return y
+
+
+def token_capacity(m_total, experts):
+    """Padded token capacity of the grouped weight-gradient operands."""
+    return 128 * (m_total // 128 + experts)
+
+
+def quant_transpose_grouped(x, offsets, stream=None):
+    rows, cols = x.shape
+    cap = token_capacity(rows, offsets.shape[0] - 1)
+    q_t = torch.zeros((cols, cap), dtype=torch.uint8, device=x.device)
+    s_t = torch.zeros((cols, cap // 128), dtype=torch.float32, device=x.device)
+    fp8q_quant_transpose_grouped(x, offsets, q_t, s_t, stream)
+    return q_t, s_t
+
+
+def grouped_gemm_dgrad(dyq, dys, wq_t, ws, offsets, out_dtype=torch.bfloat16, stream=None):
+    dx = torch.empty((dyq.shape[0], wq_t.shape[0]), dtype=out_dtype, device=dyq.device)
+    fp8q_grouped_gemm_dgrad(dyq, dys, wq_t, ws, offsets, dx, stream)
+    return dx
+
+
+def grouped_gemm_wgrad(dyq_t, dys_t, xq_t, xs_t, offsets, m_total, dw=None, stream=None):
+    accumulate = dw is not None
+    if dw is None:
+        dw = torch.empty((offsets.shape[0] - 1, dyq_t.shape[0], xq_t.shape[0]), dtype=torch.float32,
+                         device=dyq_t.device)
+    fp8q_grouped_gemm_wgrad(dyq_t, dys_t, xq_t, xs_t, offsets, m_total, dw, accumulate, stream)
+    return dw

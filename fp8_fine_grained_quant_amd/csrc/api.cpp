@@ -99,6 +99,22 @@ fp8q_status fp8q_quant_transpose(const void* x, fp8q_dtype xt, int64_t rows, int
       fp8q::launch_quant_transpose(x, xt == FP8Q_BF16, rows, cols, ld_x, q_t, ld_qt, scale_t, ld_st, stream));
 }
 
+fp8q_status fp8q_quant_transpose_grouped(const void* x, fp8q_dtype xt, int64_t rows, int64_t cols, int64_t ld_x,
+                                         const int32_t* offsets, int64_t E, uint8_t* q_t, int64_t ld_qt,
+                                         float* scale_t, int64_t ld_st, hipStream_t stream) {
+  if (!valid_dtype(xt)) return FP8Q_ERR_DTYPE;
+  if (E < 1 || E > 65536) return FP8Q_ERR_SHAPE;
+  if (rows < 0 || rows > kMaxDim) return FP8Q_ERR_SHAPE;
+  const int64_t cap = 128 * (rows / 128 + E);  // padded token capacity
+  const fp8q_status c = check_quant(x, esize(xt), rows, cols, ld_x, q_t, ld_qt, cap, scale_t, ld_st, cap / 128);
+  if (c != FP8Q_OK || rows == 0 || cols == 0) return c;
+  if (!offsets) return FP8Q_ERR_NULL;
+  if (!aligned4(offsets)) return FP8Q_ERR_ALIGN;
+  if (cap / 128 > 65535) return FP8Q_ERR_SHAPE;  // grid y limit
+  return launched(fp8q::launch_quant_transpose_grouped(x, xt == FP8Q_BF16, rows, cols, ld_x, offsets, E, q_t, ld_qt,
+                                                       scale_t, ld_st, stream));
+}
+
 }  // extern "C"
 
 static fp8q_status fp8q_gemm_fprop_impl(int exact, const uint8_t* xq, const float* xs, const uint8_t* wq, const float* ws,
@@ -191,6 +207,64 @@ static fp8q_status fp8q_grouped_gemm_impl(int exact, const uint8_t* xq, const fl
 
 
 extern "C" {
+
+fp8q_status fp8q_grouped_gemm_dgrad(const uint8_t* dyq, const float* dys, const uint8_t* wq_t, const float* ws,
+                                    const int32_t* offsets, int64_t E, int64_t M_total, int64_t N, int64_t K,
+                                    void* dx, fp8q_dtype dxt, int64_t ld_dx, hipStream_t stream) {
+  if (E < 1 || E > 65536) return FP8Q_ERR_SHAPE;
+  if (M_total < 0 || N < 0 || K < 0 || M_total > kMaxDim || N > kMaxDim || K > kMaxDim) return FP8Q_ERR_SHAPE;
+  if (N % 128 != 0 || K % 128 != 0 || N > kMaxContraction || E * N > kMaxDim) return FP8Q_ERR_SHAPE;
+  if (!valid_dtype(dxt)) return FP8Q_ERR_DTYPE;
+  if (M_total == 0 || K == 0) return FP8Q_OK;
+  if (N == 0) return FP8Q_ERR_SHAPE;
+  if (!dyq || !dys || !wq_t || !ws || !offsets) return FP8Q_ERR_NULL;
+  const fp8q_status c = check_gemm_out(dx, dxt, ld_dx, K);
+  if (c != FP8Q_OK) return c;
+  if (!aligned16(dyq) || !aligned16(wq_t) || !aligned4(dys) || !aligned4(ws) || !aligned4(offsets))
+    return FP8Q_ERR_ALIGN;
+  if ((M_total / 256 + E) * (K / 128) > kMaxGroups) return FP8Q_ERR_SHAPE;
+  // Per expert: the Dgrad NT form (A = dY rows of the expert, contraction N)
+  // with B = W_e^T = columns [eN, (e+1)N) of the stacked transposed codes
+  // [K, E*N], and the block scale of (output column k, chunk kb) at
+  // ws[e*N/128 + kb, k/128].
+  GemmArgs a{};
+  a.A = dyq; a.B = wq_t; a.sa = dys; a.sb = ws; a.C = dx;
+  a.lda = N; a.ldb = E * N; a.ld_sa = N / 128; a.sb_rs = 1; a.sb_cs = K / 128; a.ldc = ld_dx;
+  a.M = M_total; a.N = K; a.K = N;
+  a.sb_mode = fp8q::kSbBlock; a.out_f32 = dxt == FP8Q_F32; a.accumulate = 0; a.exact = 0;
+  a.offsets = offsets; a.E = E; a.b_estride = N; a.sb_estride = (N / 128) * (K / 128);
+  return launched(fp8q::launch_gemm(a, stream));
+}
+
+fp8q_status fp8q_grouped_gemm_wgrad(const uint8_t* dyq_t, const float* dys_t, const uint8_t* xq_t,
+                                    const float* xs_t, const int32_t* offsets, int64_t E, int64_t M_total,
+                                    int64_t N, int64_t K, int64_t ld_t, float* dw, int accumulate,
+                                    hipStream_t stream) {
+  if (E < 1 || E > 65536) return FP8Q_ERR_SHAPE;
+  if (M_total < 0 || N < 0 || K < 0 || M_total > kMaxDim || N > kMaxDim || K > kMaxDim) return FP8Q_ERR_SHAPE;
+  if (K % 128 != 0 || M_total > kMaxContraction) return FP8Q_ERR_SHAPE;
+  if (accumulate != 0 && accumulate != 1) return FP8Q_ERR_SHAPE;
+  if (N == 0 || K == 0) return FP8Q_OK;
+  if (!dyq_t || !dys_t || !xq_t || !xs_t || !offsets || !dw) return FP8Q_ERR_NULL;
+  const int64_t cap = 128 * (M_total / 128 + E);
+  if (ld_t < cap) return FP8Q_ERR_STRIDE;
+  if (ld_t % 128 != 0) return FP8Q_ERR_ALIGN;
+  if (!aligned16(dyq_t) || !aligned16(xq_t) || !aligned16(dw) || !aligned4(dys_t) || !aligned4(xs_t) ||
+      !aligned4(offsets))
+    return FP8Q_ERR_ALIGN;
+  if (E * ((N + 255) / 256) * (K / 128) > kMaxGroups) return FP8Q_ERR_SHAPE;
+  // Per expert: the Wgrad NT form over the expert's padded token chunks
+  // (A = dY^T codes [N, ld_t], B = X^T codes [K, ld_t], one scale per row
+  // per chunk), written to dw + e*N*K.
+  GemmArgs a{};
+  a.A = dyq_t; a.B = xq_t; a.sa = dys_t; a.sb = xs_t; a.C = dw;
+  a.lda = ld_t; a.ldb = ld_t; a.ld_sa = ld_t / 128; a.sb_rs = ld_t / 128; a.sb_cs = 1; a.ldc = K;
+  a.M = N; a.N = K; a.K = ld_t;
+  a.sb_mode = fp8q::kSbRow; a.out_f32 = 1; a.accumulate = accumulate; a.exact = 0;
+  a.offsets = offsets; a.E = E; a.b_estride = 0; a.sb_estride = 0;
+  a.k_grouped = 1; a.c_estride = N * K;
+  return launched(fp8q::launch_gemm(a, stream));
+}
 
 fp8q_status fp8q_gemm_fprop(const uint8_t* xq, const float* xs, const uint8_t* wq, const float* ws, int64_t M,
                             int64_t N, int64_t K, void* y, fp8q_dtype yt, int64_t ld_y, hipStream_t stream) {

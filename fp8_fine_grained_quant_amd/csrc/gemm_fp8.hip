@@ -109,7 +109,7 @@ __device__ __forceinline__ void row_scales(float v, float k, float (&out)[4]) {
 
 }  // namespace
 
-template <int SB_MODE, int OUT_F32, bool GROUPED>
+template <int SB_MODE, int OUT_F32, bool GROUPED, bool KG>
 __global__ __launch_bounds__(kNT) void k_gemm_fp8(GemmArgs p) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
   typedef Stage<SB_MODE> S;
@@ -125,7 +125,16 @@ __global__ __launch_bounds__(kNT) void k_gemm_fp8(GemmArgs p) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, g = lane >> 4;
-  const int nk = (int)(p.K / kBK);
+  // chunks of the contraction this tile runs over: all of K, or (grouped
+  // contraction) the expert's padded chunks starting at chunk cb
+  int nk = (int)(p.K / kBK), cb = 0;
+  if (KG) {
+    const int lo = p.offsets[tc.e], hi = p.offsets[tc.e + 1];
+    nk = (hi - lo + kBK - 1) / kBK;
+    cb = lo / kBK + tc.e;
+  }
+  GemmArgs po = p;  // the output this tile writes (grouped contraction: the expert's own)
+  if (KG) po.C = reinterpret_cast<float*>(p.C) + (int64_t)tc.e * p.c_estride;
   const uint8_t* Bp = p.B + (GROUPED ? (int64_t)tc.e * p.b_estride : 0);
   const float* sbp = p.sb + (GROUPED ? (int64_t)tc.e * p.sb_estride : 0);
   const int rows = (int)min(tc.mend - tc.m0, (int64_t)kBM);  // valid rows of the tile, >= 1
@@ -153,6 +162,7 @@ __global__ __launch_bounds__(kNT) void k_gemm_fp8(GemmArgs p) {
   constexpr int kDma = kIA + kIB + 1 + (ROW ? 1 : 0);
   // the d-th direct load of chunk kb into stage st
   auto issue_one = [&](int kb, uint8_t* st, int d) {
+    kb += cb;
     const uint32_t ka = (uint32_t)kb * kBK;
     if (d < kIA) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, (lds_ptr)(st + S::a + (w * kIA + d) * 1024), 16,
@@ -215,6 +225,11 @@ __global__ __launch_bounds__(kNT) void k_gemm_fp8(GemmArgs p) {
     for (int j = 0; j < kTN; ++j)
 #pragma unroll
       for (int r = 0; r < 4; ++r) acc[i][j][r] = 0.f;
+  if (KG && nk == 0) {
+    // an expert without tokens: its gradient is zero
+    if (!p.accumulate) store_tile<kTM, kTN, OUT_F32, OUT_F32 ? 16 : 32>(acc, st0 + w * 12288, po, tc.m0 + w * 64, tc.mend, tc.n0, lane);
+    return;
+  }
 
   // state carried from chunk to chunk
   v8i a[kTM];           // A fragments of the current chunk
@@ -371,26 +386,30 @@ __global__ __launch_bounds__(kNT) void k_gemm_fp8(GemmArgs p) {
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   __builtin_amdgcn_s_barrier();
   fence();
-  store_tile<kTM, kTN, OUT_F32, OUT_F32 ? 16 : 32>(acc, st0 + w * 12288, p, tc.m0 + w * 64, tc.mend, tc.n0, lane);
+  store_tile<kTM, kTN, OUT_F32, OUT_F32 ? 16 : 32>(acc, st0 + w * 12288, po, tc.m0 + w * 64, tc.mend, tc.n0, lane);
 #endif  // __HIP_DEVICE_COMPILE__
 }
 
 namespace {
 
-template <int SB_MODE, int OUT_F32, bool GROUPED>
+template <int SB_MODE, int OUT_F32, bool GROUPED, bool KG = false>
 hipError_t launch_one(const GemmArgs& a, hipStream_t st) {
-  const int64_t tiles_n = a.N / kBN;
-  const int64_t tiles = GROUPED ? ((a.M + kBM - 1) / kBM + a.E) * tiles_n  // upper bound: a partial tile per expert
-                                : ((a.M + kBM - 1) / kBM) * tiles_n;
+  const int64_t tiles_n = a.N / kBN, tiles_m = (a.M + kBM - 1) / kBM;
+  const int64_t tiles = KG ? a.E * tiles_m * tiles_n                     // every expert: a full grid
+                        : GROUPED ? (tiles_m + a.E) * tiles_n             // upper bound: a partial tile per expert
+                                  : tiles_m * tiles_n;
   if (tiles <= 0) return hipSuccess;
-  hipLaunchKernelGGL((k_gemm_fp8<SB_MODE, OUT_F32, GROUPED>), dim3((uint32_t)tiles), dim3(kNT), 0, st, a);
+  hipLaunchKernelGGL((k_gemm_fp8<SB_MODE, OUT_F32, GROUPED, KG>), dim3((uint32_t)tiles), dim3(kNT), 0, st, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_gemm_fp8(const GemmArgs& a, hipStream_t st) {
-  if (a.sb_mode == kSbRow) return launch_one<kSbRow, 1, false>(a, st);  // weight gradient: FP32 out
+  if (a.sb_mode == kSbRow) {  // weight gradients: FP32 out
+    if (a.k_grouped) return launch_one<kSbRow, 1, true, true>(a, st);
+    return launch_one<kSbRow, 1, false>(a, st);
+  }
   if (a.offsets != nullptr)
     return a.out_f32 ? launch_one<kSbBlock, 1, true>(a, st) : launch_one<kSbBlock, 0, true>(a, st);
   return a.out_f32 ? launch_one<kSbBlock, 1, false>(a, st) : launch_one<kSbBlock, 0, false>(a, st);

@@ -41,7 +41,25 @@ __device__ __forceinline__ bool tile_coord(const GemmArgs& p, TileCoord& tc) {
     tc.e = 0;
     return true;
   }
-  // grouped: walk the experts' tile counts; tiles never straddle experts
+  if (p.k_grouped) {
+    // grouped contraction: every expert owns a full M x N grid of tiles, in
+    // the plain band order
+    const int tiles_m = (int)((p.M + BM - 1) / BM);
+    const int per_e = tiles_m * tiles_n;
+    const int e = t / per_e;
+    if (e >= (int)p.E) return false;
+    const int tl = t - e * per_e;
+    const int band = kGroupM * tiles_n;
+    const int b = tl / band, first_m = b * kGroupM;
+    const int gm = min(tiles_m - first_m, kGroupM);
+    const int in_band = tl - b * band;
+    tc.m0 = (int64_t)(first_m + in_band % gm) * BM;
+    tc.n0 = (in_band / gm) * BN;
+    tc.mend = p.M;
+    tc.e = e;
+    return true;
+  }
+  // grouped rows: walk the experts' tile counts; tiles never straddle experts
   int64_t base = 0, lo = 0, hi = 0, mt = 0;
   int e = 0;
   for (; e < (int)p.E; ++e) {

@@ -17,6 +17,13 @@ hipError_t launch_quant_weight(const void* w, bool w_bf16, int64_t rows, int64_t
 hipError_t launch_quant_transpose(const void* x, bool x_bf16, int64_t rows, int64_t cols, int64_t ld_x,
                                   uint8_t* q_t, int64_t ld_qt, float* s_t, int64_t ld_st, hipStream_t st);
 
+// Per expert e (rows [offsets[e], offsets[e+1]) of x), the quantize-transpose
+// of that block alone, written at padded token column 128*(offsets[e]/128 + e);
+// the tail of an expert's last 128-token chunk is written as code 0.
+hipError_t launch_quant_transpose_grouped(const void* x, bool x_bf16, int64_t rows, int64_t cols, int64_t ld_x,
+                                          const int32_t* offsets, int64_t E, uint8_t* q_t, int64_t ld_qt,
+                                          float* s_t, int64_t ld_st, hipStream_t st);
+
 // How the scale of the B operand (rows = output columns) is indexed.
 enum SbMode : int {
   kSbBlock = 0,  // one scale per 128 output columns per chunk: sb[(n/128)*sb_rs + kb*sb_cs]
@@ -41,6 +48,11 @@ struct GemmArgs {
   // grouped: rows [offsets[e], offsets[e+1]) use B + e*b_estride, sb + e*sb_estride
   const int32_t* offsets;  // NULL for a plain GEMM
   int64_t E, b_estride, sb_estride;
+  // grouped contraction (k_grouped = 1): expert e contracts over the padded
+  // chunks [offsets[e]/128 + e, + ceil(m_e/128)) of A and B (token-padded
+  // operands), and writes its own output C + e*c_estride; M, N are per expert
+  int k_grouped;
+  int64_t c_estride;
 };
 
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t st);

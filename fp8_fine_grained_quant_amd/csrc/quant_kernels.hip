@@ -220,16 +220,35 @@ hipError_t launch_quant_weight(const void* w, bool w_bf16, int64_t rows, int64_t
 // reduced over the 16 threads of a channel (xor 16/32 inside the wave, LDS
 // across the 4 waves), and each channel's 8 codes are converted pairwise
 // down the column, so they leave as one 8-byte segment of the q_t row.
-template <class In>
+template <class In, bool G>
 __global__ __launch_bounds__(256) void k_quant_transpose(const typename In::elem* __restrict__ x, int64_t ld_x,
                                                          int rows, int cols,
                                                          uint8_t* __restrict__ qt, int64_t ld_qt,
-                                                         float* __restrict__ st, int64_t ld_st) {
+                                                         float* __restrict__ st, int64_t ld_st,
+                                                         const int32_t* __restrict__ offsets, int E) {
   __shared__ uint32_t red[4][128];
   const int t = threadIdx.x;
   const int c8 = t & 15, rblk = t >> 4;
   const int bi = blockIdx.y, bj = blockIdx.x;
-  const int r0 = bi * 128 + rblk * 8;
+  // Output chunk bi (token columns [128 bi, 128 bi + 128) of q_t) comes from
+  // input rows [rlo, rlo + 128), of which those below rhi exist.
+  int rlo = bi * 128, rhi = rows;
+  if (G) {
+    // the expert whose padded chunks [start_e, start_e + ceil(m_e/128)) hold
+    // bi, start_e = offsets[e]/128 + e (strictly increasing in e)
+    int lo = 0, hi = E - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (offsets[mid] / 128 + mid <= bi) lo = mid;
+      else hi = mid - 1;
+    }
+    const int o0 = offsets[lo], o1 = offsets[lo + 1], start = o0 / 128 + lo;
+    if (bi < start || bi >= start + (o1 - o0 + 127) / 128) return;  // a chunk no expert owns
+    rlo = o0 + 128 * (bi - start);
+    rhi = o1;
+  }
+  const int r0 = rlo + rblk * 8;           // first input row of this thread
+  const int oc0 = bi * 128 + rblk * 8;     // its output token column
   const int c0 = bj * 128 + c8 * 8;
   float v[8][8];
 #pragma unroll
@@ -237,7 +256,7 @@ __global__ __launch_bounds__(256) void k_quant_transpose(const typename In::elem
     const int r = r0 + i;
 #pragma unroll
     for (int e = 0; e < 8; ++e) v[i][e] = 0.f;
-    if (r < rows) {
+    if (r < rhi) {
       const typename In::elem* p = x + (int64_t)r * ld_x + c0;
       if (c0 + 8 <= cols) {
         In::template load8<0>(p, v[i]);
@@ -273,14 +292,16 @@ __global__ __launch_bounds__(256) void k_quant_transpose(const typename In::elem
     group_scale(__uint_as_float(a), sc, inv[e]);
     if (rblk == 0 && c0 + e < cols) st[(int64_t)(c0 + e) * ld_st + bi] = sc;
   }
-  const bool full_r = r0 + 8 <= rows;
+  // grouped: rows past the expert's end are padding, stored as code 0 (their
+  // values were loaded as 0)
+  const bool full_r = G || r0 + 8 <= rows;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     const int c = c0 + e;
     if (c >= cols) break;
     const uint32_t d0 = pack4_e4m3(v[0][e] * inv[e], v[1][e] * inv[e], v[2][e] * inv[e], v[3][e] * inv[e]);
     const uint32_t d1 = pack4_e4m3(v[4][e] * inv[e], v[5][e] * inv[e], v[6][e] * inv[e], v[7][e] * inv[e]);
-    uint8_t* tp = qt + (int64_t)c * ld_qt + r0;
+    uint8_t* tp = qt + (int64_t)c * ld_qt + oc0;
     if (full_r) {
       st_stream8<kNtTransStore>(tp, d0, d1);
     } else {
@@ -295,11 +316,25 @@ hipError_t launch_quant_transpose(const void* x, bool x_bf16, int64_t rows, int6
                                   uint8_t* q_t, int64_t ld_qt, float* s_t, int64_t ld_st, hipStream_t st) {
   const dim3 grid((uint32_t)((cols + 127) / 128), (uint32_t)((rows + 127) / 128));
   if (x_bf16)
-    hipLaunchKernelGGL(k_quant_transpose<BF16In>, grid, dim3(256), 0, st, (const uint16_t*)x, ld_x, (int)rows,
-                       (int)cols, q_t, ld_qt, s_t, ld_st);
+    hipLaunchKernelGGL((k_quant_transpose<BF16In, false>), grid, dim3(256), 0, st, (const uint16_t*)x, ld_x,
+                       (int)rows, (int)cols, q_t, ld_qt, s_t, ld_st, nullptr, 0);
   else
-    hipLaunchKernelGGL(k_quant_transpose<F32In>, grid, dim3(256), 0, st, (const float*)x, ld_x, (int)rows,
-                       (int)cols, q_t, ld_qt, s_t, ld_st);
+    hipLaunchKernelGGL((k_quant_transpose<F32In, false>), grid, dim3(256), 0, st, (const float*)x, ld_x,
+                       (int)rows, (int)cols, q_t, ld_qt, s_t, ld_st, nullptr, 0);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_transpose_grouped(const void* x, bool x_bf16, int64_t rows, int64_t cols, int64_t ld_x,
+                                          const int32_t* offsets, int64_t E, uint8_t* q_t, int64_t ld_qt,
+                                          float* s_t, int64_t ld_st, hipStream_t st) {
+  // one block per padded 128-token chunk of the capacity 128*(rows/128 + E)
+  const dim3 grid((uint32_t)((cols + 127) / 128), (uint32_t)(rows / 128 + E));
+  if (x_bf16)
+    hipLaunchKernelGGL((k_quant_transpose<BF16In, true>), grid, dim3(256), 0, st, (const uint16_t*)x, ld_x,
+                       (int)rows, (int)cols, q_t, ld_qt, s_t, ld_st, offsets, (int)E);
+  else
+    hipLaunchKernelGGL((k_quant_transpose<F32In, true>), grid, dim3(256), 0, st, (const float*)x, ld_x,
+                       (int)rows, (int)cols, q_t, ld_qt, s_t, ld_st, offsets, (int)E);
   return hipGetLastError();
 }
 

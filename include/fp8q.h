@@ -176,6 +176,67 @@ fp8q_status fp8q_grouped_gemm(const uint8_t* xq, const float* xs, const uint8_t*
                               void* y, fp8q_dtype yt, int64_t ld_y, hipStream_t stream);
 
 /*
+ * MoE backward.  The MoE layers' GEMMs run in FP8 like the dense ones (the
+ * innerforce.co.kr excerpt of the DeepSeek-V3 report, the FP8 framework
+ * paragraph), with the dense layer's operands per product ("DeepSeek FP8
+ * Training", input- and weight-gradient lists).  The expert layouts are this
+ * library's own; the pages give no grouped algorithm.  `offsets` is as for
+ * fp8q_grouped_gemm (DEVICE int32 [E+1], never read on the host).
+ *
+ * Token-padded layout of the weight-gradient operands: the tokens of expert
+ * e (rows [o_e, o_{e+1}) of the input) occupy token columns [p_e, p_e + m_e)
+ * with p_e = 128 * (o_e / 128 + e) (integer division), so that no 128-token
+ * group mixes two experts; the columns from p_e + m_e to the end of that
+ * 128-token chunk hold code 0.  The padded axis has capacity
+ * cap = 128 * (M_total / 128 + E); columns owned by no expert are not written.
+ */
+
+/*
+ * Grouped quantize + transpose: fp8q_quant_transpose applied to every
+ * expert's block of rows on its own (a trailing partial group uses only the
+ * expert's tokens), written in the token-padded layout.
+ *   x       : [rows = M_total, cols] BF16 or FP32, stride ld_x
+ *   q_t     : [cols, ld_qt] E4M3 codes, ld_qt >= cap (multiple of 16)
+ *   scale_t : [cols, ld_st] FP32, ld_st >= cap / 128; chunk j = token
+ *             columns [128j, 128j + 128)
+ * Rules: 1 <= E <= 65536, cap / 128 <= 65535.
+ */
+fp8q_status fp8q_quant_transpose_grouped(const void* x, fp8q_dtype xt, int64_t rows, int64_t cols, int64_t ld_x,
+                                         const int32_t* offsets, int64_t E, uint8_t* q_t, int64_t ld_qt,
+                                         float* scale_t, int64_t ld_st, hipStream_t stream);
+
+/*
+ * Grouped Dgrad: for every expert e, rows [o_e, o_{e+1}) of dX are
+ * dY[o_e:o_{e+1}, :] . W_e.
+ *   dyq  : [M_total, N] codes (1x128 groups along N), dys : [M_total, N/128]
+ *   wq_t : [K, E*N] codes = the q_t output of fp8q_quant_weight_128x128 on the
+ *          stacked weights [E*N, K]; W_e^T is columns [eN, (e+1)N)
+ *   ws   : the SAME [E*N/128, K/128] scale array of that call
+ *   dx   : [M_total, K] of type dxt, row stride ld_dx (rules as fp8q_gemm_dgrad)
+ * Rules: N % 128 == 0, K % 128 == 0, 1 <= E <= 65536, E*N < 2^31.
+ */
+fp8q_status fp8q_grouped_gemm_dgrad(const uint8_t* dyq, const float* dys, const uint8_t* wq_t, const float* ws,
+                                    const int32_t* offsets, int64_t E, int64_t M_total, int64_t N, int64_t K,
+                                    void* dx, fp8q_dtype dxt, int64_t ld_dx, hipStream_t stream);
+
+/*
+ * Grouped Wgrad: dW_e (= or +=) dY[o_e:o_{e+1}]^T . X[o_e:o_{e+1}] for every
+ * expert, a contraction over that expert's own tokens.
+ *   dyq_t, dys_t : fp8q_quant_transpose_grouped of dY [M_total, N]
+ *                  ([N, ld_t] codes, [N, ld_t/128] scales)
+ *   xq_t,  xs_t  : fp8q_quant_transpose_grouped of X [M_total, K]
+ *                  ([K, ld_t] codes, [K, ld_t/128] scales)
+ *   ld_t : the padded token stride of all four, ld_t >= cap, ld_t % 128 == 0
+ *   dw   : [E, N, K] FP32, contiguous; an expert with no tokens gets 0
+ *          (accumulate = 0) or is left unchanged (accumulate = 1)
+ * Rules: K % 128 == 0, any N >= 0, M_total <= 131072, 1 <= E <= 65536.
+ */
+fp8q_status fp8q_grouped_gemm_wgrad(const uint8_t* dyq_t, const float* dys_t, const uint8_t* xq_t,
+                                    const float* xs_t, const int32_t* offsets, int64_t E, int64_t M_total,
+                                    int64_t N, int64_t K, int64_t ld_t, float* dw, int accumulate,
+                                    hipStream_t stream);
+
+/*
  * Exact-accumulation variants.  Same arguments, rules, layouts and results
  * definition as the four GEMMs above; only the in-chunk arithmetic differs.
  * gfx950's FP8 matrix instruction adds the 8 products of each group of 8

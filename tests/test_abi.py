@@ -46,8 +46,8 @@ def test_every_kernel_launch_stub_is_defined(lib):
     out = subprocess.run(["nm", "-D", fq.LIB_PATH], capture_output=True, text=True).stdout
     undefined = [l for l in out.splitlines() if " U " in l and "__device_stub__" in l]
     assert not undefined, undefined[:3]
-    # 3 quantizers + 5 FP8 GEMM and 5 exact GEMM instantiations
-    assert sum(1 for l in out.splitlines() if "__device_stub__" in l) >= 13
+    # 3 quantizers (+1 grouped transpose) + 6 FP8 GEMM and 5 exact GEMM instantiations
+    assert sum(1 for l in out.splitlines() if "__device_stub__" in l) >= 15
 
 
 def test_status_strings(lib):
@@ -95,6 +95,26 @@ def test_gemm_argument_errors(lib):
     assert gg(A16, A16, A16, A16, A16, 0, 64, 128, 256, A16, 0, 128, None) == SHAPE  # E = 0
     assert gg(A16, A16, A16, A16, None, 4, 64, 128, 256, A16, 0, 128, None) == NULL
     assert gg(A16, A16, A16, A16, A16 + 2, 4, 64, 128, 256, A16, 0, 128, None) == ALIGN
+
+
+def test_grouped_backward_argument_errors(lib):
+    tg = lib.fp8q_quant_transpose_grouped
+    # rows 300, E 4: capacity 128 * (2 + 4) = 768 token columns, 6 scale columns
+    assert tg(A16, 0, 300, 64, 64, A16, 0, A16, 768, A16, 6, None) == SHAPE    # E = 0
+    assert tg(A16, 0, 300, 64, 64, A16, 4, A16, 640, A16, 6, None) == STRIDE   # ld_qt < capacity
+    assert tg(A16, 0, 300, 64, 64, A16, 4, A16, 768, A16, 5, None) == STRIDE   # ld_st < capacity/128
+    assert tg(A16, 0, 300, 64, 64, None, 4, A16, 768, A16, 6, None) == NULL
+    assert tg(A16, 0, 0, 64, 64, None, 4, None, 768, None, 6, None) == OK      # empty: no-op
+    gd = lib.fp8q_grouped_gemm_dgrad
+    assert gd(A16, A16, A16, A16, A16, 4, 64, 200, 256, A16, 0, 256, None) == SHAPE  # N % 128
+    assert gd(A16, A16, A16, A16, None, 4, 64, 256, 256, A16, 0, 256, None) == NULL
+    assert gd(A16, A16, A16, A16, A16, 0, 64, 256, 256, A16, 0, 256, None) == SHAPE  # E = 0
+    gw = lib.fp8q_grouped_gemm_wgrad
+    assert gw(A16, A16, A16, A16, A16, 4, 300, 128, 256, 640, A16, 0, None) == STRIDE  # ld_t < 768
+    assert gw(A16, A16, A16, A16, A16, 4, 300, 128, 256, 800, A16, 0, None) == ALIGN   # ld_t % 128
+    assert gw(A16, A16, A16, A16, A16, 4, 300, 128, 200, 768, A16, 0, None) == SHAPE   # K % 128
+    assert gw(A16, A16, A16, A16, A16, 4, 300, 128, 256, 768, A16, 2, None) == SHAPE   # accumulate flag
+    assert gw(A16, A16, A16, A16, A16, 4, 300, 0, 256, 768, A16, 0, None) == OK        # N = 0
 
 
 def test_binding_refuses_cpu_tensors():
