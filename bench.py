@@ -11,6 +11,11 @@ One step = one pass of the whole hot path over one batch of synthetic inputs:
     quant_act(X) -> quant_weight(W stacked) -> grouped Fprop (bf16)
 Inputs are generated and resident in HBM before the timed region.
 
+Reported beside the step (not part of its value): the MoE layer's backward,
+dY [16384,2048] bf16 -> quant_act(dY), quant_weight(W stacked, +q_t) ->
+grouped Dgrad (bf16); grouped quant_transpose(X), (dY) -> grouped Wgrad
+(dW [32,2048,7168] fp32), timed the same way over its own passes.
+
 Prints one JSON line on stdout; progress goes to stderr.
 """
 
@@ -47,14 +52,15 @@ def host_inputs():
     x, w = synth.linear_x_w()
     dy = synth.linear_dy()
     xm, wm, off = synth.moe_fprop()
+    dym = synth.moe_dy()
     log(f"inputs generated in {time.time() - t0:.1f}s")
-    return dict(x=x, w=w, dy=dy, xm=xm, wm=wm, off=off)
+    return dict(x=x, w=w, dy=dy, xm=xm, wm=wm, off=off, dym=dym)
 
 
 def build_workload(H, dev):
     g = lambda t: t.to(dev)
     return dict(x=g(H["x"]), w=g(H["w"]), dy=g(H["dy"]), xm=g(H["xm"]),
-                wm=g(H["wm"]).reshape(-1, H["wm"].shape[2]), off=g(H["off"]))
+                wm=g(H["wm"]).reshape(-1, H["wm"].shape[2]), off=g(H["off"]), dym=g(H["dym"]))
 
 
 def make_ops(L, dev):
@@ -100,6 +106,80 @@ def make_ops(L, dev):
          "mfma", 2.0 * Mm * Nm * K),
     ]
     return ops, O
+
+
+def make_moe_bwd_ops(L, dev):
+    """The MoE layer's backward kernels, as make_ops."""
+    import torch
+    import fp8_fine_grained_quant_amd as fq
+
+    u8, f32 = torch.uint8, torch.float32
+    E = 32
+    Mm, K = L["xm"].shape
+    Nm = L["wm"].shape[0] // E
+    cap = fq.token_capacity(Mm, E)
+    e = lambda *s, dt=u8: torch.empty(*s, dtype=dt, device=dev)
+    B = dict(dyq=e(Mm, Nm), dys=e(Mm, Nm // 128, dt=f32), wq=e(E * Nm, K), wq_t=e(K, E * Nm),
+             ws=e(E * Nm // 128, K // 128, dt=f32), dx=e(Mm, K, dt=torch.bfloat16),
+             xq_t=e(K, cap), xs_t=e(K, cap // 128, dt=f32), dyq_t=e(Nm, cap), dys_t=e(Nm, cap // 128, dt=f32),
+             dw=e(E, Nm, K, dt=f32))
+    act_bytes = lambda r, c, es: r * c * (es + 1) + r * cdiv(c, 128) * 4
+    ops = [
+        ("quant_act dY_moe", lambda: fq.fp8q_quant_act_1x128(L["dym"], B["dyq"], B["dys"]), "hbm",
+         act_bytes(Mm, Nm, 2)),
+        ("quant_weight W_moe (+q_t)", lambda: fq.fp8q_quant_weight_128x128(L["wm"], B["wq"], B["wq_t"], B["ws"]),
+         "hbm", E * Nm * K * 6 + cdiv(E * Nm, 128) * cdiv(K, 128) * 4),
+        ("grouped_gemm_dgrad", lambda: fq.fp8q_grouped_gemm_dgrad(B["dyq"], B["dys"], B["wq_t"], B["ws"], L["off"],
+                                                                  B["dx"]), "mfma", 2.0 * Mm * Nm * K),
+        ("quant_transpose_grouped X_moe", lambda: fq.fp8q_quant_transpose_grouped(L["xm"], L["off"], B["xq_t"],
+                                                                                 B["xs_t"]), "hbm",
+         act_bytes(Mm, K, 2)),
+        ("quant_transpose_grouped dY_moe", lambda: fq.fp8q_quant_transpose_grouped(L["dym"], L["off"], B["dyq_t"],
+                                                                                  B["dys_t"]), "hbm",
+         act_bytes(Mm, Nm, 2)),
+        ("grouped_gemm_wgrad", lambda: fq.fp8q_grouped_gemm_wgrad(B["dyq_t"], B["dys_t"], B["xq_t"], B["xs_t"],
+                                                                  L["off"], Mm, B["dw"]), "mfma",
+         2.0 * Mm * Nm * K),
+    ]
+    return ops, B
+
+
+def time_ops(ops, steps, warmup, stream):
+    """Run `warmup` untimed passes, then `steps` passes with HIP events around
+    every launch on `stream`; returns (ms per pass, per-kernel summaries)."""
+    import torch
+
+    for _ in range(warmup):
+        for _, fn, _, _ in ops:
+            fn()
+    torch.cuda.synchronize()
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in ops]
+          for _ in range(steps)]
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for s in range(steps):
+        for i, (_, fn, _, _) in enumerate(ops):
+            ev[s][i][0].record(stream)
+            fn()
+            ev[s][i][1].record(stream)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    ms_pass = t_start.elapsed_time(t_end) / steps
+    kernels = {}
+    for i, (name, _, kind, work) in enumerate(ops):
+        times = sorted(ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(steps))
+        avg_ms = sum(times) / len(times)
+        d = {"avg_us": round(avg_ms * 1e3, 2), "median_us": round(times[len(times) // 2] * 1e3, 2)}
+        if kind == "mfma":
+            a = work / (avg_ms * 1e-3) / 1e12
+            d.update(gflop=round(work / 1e9, 3), tflops=round(a, 1), frac_peak=round(a / PEAK_FP8_TFLOPS, 4))
+        else:
+            a = work / (avg_ms * 1e-3) / 1e9
+            d.update(mbytes=round(work / 1e6, 3), gbs=round(a, 1), frac_peak=round(a / PEAK_HBM_GBS, 4))
+        kernels[name] = d
+        log(f"{name:32s} {d}")
+    return ms_pass, kernels
 
 
 def cpu_baseline(H, frac):
@@ -219,44 +299,15 @@ def main():
     ops, O = make_ops(L, dev)
     names = [o[0] for o in ops]
 
-    def step():
-        for _, fn, _, _ in ops:
-            fn()
-
-    log(f"warmup {args.warmup} steps")
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-
     stream = torch.cuda.current_stream()
-    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in ops]
-          for _ in range(args.steps)]
-    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    log(f"timing {args.steps} steps")
-    torch.cuda.synchronize()
-    t_start.record(stream)
-    for s in range(args.steps):
-        for i, (_, fn, _, _) in enumerate(ops):
-            ev[s][i][0].record(stream)
-            fn()
-            ev[s][i][1].record(stream)
-    t_end.record(stream)
-    torch.cuda.synchronize()
-    ms_step = t_start.elapsed_time(t_end) / args.steps
+    log(f"warmup {args.warmup} steps, timing {args.steps} steps")
+    ms_step, kernels = time_ops(ops, args.steps, args.warmup, stream)
 
-    kernels = {}
-    for i, (name, _, kind, work) in enumerate(ops):
-        times = sorted(ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(args.steps))
-        avg_ms = sum(times) / len(times)
-        d = {"avg_us": round(avg_ms * 1e3, 2), "median_us": round(times[len(times) // 2] * 1e3, 2)}
-        if kind == "mfma":
-            a = work / (avg_ms * 1e-3) / 1e12
-            d.update(gflop=round(work / 1e9, 3), tflops=round(a, 1), frac_peak=round(a / PEAK_FP8_TFLOPS, 4))
-        else:
-            a = work / (avg_ms * 1e-3) / 1e9
-            d.update(mbytes=round(work / 1e6, 3), gbs=round(a, 1), frac_peak=round(a / PEAK_HBM_GBS, 4))
-        kernels[name] = d
-        log(f"{name:24s} {d}")
+    # the MoE backward, beside the step
+    bops, _ = make_moe_bwd_ops(L, dev)
+    log(f"MoE backward: warmup {args.warmup}, timing {args.steps} passes")
+    ms_bwd, bkernels = time_ops(bops, args.steps, args.warmup, stream)
+    bwd_flops = sum(w for _, _, k, w in bops if k == "mfma")
 
     gemm_flops = sum(w for _, _, k, w in ops if k == "mfma")
     value = gemm_flops / (ms_step * 1e-3) / 1e12
@@ -300,6 +351,15 @@ def main():
         "roofline": roof,
         "kernel_source_sha": kernel_source_hash(),
         "kernels": kernels,
+        "moe_backward": {
+            "workload": "MoE layer backward: dY [16384,2048] bf16 (Student-t(3), 1% token rows x100), X and the "
+                        "32 experts' W as the step's MoE layer; grouped Dgrad (bf16 dX) and grouped Wgrad "
+                        "(fp32 dW [32,2048,7168]) with their online quantization",
+            "ms_per_pass": round(ms_bwd, 4),
+            "gemm_gflop_per_pass": round(bwd_flops / 1e9, 2),
+            "gemm_tflops": round(bwd_flops / (ms_bwd * 1e-3) / 1e12, 2),
+            "kernels": bkernels,
+        },
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -395,7 +395,7 @@ namespace {
 template <int SB_MODE, int OUT_F32, bool GROUPED, bool KG = false>
 hipError_t launch_one(const GemmArgs& a, hipStream_t st) {
   const int64_t tiles_n = a.N / kBN, tiles_m = (a.M + kBM - 1) / kBM;
-  const int64_t tiles = KG ? a.E * tiles_m * tiles_n                     // every expert: a full grid
+  const int64_t tiles = KG ? a.E * tiles_m * 8 * ((tiles_n + 7) / 8)    // every expert: 8 XCD slices
                         : GROUPED ? (tiles_m + a.E) * tiles_n             // upper bound: a partial tile per expert
                                   : tiles_m * tiles_n;
   if (tiles <= 0) return hipSuccess;

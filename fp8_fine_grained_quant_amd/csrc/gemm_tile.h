@@ -42,19 +42,24 @@ __device__ __forceinline__ bool tile_coord(const GemmArgs& p, TileCoord& tc) {
     return true;
   }
   if (p.k_grouped) {
-    // grouped contraction: every expert owns a full M x N grid of tiles, in
-    // the plain band order
+    // grouped contraction: every expert owns a full M x N grid of tiles, and
+    // tiles of different experts differ in work (the expert's token count).
+    // Each XCD takes an equal slice of every expert: n-tiles
+    // [xcd*nx, xcd*nx + nx) with all m-tiles, walked expert by expert with
+    // the m-tiles innermost, so the XCD reads each of its X^T column blocks
+    // once and shares the expert's dY^T rows among its workgroups.  (Taking
+    // the experts in turns tile by tile instead measured 1.6x slower: the
+    // XCD's L2 then holds no expert's operands long enough.)
     const int tiles_m = (int)((p.M + BM - 1) / BM);
-    const int per_e = tiles_m * tiles_n;
-    const int e = t / per_e;
+    const int nx = (tiles_n + 7) / 8;
+    const int per_ex = tiles_m * nx;
+    const int e = (bid >> 3) / per_ex;
     if (e >= (int)p.E) return false;
-    const int tl = t - e * per_e;
-    const int band = kGroupM * tiles_n;
-    const int b = tl / band, first_m = b * kGroupM;
-    const int gm = min(tiles_m - first_m, kGroupM);
-    const int in_band = tl - b * band;
-    tc.m0 = (int64_t)(first_m + in_band % gm) * BM;
-    tc.n0 = (in_band / gm) * BN;
+    const int tl = (bid >> 3) - e * per_ex;
+    const int n = xcd * nx + tl / tiles_m;
+    if (n >= tiles_n) return false;
+    tc.m0 = (int64_t)(tl % tiles_m) * BM;
+    tc.n0 = n * BN;
     tc.mend = p.M;
     tc.e = e;
     return true;
