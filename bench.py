@@ -144,6 +144,23 @@ def make_moe_bwd_ops(L, dev):
     return ops, B
 
 
+def make_dual_ops(L, dev):
+    """The dual-output quantizer on the linear layer's X and dY (each feeds a
+    row-quantized GEMM and the weight-gradient GEMM), as make_ops."""
+    import torch
+    import fp8_fine_grained_quant_amd as fq
+
+    ops = []
+    for name, x in (("X", L["x"]), ("dY", L["dy"])):
+        m, c = x.shape
+        e = lambda *s, dt=torch.uint8: torch.empty(*s, dtype=dt, device=dev)
+        bufs = (e(m, c), e(m, cdiv(c, 128), dt=torch.float32), e(c, m), e(c, cdiv(m, 128), dt=torch.float32))
+        work = m * c * 4 + (m * cdiv(c, 128) + c * cdiv(m, 128)) * 4
+        ops.append((f"quant_act_transpose {name}",
+                    (lambda x=x, b=bufs: fq.fp8q_quant_act_transpose(x, *b)), "hbm", work))
+    return ops
+
+
 def time_ops(ops, steps, warmup, stream):
     """Run `warmup` untimed passes, then `steps` passes with HIP events around
     every launch on `stream`; returns (ms per pass, per-kernel summaries)."""
@@ -309,6 +326,11 @@ def main():
     ms_bwd, bkernels = time_ops(bops, args.steps, args.warmup, stream)
     bwd_flops = sum(w for _, _, k, w in bops if k == "mfma")
 
+    # the dual-output quantizer, beside the step (the step keeps the separate ones)
+    dops = make_dual_ops(L, dev)
+    log(f"dual-output quantizer: warmup {args.warmup}, timing {args.steps} passes")
+    _, dkernels = time_ops(dops, args.steps, args.warmup, stream)
+
     gemm_flops = sum(w for _, _, k, w in ops if k == "mfma")
     value = gemm_flops / (ms_step * 1e-3) / 1e12
     dom = max(range(len(ops)), key=lambda i: kernels[names[i]]["avg_us"])
@@ -359,6 +381,13 @@ def main():
             "gemm_gflop_per_pass": round(bwd_flops / 1e9, 2),
             "gemm_tflops": round(bwd_flops / (ms_bwd * 1e-3) / 1e12, 2),
             "kernels": bkernels,
+        },
+        "dual_output_quantizer": {
+            "workload": "quant_act_1x128 + quant_transpose of the linear layer's X [4096,7168] and dY [4096,2048] "
+                        "(bf16) in one pass each",
+            "kernels": dkernels,
+            "separate_us": {n: round(kernels[f"quant_act {n}"]["avg_us"] + kernels[f"quant_transpose {n}"]["avg_us"],
+                                     2) for n in ("X", "dY")},
         },
         "cpu_baseline": cpu,
     }

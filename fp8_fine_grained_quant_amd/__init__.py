@@ -39,7 +39,7 @@ EXPORTS = ["fp8q_status_string", "fp8q_quant_act_1x128", "fp8q_quant_weight_128x
            "fp8q_quant_transpose", "fp8q_gemm_fprop", "fp8q_gemm_dgrad", "fp8q_gemm_wgrad",
            "fp8q_grouped_gemm", "fp8q_gemm_fprop_exact", "fp8q_gemm_dgrad_exact", "fp8q_gemm_wgrad_exact",
            "fp8q_grouped_gemm_exact", "fp8q_quant_transpose_grouped", "fp8q_grouped_gemm_dgrad",
-           "fp8q_grouped_gemm_wgrad"]
+           "fp8q_grouped_gemm_wgrad", "fp8q_quant_act_transpose"]
 
 
 class Fp8qError(RuntimeError):
@@ -70,6 +70,7 @@ def load_library(path=LIB_PATH):
         "fp8q_gemm_wgrad": ([P, P, P, P, I64, I64, I64, P, I64, I32, P], I32),
         "fp8q_grouped_gemm": ([P, P, P, P, P, I64, I64, I64, I64, P, I32, I64, P], I32),
         "fp8q_quant_transpose_grouped": ([P, I32, I64, I64, I64, P, I64, P, I64, P, I64, P], I32),
+        "fp8q_quant_act_transpose": ([P, I32, I64, I64, I64, P, I64, P, I64, P, I64, P, I64, P], I32),
         "fp8q_grouped_gemm_dgrad": ([P, P, P, P, P, I64, I64, I64, I64, P, I32, I64, P], I32),
         "fp8q_grouped_gemm_wgrad": ([P, P, P, P, P, I64, I64, I64, I64, I64, P, I32, P], I32),
     }
@@ -204,6 +205,15 @@ def fp8q_grouped_gemm(xq, xs, wq, ws, offsets, y, stream=None, exact=False):
            "fp8q_grouped_gemm")
 
 
+def fp8q_quant_act_transpose(x, q, scale, q_t, scale_t, stream=None):
+    _on_gpu(x, q, scale, q_t, scale_t)
+    rows, cols = x.shape
+    _check(load_library().fp8q_quant_act_transpose(_ptr(x), _dtype_code(x), rows, cols, _ld(x), _ptr(q), _ld(q),
+                                                    _ptr(scale), _ld(scale), _ptr(q_t), _ld(q_t), _ptr(scale_t),
+                                                    _ld(scale_t), _stream(stream)),
+           "fp8q_quant_act_transpose")
+
+
 def fp8q_quant_transpose_grouped(x, offsets, q_t, scale_t, stream=None):
     _on_gpu(x, offsets, q_t, scale_t)
     _contig(offsets)
@@ -334,3 +344,14 @@ def grouped_gemm_wgrad(dyq_t, dys_t, xq_t, xs_t, offsets, m_total, dw=None, stre
                          device=dyq_t.device)
     fp8q_grouped_gemm_wgrad(dyq_t, dys_t, xq_t, xs_t, offsets, m_total, dw, accumulate, stream)
     return dw
+
+
+def quant_act_transpose(x, stream=None):
+    """Both quantizations of x from one read: (q, s, q_t, s_t)."""
+    rows, cols = x.shape
+    q = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
+    s = torch.empty((rows, _cdiv(cols, 128)), dtype=torch.float32, device=x.device)
+    q_t = torch.empty((cols, rows), dtype=torch.uint8, device=x.device)
+    s_t = torch.empty((cols, _cdiv(rows, 128)), dtype=torch.float32, device=x.device)
+    fp8q_quant_act_transpose(x, q, s, q_t, s_t, stream)
+    return q, s, q_t, s_t

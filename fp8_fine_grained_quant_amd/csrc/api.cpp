@@ -99,6 +99,19 @@ fp8q_status fp8q_quant_transpose(const void* x, fp8q_dtype xt, int64_t rows, int
       fp8q::launch_quant_transpose(x, xt == FP8Q_BF16, rows, cols, ld_x, q_t, ld_qt, scale_t, ld_st, stream));
 }
 
+fp8q_status fp8q_quant_act_transpose(const void* x, fp8q_dtype xt, int64_t rows, int64_t cols, int64_t ld_x,
+                                     uint8_t* q, int64_t ld_q, float* scale, int64_t ld_s, uint8_t* q_t,
+                                     int64_t ld_qt, float* scale_t, int64_t ld_st, hipStream_t stream) {
+  if (!valid_dtype(xt)) return FP8Q_ERR_DTYPE;
+  fp8q_status c = check_quant(x, esize(xt), rows, cols, ld_x, q, ld_q, cols, scale, ld_s, cdiv(cols, 128));
+  if (c != FP8Q_OK || rows == 0 || cols == 0) return c;
+  c = check_quant(x, esize(xt), rows, cols, ld_x, q_t, ld_qt, rows, scale_t, ld_st, cdiv(rows, 128));
+  if (c != FP8Q_OK) return c;
+  if (cdiv(rows, 128) > 65535) return FP8Q_ERR_SHAPE;
+  return launched(fp8q::launch_quant_act_transpose(x, xt == FP8Q_BF16, rows, cols, ld_x, q, ld_q, scale, ld_s,
+                                                   q_t, ld_qt, scale_t, ld_st, stream));
+}
+
 fp8q_status fp8q_quant_transpose_grouped(const void* x, fp8q_dtype xt, int64_t rows, int64_t cols, int64_t ld_x,
                                          const int32_t* offsets, int64_t E, uint8_t* q_t, int64_t ld_qt,
                                          float* scale_t, int64_t ld_st, hipStream_t stream) {

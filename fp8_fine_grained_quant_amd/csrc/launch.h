@@ -17,6 +17,11 @@ hipError_t launch_quant_weight(const void* w, bool w_bf16, int64_t rows, int64_t
 hipError_t launch_quant_transpose(const void* x, bool x_bf16, int64_t rows, int64_t cols, int64_t ld_x,
                                   uint8_t* q_t, int64_t ld_qt, float* s_t, int64_t ld_st, hipStream_t st);
 
+// quant_act_1x128 and quant_transpose of the same x from one read of it.
+hipError_t launch_quant_act_transpose(const void* x, bool x_bf16, int64_t rows, int64_t cols, int64_t ld_x,
+                                      uint8_t* q, int64_t ld_q, float* s, int64_t ld_s, uint8_t* q_t,
+                                      int64_t ld_qt, float* s_t, int64_t ld_st, hipStream_t st);
+
 // Per expert e (rows [offsets[e], offsets[e+1]) of x), the quantize-transpose
 // of that block alone, written at padded token column 128*(offsets[e]/128 + e);
 // the tail of an expert's last 128-token chunk is written as code 0.

@@ -220,12 +220,18 @@ hipError_t launch_quant_weight(const void* w, bool w_bf16, int64_t rows, int64_t
 // reduced over the 16 threads of a channel (xor 16/32 inside the wave, LDS
 // across the 4 waves), and each channel's 8 codes are converted pairwise
 // down the column, so they leave as one 8-byte segment of the q_t row.
-template <class In, bool G>
+//
+// D (dual output): the same tile also yields the 1x128 row quantization -- a
+// tile's 128 channels of one token are exactly one 1x128 group -- so X is
+// read once for both the row codes q [rows, cols] and the transposed ones.
+template <class In, bool G, bool D>
 __global__ __launch_bounds__(256) void k_quant_transpose(const typename In::elem* __restrict__ x, int64_t ld_x,
                                                          int rows, int cols,
                                                          uint8_t* __restrict__ qt, int64_t ld_qt,
                                                          float* __restrict__ st, int64_t ld_st,
-                                                         const int32_t* __restrict__ offsets, int E) {
+                                                         const int32_t* __restrict__ offsets, int E,
+                                                         uint8_t* __restrict__ q, int64_t ld_q,
+                                                         float* __restrict__ s, int64_t ld_s) {
   __shared__ uint32_t red[4][128];
   const int t = threadIdx.x;
   const int c8 = t & 15, rblk = t >> 4;
@@ -265,6 +271,31 @@ __global__ __launch_bounds__(256) void k_quant_transpose(const typename In::elem
         for (int e = 0; e < 8; ++e)
           if (c0 + e < cols) v[i][e] = In::load1(p + e);
       }
+    }
+  }
+  if (D) {
+    // row groups: the 16 threads of a token row form one DPP row of a wave
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      uint32_t a = 0;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) a = max(a, abs_bits(v[i][e]));
+      a = row16_max_u32(a);
+      const int r = r0 + i;
+      if (r >= rows) continue;
+      float sc, iv;
+      group_scale(__uint_as_float(a), sc, iv);
+      const uint32_t w0 = pack4_e4m3(v[i][0] * iv, v[i][1] * iv, v[i][2] * iv, v[i][3] * iv);
+      const uint32_t w1 = pack4_e4m3(v[i][4] * iv, v[i][5] * iv, v[i][6] * iv, v[i][7] * iv);
+      uint8_t* qp = q + (int64_t)r * ld_q + c0;
+      if (c0 + 8 <= cols) {
+        *reinterpret_cast<uint2*>(qp) = make_uint2(w0, w1);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (c0 + e < cols) qp[e] = (uint8_t)(((e < 4 ? w0 : w1) >> (8 * (e & 3))) & 0xFF);
+      }
+      if (c8 == 0) s[(int64_t)r * ld_s + bj] = sc;
     }
   }
   uint32_t m[8];
@@ -316,11 +347,24 @@ hipError_t launch_quant_transpose(const void* x, bool x_bf16, int64_t rows, int6
                                   uint8_t* q_t, int64_t ld_qt, float* s_t, int64_t ld_st, hipStream_t st) {
   const dim3 grid((uint32_t)((cols + 127) / 128), (uint32_t)((rows + 127) / 128));
   if (x_bf16)
-    hipLaunchKernelGGL((k_quant_transpose<BF16In, false>), grid, dim3(256), 0, st, (const uint16_t*)x, ld_x,
-                       (int)rows, (int)cols, q_t, ld_qt, s_t, ld_st, nullptr, 0);
+    hipLaunchKernelGGL((k_quant_transpose<BF16In, false, false>), grid, dim3(256), 0, st, (const uint16_t*)x, ld_x,
+                       (int)rows, (int)cols, q_t, ld_qt, s_t, ld_st, nullptr, 0, nullptr, 0, nullptr, 0);
   else
-    hipLaunchKernelGGL((k_quant_transpose<F32In, false>), grid, dim3(256), 0, st, (const float*)x, ld_x,
-                       (int)rows, (int)cols, q_t, ld_qt, s_t, ld_st, nullptr, 0);
+    hipLaunchKernelGGL((k_quant_transpose<F32In, false, false>), grid, dim3(256), 0, st, (const float*)x, ld_x,
+                       (int)rows, (int)cols, q_t, ld_qt, s_t, ld_st, nullptr, 0, nullptr, 0, nullptr, 0);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_act_transpose(const void* x, bool x_bf16, int64_t rows, int64_t cols, int64_t ld_x,
+                                      uint8_t* q, int64_t ld_q, float* s, int64_t ld_s, uint8_t* q_t,
+                                      int64_t ld_qt, float* s_t, int64_t ld_st, hipStream_t st) {
+  const dim3 grid((uint32_t)((cols + 127) / 128), (uint32_t)((rows + 127) / 128));
+  if (x_bf16)
+    hipLaunchKernelGGL((k_quant_transpose<BF16In, false, true>), grid, dim3(256), 0, st, (const uint16_t*)x, ld_x,
+                       (int)rows, (int)cols, q_t, ld_qt, s_t, ld_st, nullptr, 0, q, ld_q, s, ld_s);
+  else
+    hipLaunchKernelGGL((k_quant_transpose<F32In, false, true>), grid, dim3(256), 0, st, (const float*)x, ld_x,
+                       (int)rows, (int)cols, q_t, ld_qt, s_t, ld_st, nullptr, 0, q, ld_q, s, ld_s);
   return hipGetLastError();
 }
 
@@ -330,11 +374,11 @@ hipError_t launch_quant_transpose_grouped(const void* x, bool x_bf16, int64_t ro
   // one block per padded 128-token chunk of the capacity 128*(rows/128 + E)
   const dim3 grid((uint32_t)((cols + 127) / 128), (uint32_t)(rows / 128 + E));
   if (x_bf16)
-    hipLaunchKernelGGL((k_quant_transpose<BF16In, true>), grid, dim3(256), 0, st, (const uint16_t*)x, ld_x,
-                       (int)rows, (int)cols, q_t, ld_qt, s_t, ld_st, offsets, (int)E);
+    hipLaunchKernelGGL((k_quant_transpose<BF16In, true, false>), grid, dim3(256), 0, st, (const uint16_t*)x, ld_x,
+                       (int)rows, (int)cols, q_t, ld_qt, s_t, ld_st, offsets, (int)E, nullptr, 0, nullptr, 0);
   else
-    hipLaunchKernelGGL((k_quant_transpose<F32In, true>), grid, dim3(256), 0, st, (const float*)x, ld_x,
-                       (int)rows, (int)cols, q_t, ld_qt, s_t, ld_st, offsets, (int)E);
+    hipLaunchKernelGGL((k_quant_transpose<F32In, true, false>), grid, dim3(256), 0, st, (const float*)x, ld_x,
+                       (int)rows, (int)cols, q_t, ld_qt, s_t, ld_st, offsets, (int)E, nullptr, 0, nullptr, 0);
   return hipGetLastError();
 }
 

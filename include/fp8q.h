@@ -120,6 +120,19 @@ fp8q_status fp8q_quant_transpose(const void* x, fp8q_dtype xt, int64_t rows, int
                                  uint8_t* q_t, int64_t ld_qt, float* scale_t, int64_t ld_st, hipStream_t stream);
 
 /*
+ * Dual-output quantizer: fp8q_quant_act_1x128 and fp8q_quant_transpose of the
+ * same x in one pass that reads x once (a layer's input X, or its output
+ * gradient dY, feeds both a row-quantized GEMM and the weight-gradient GEMM;
+ * "DeepSeek FP8 Training", Fprop and weight-gradient lists).  The outputs are
+ * byte for byte those of the two separate calls; the arguments and rules are
+ * theirs combined (q, scale as fp8q_quant_act_1x128; q_t, scale_t as
+ * fp8q_quant_transpose).
+ */
+fp8q_status fp8q_quant_act_transpose(const void* x, fp8q_dtype xt, int64_t rows, int64_t cols, int64_t ld_x,
+                                     uint8_t* q, int64_t ld_q, float* scale, int64_t ld_s, uint8_t* q_t,
+                                     int64_t ld_qt, float* scale_t, int64_t ld_st, hipStream_t stream);
+
+/*
  * Fprop: Y[M,N] = X[M,K] . W[N,K]^T ("DeepSeek FP8 Training", Fprop pipeline:
  * FP8 GEMM with FP32 accumulation, result stored as BF16).
  *   xq : [M, K] codes, contiguous;  xs : [M, K/128] FP32, contiguous

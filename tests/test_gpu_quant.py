@@ -228,3 +228,48 @@ def test_transpose_equals_act_of_transposed_on_gpu():
     q_t, s_t = fq.quant_transpose(dy)
     q2, s2 = fq.quant_act_1x128(dy.t().contiguous())
     assert torch.equal(q_t, q2) and torch.equal(s_t, s2)
+
+
+# ------------------------------------------------------- dual-output quantizer
+@pytest.mark.parametrize("shape", [(1, 1), (128, 128), (300, 70), (1, 5), (257, 129), (129, 1), (1000, 24),
+                                   (130, 300)])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_act_transpose_edge_shapes_with_guards(shape, dtype):
+    rows, cols = shape
+    a = synth.general(rows, cols, seed=rows + 17 * cols, kind="t3", outlier_frac=0.02, outlier_mul=100.0)
+    x_cpu = torch.from_numpy(a.astype(np.float32)).to(dtype)
+    _, x = _padded(gpu(x_cpu))
+    r16 = lambda n: ((n + 15) // 16) * 16 + 16
+    g_r, g_c = (cols + 127) // 128, (rows + 127) // 128
+    qbuf = torch.full((rows + 1, r16(cols)), 0x3C, dtype=torch.uint8, device=DEV)
+    sbuf = torch.full((rows + 1, g_r + 1), -5.0, dtype=torch.float32, device=DEV)
+    qtbuf = torch.full((cols + 1, r16(rows)), 0x3C, dtype=torch.uint8, device=DEV)
+    stbuf = torch.full((cols + 1, g_c + 1), -5.0, dtype=torch.float32, device=DEV)
+    q, s, q_t, s_t = qbuf[:rows, :cols], sbuf[:rows, :g_r], qtbuf[:cols, :rows], stbuf[:cols, :g_c]
+    fq.fp8q_quant_act_transpose(x, q, s, q_t, s_t)
+    torch.cuda.synchronize()
+    qo, so = oracle.quant_act_1x128(f32(x_cpu))
+    qto, sto = oracle.quant_transpose(f32(x_cpu))
+    assert_bytes_equal(np_u8(q), qo, f"{shape} row codes")
+    assert_scales_equal(s.cpu().numpy(), so, f"{shape} row scales")
+    assert_bytes_equal(np_u8(q_t), qto, f"{shape} transposed codes")
+    assert_scales_equal(s_t.cpu().numpy(), sto, f"{shape} transposed scales")
+    for buf, r, c, fill in ((qbuf, rows, cols, 0x3C), (qtbuf, cols, rows, 0x3C), (sbuf, rows, g_r, -5.0),
+                            (stbuf, cols, g_c, -5.0)):
+        assert torch.all(buf[:r, c:] == fill) and torch.all(buf[r] == fill)
+
+
+@pytest.mark.parametrize("which", ["C2 X", "C3 dY"])
+def test_act_transpose_equals_the_two_quantizers_full_size(which):
+    x = gpu(synth.linear_x_w()[0] if which == "C2 X" else synth.linear_dy())
+    log(f"{which} dual-output quantizer against quant_act_1x128 + quant_transpose")
+    q, s, q_t, s_t = fq.quant_act_transpose(x)
+    q1, s1 = fq.quant_act_1x128(x)
+    q2, s2 = fq.quant_transpose(x)
+    torch.cuda.synchronize()
+    assert torch.equal(q, q1) and torch.equal(s, s1)
+    assert torch.equal(q_t, q2) and torch.equal(s_t, s2)
+    rows = sample_rows(x.shape[0], 32, 5, must=(0, x.shape[0] - 1))
+    qo, so = oracle.quant_act_1x128(f32(x[torch.from_numpy(rows).to(DEV)]))
+    assert_bytes_equal(np_u8(q)[rows], qo, which + " row codes (sampled rows)")
+    assert_scales_equal(s.cpu().numpy()[rows], so, which + " row scales (sampled rows)")
