@@ -63,15 +63,23 @@ constexpr int kMaxChunks = 1024;
 constexpr int kSkew = 3;                          // promotion trails its MFMA by 3 slots
 static_assert(kTM == 4 && kSkew == kTM - 1, "the slot schedule below assumes 4 row sub-tiles");
 
-template <int SB_MODE>
+// SC4: the row scales travel in blocks of 4 chunks (16 bytes per row, one
+// load per 4 chunks into a 2-block ring) instead of 4 bytes per row per
+// chunk in every stage.  A row's scales of consecutive chunks sit in one
+// cache line, so this cuts the scale loads' line requests fourfold; it needs
+// 16-byte aligned scale rows.
+template <int SB_MODE, bool SC4>
 struct Stage {
   static constexpr int a = 0;                     // [256 rows][128 B], swizzled
   static constexpr int b = kBM * kBK;             // [128 rows][128 B], swizzled
-  static constexpr int sa = b + kBN * kBK;        // 256 row scales
-  static constexpr int sb = sa + 4 * kNT;         // row mode: 128 column scales (+128 spare)
+  static constexpr int sa = b + kBN * kBK;        // 256 row scales (not SC4)
+  static constexpr int sb = sa + (SC4 ? 0 : 4 * kNT);  // row mode: 128 column scales (+128 spare)
   static constexpr int bytes = sb + (SB_MODE == kSbRow ? 4 * kNT : 0);
   static constexpr int sbk_len = SB_MODE == kSbBlock ? kMaxChunks : 4;
-  static_assert(3 * bytes + 4 * sbk_len <= 160 * 1024, "LDS of one CU");
+  static constexpr int ring = SC4 ? 2 * 256 * 4 : 4;      // floats of the SC4 row-scale ring
+  static constexpr int dummy = SC4 ? 1024 : 16;           // bytes: target of count-keeping loads
+  static_assert(!SC4 || SB_MODE == kSbBlock, "block scales of B only");
+  static_assert(3 * bytes + 4 * sbk_len + 4 * ring + dummy <= 160 * 1024, "LDS of one CU");
   static_assert(4 * 12288 <= bytes, "epilogue staging fits in one stage");
 };
 
@@ -109,15 +117,17 @@ __device__ __forceinline__ void row_scales(float v, float k, float (&out)[4]) {
 
 }  // namespace
 
-template <int SB_MODE, int OUT_F32, bool GROUPED, bool KG>
+template <int SB_MODE, int OUT_F32, bool GROUPED, bool KG, bool SC4>
 __global__ __launch_bounds__(kNT) void k_gemm_fp8(GemmArgs p) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
-  typedef Stage<SB_MODE> S;
+  typedef Stage<SB_MODE, SC4> S;
   constexpr bool ROW = SB_MODE == kSbRow;
   __shared__ __attribute__((aligned(16))) uint8_t st0[S::bytes];
   __shared__ __attribute__((aligned(16))) uint8_t st1[S::bytes];
   __shared__ __attribute__((aligned(16))) uint8_t st2[S::bytes];
   __shared__ __attribute__((aligned(16))) float sbk_all[S::sbk_len];  // block mode: B scale per chunk
+  __shared__ __attribute__((aligned(16))) float scA[S::ring];          // SC4: row scales, 2 blocks of 4 chunks
+  __shared__ __attribute__((aligned(16))) uint8_t dmy[S::dummy];
 
   TileCoord tc;
   if (!tile_coord<kBM, kBN, GROUPED>(p, tc)) return;
@@ -172,8 +182,17 @@ __global__ __launch_bounds__(kNT) void k_gemm_fp8(GemmArgs p) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, (lds_ptr)(st + S::b + (w * kIB + q) * 1024), 16,
                                                voffB + q * stepB, ka, 0, 0);
     } else if (d == kIA + kIB) {
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rSa, (lds_ptr)(st + S::sa + w * 256), 4, voffSa, (uint32_t)kb * 4, 0,
-                                               0);
+      if (SC4) {
+        // every 4th chunk the row scales of chunks kb..kb+3, else an
+        // out-of-range load (no memory access) that keeps the count per chunk
+        const bool real = (kb & 3) == 0;
+        uint8_t* dst = real ? reinterpret_cast<uint8_t*>(scA) + ((kb >> 2) & 1) * 4096 + w * 1024 : dmy;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rSa, (lds_ptr)dst, 16, voffSa,
+                                                 real ? (uint32_t)kb * 4 : 0x40000000u, 0, 0);
+      } else {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rSa, (lds_ptr)(st + S::sa + w * 256), 4, voffSa, (uint32_t)kb * 4,
+                                                 0, 0);
+      }
     } else {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rSb, (lds_ptr)(st + S::sb + w * 256), 4, voffSb, (uint32_t)kb * 4, 0,
                                                0);
@@ -209,9 +228,10 @@ __global__ __launch_bounds__(kNT) void k_gemm_fp8(GemmArgs p) {
   // group's 16 values; row_scales hands every lane of the group entry (i, r)
   // (DPP row_newbcast): one 4-byte LDS read per chunk instead of four
   // 16-byte ones.
-  const int offSa = 4 * (w * 64 + 16 * (l16 >> 2) + 4 * g + (l16 & 3));
-  auto rdSa = [&](const uint8_t* st) -> float {
-    return *reinterpret_cast<const float*>(st + S::sa + offSa);
+  const int rowSa = w * 64 + 16 * (l16 >> 2) + 4 * g + (l16 & 3);
+  auto rdSa = [&](const uint8_t* st, int kb) -> float {
+    if (SC4) return scA[((kb >> 2) & 1) * 1024 + rowSa * 4 + (kb & 3)];
+    return *reinterpret_cast<const float*>(st + S::sa + 4 * rowSa);
   };
 
   auto rdSb = [&](const uint8_t* st, int j) -> float {
@@ -278,7 +298,7 @@ __global__ __launch_bounds__(kNT) void k_gemm_fp8(GemmArgs p) {
 #pragma unroll
   for (int i = 0; i < kTM; ++i) {
     a[i] = rdA(st0, i);
-    if (i == 0) sa_nx = rdSa(st0);
+    if (i == 0) sa_nx = rdSa(st0, 0);
     pp[i] = v4f{0.f, 0.f, 0.f, 0.f};
   }
   bring[0] = rdB(st0, 0);
@@ -341,7 +361,7 @@ __global__ __launch_bounds__(kNT) void k_gemm_fp8(GemmArgs p) {
           // a[i] is no longer needed for this chunk: fetch the next chunk's
           a[i] = rdA(nxt, i);
           if (i == 0) {
-            sa_nx = rdSa(nxt);
+            sa_nx = rdSa(nxt, min(c + 1, nk - 1));
             if (!ROW) sbk_nx = sbk_all[min(c + 1, nk - 1)];
           }
         }
@@ -392,14 +412,14 @@ __global__ __launch_bounds__(kNT) void k_gemm_fp8(GemmArgs p) {
 
 namespace {
 
-template <int SB_MODE, int OUT_F32, bool GROUPED, bool KG = false>
+template <int SB_MODE, int OUT_F32, bool GROUPED, bool KG = false, bool SC4 = false>
 hipError_t launch_one(const GemmArgs& a, hipStream_t st) {
   const int64_t tiles_n = a.N / kBN, tiles_m = (a.M + kBM - 1) / kBM;
   const int64_t tiles = KG ? a.E * tiles_m * 8 * ((tiles_n + 7) / 8)    // every expert: 8 XCD slices
                         : GROUPED ? (tiles_m + a.E) * tiles_n             // upper bound: a partial tile per expert
                                   : tiles_m * tiles_n;
   if (tiles <= 0) return hipSuccess;
-  hipLaunchKernelGGL((k_gemm_fp8<SB_MODE, OUT_F32, GROUPED, KG>), dim3((uint32_t)tiles), dim3(kNT), 0, st, a);
+  hipLaunchKernelGGL((k_gemm_fp8<SB_MODE, OUT_F32, GROUPED, KG, SC4>), dim3((uint32_t)tiles), dim3(kNT), 0, st, a);
   return hipGetLastError();
 }
 
@@ -410,8 +430,15 @@ hipError_t launch_gemm_fp8(const GemmArgs& a, hipStream_t st) {
     if (a.k_grouped) return launch_one<kSbRow, 1, true, true>(a, st);
     return launch_one<kSbRow, 1, false>(a, st);
   }
-  if (a.offsets != nullptr)
+  // row scales in 16-byte blocks of 4 chunks when every scale row is 16-byte aligned
+  const bool sc4 = a.ld_sa % 4 == 0 && (reinterpret_cast<uintptr_t>(a.sa) & 15) == 0;
+  if (a.offsets != nullptr) {
+    if (sc4) return a.out_f32 ? launch_one<kSbBlock, 1, true, false, true>(a, st)
+                              : launch_one<kSbBlock, 0, true, false, true>(a, st);
     return a.out_f32 ? launch_one<kSbBlock, 1, true>(a, st) : launch_one<kSbBlock, 0, true>(a, st);
+  }
+  if (sc4) return a.out_f32 ? launch_one<kSbBlock, 1, false, false, true>(a, st)
+                            : launch_one<kSbBlock, 0, false, false, true>(a, st);
   return a.out_f32 ? launch_one<kSbBlock, 1, false>(a, st) : launch_one<kSbBlock, 0, false>(a, st);
 }
 
