@@ -78,7 +78,6 @@ struct Stage {
   static constexpr int sbk_len = SB_MODE == kSbBlock ? kMaxChunks : 4;
   static constexpr int ring = SC4 ? 2 * 256 * 4 : 4;      // floats of the SC4 row-scale ring
   static constexpr int dummy = SC4 ? 1024 : 16;           // bytes: target of count-keeping loads
-  static_assert(!SC4 || SB_MODE == kSbBlock, "block scales of B only");
   static_assert(3 * bytes + 4 * sbk_len + 4 * ring + dummy <= 160 * 1024, "LDS of one CU");
   static_assert(4 * 12288 <= bytes, "epilogue staging fits in one stage");
 };
@@ -183,12 +182,13 @@ __global__ __launch_bounds__(kNT) void k_gemm_fp8(GemmArgs p) {
                                                voffB + q * stepB, ka, 0, 0);
     } else if (d == kIA + kIB) {
       if (SC4) {
-        // every 4th chunk the row scales of chunks kb..kb+3, else an
-        // out-of-range load (no memory access) that keeps the count per chunk
-        const bool real = (kb & 3) == 0;
+        // the row scales of the aligned block of 4 chunks that starts at
+        // chunk kb (or holds the tile's first chunk), else an out-of-range
+        // load (no memory access) that keeps the count per chunk
+        const bool real = (kb & 3) == 0 || kb == cb;
         uint8_t* dst = real ? reinterpret_cast<uint8_t*>(scA) + ((kb >> 2) & 1) * 4096 + w * 1024 : dmy;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rSa, (lds_ptr)dst, 16, voffSa,
-                                                 real ? (uint32_t)kb * 4 : 0x40000000u, 0, 0);
+                                                 real ? (uint32_t)(kb & ~3) * 4 : 0x40000000u, 0, 0);
       } else {
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rSa, (lds_ptr)(st + S::sa + w * 256), 4, voffSa, (uint32_t)kb * 4,
                                                  0, 0);
@@ -229,7 +229,8 @@ __global__ __launch_bounds__(kNT) void k_gemm_fp8(GemmArgs p) {
   // (DPP row_newbcast): one 4-byte LDS read per chunk instead of four
   // 16-byte ones.
   const int rowSa = w * 64 + 16 * (l16 >> 2) + 4 * g + (l16 & 3);
-  auto rdSa = [&](const uint8_t* st, int kb) -> float {
+  auto rdSa = [&](const uint8_t* st, int kb) -> float {  // kb: the tile's chunk index
+    kb += cb;
     if (SC4) return scA[((kb >> 2) & 1) * 1024 + rowSa * 4 + (kb & 3)];
     return *reinterpret_cast<const float*>(st + S::sa + 4 * rowSa);
   };
@@ -426,12 +427,12 @@ hipError_t launch_one(const GemmArgs& a, hipStream_t st) {
 }  // namespace
 
 hipError_t launch_gemm_fp8(const GemmArgs& a, hipStream_t st) {
-  if (a.sb_mode == kSbRow) {  // weight gradients: FP32 out
+  const bool sc4 = a.ld_sa % 4 == 0 && (reinterpret_cast<uintptr_t>(a.sa) & 15) == 0;
+  if (a.sb_mode == kSbRow) {  // weight gradients: FP32 out (row scales 128 B per row: no gain from blocks)
     if (a.k_grouped) return launch_one<kSbRow, 1, true, true>(a, st);
     return launch_one<kSbRow, 1, false>(a, st);
   }
   // row scales in 16-byte blocks of 4 chunks when every scale row is 16-byte aligned
-  const bool sc4 = a.ld_sa % 4 == 0 && (reinterpret_cast<uintptr_t>(a.sa) & 15) == 0;
   if (a.offsets != nullptr) {
     if (sc4) return a.out_f32 ? launch_one<kSbBlock, 1, true, false, true>(a, st)
                               : launch_one<kSbBlock, 0, true, false, true>(a, st);
