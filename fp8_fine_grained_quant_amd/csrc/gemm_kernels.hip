@@ -1,51 +1,38 @@
-// Block-scaled FP8 GEMM with FP32 promotion every 128-long K chunk (gfx950).
+// Exact-accumulation variant of the block-scaled FP8 GEMM (gfx950): the
+// `_exact` entry points.
 //
-// What is computed ("DeepSeek FP8 Training", Fprop pipeline and the weight-
-// and input-gradient lists; innerforce.co.kr excerpt of the DeepSeek-V3 report,
-// paragraph after Figure 7 (a): dequantization folded into increased-precision
-// accumulation; "unified E4M3 format" page, "Enhanced Numerical Stability":
-// partial results promoted to FP32 registers at intervals):
+// What is computed is the same as the FP8 kernel's ("DeepSeek FP8 Training",
+// Fprop pipeline and the weight- and input-gradient lists; innerforce.co.kr
+// excerpt of the DeepSeek-V3 report, paragraph after Figure 7 (a):
+// dequantization folded into increased-precision accumulation; "unified E4M3
+// format" page, "Enhanced Numerical Stability": partial results promoted to
+// FP32 registers at intervals):
 //
 //     C[m, n] = sum_kb  P_kb[m, n] * sA(m, kb) * sB(n, kb)
 //
-// where P_kb is the FP8 x FP8 product over the 128 K of chunk kb, computed by
-// one v_mfma_f32_16x16x128_f8f6f4 per 16x16 sub-tile (so one MFMA is exactly
-// one promotion interval), and the scale-and-add runs as FP32 FMAs on the
-// vector ALU into accumulators kept in architectural VGPRs.
+// gfx950's FP8 matrix instruction aligns the 8 products of each group of 8
+// consecutive K to the largest one and truncates the others 13 bits below
+// its exponent (measured), the analogue of the limited accumulation the pages
+// report for H800 tensor cores.  This kernel converts the codes exactly to
+// BF16 (every E4M3 value is a BF16 value) and forms P_kb with four
+// v_mfma_f32_16x16x32_bf16 per 16x16 sub-tile, whose products are exact and
+// whose sums are FP32; the promotion is the FP8 kernel's (one FMA per element
+// and chunk into FP32 accumulators).
 //
-// Tiling (MI355X-first: 256 CUs, 64-wide waves, 160 KB LDS per CU), set by a
-// compile-time configuration (waves in M x N, MFMA sub-tiles per wave):
-//   * default workgroup tile 256 x 128 with 4 waves, one per SIMD, each wave a
-//     64 x 128 strip (4 x 8 MFMA sub-tiles, 128 FP32 accumulators per lane in
-//     architectural VGPRs, which leaves room for double-buffered operands and
-//     MFMA results so a wave's promotion FMAs issue under its next MFMAs);
-//   * B (the operand every wave shares) is staged through a double-buffered
-//     LDS tile with a 144-byte row pitch (conflict-free 16-byte reads across
-//     16 rows); A, private to a wave, goes from global memory straight into
-//     the MFMA register layout one chunk ahead;
-//   * the main loop is branch-free (clamped addresses instead of conditional
-//     loads) so the compiler's wait counts only cover the chunk in use;
-//   * the chunk's A-row scales (and per-column B scales for Wgrad) are staged
-//     in LDS beside the tile;
-//   * the epilogue stages the tile through LDS so every global store is a full
-//     16-byte row segment;
-//   * tiles are renumbered so that the workgroups of one XCD (dispatch is
-//     round-robin over the 8 XCDs) form a compact 2-D block of the output and
-//     share A rows and B columns in that XCD's L2.
+// Tiling: workgroup tile 256 x 128, four waves of 64 x 128 (4 x 8 sub-tiles).
+// B, shared by the waves, is converted to BF16 once per workgroup while it is
+// staged in a double-buffered LDS tile (272-byte row pitch: conflict-free
+// 16-byte reads across 16 rows); A, private to a wave, goes from global memory
+// into registers one chunk ahead and is converted per wave.  The chunk's
+// A-row scales (and per-column B scales for Wgrad) are staged in LDS beside
+// the tile; the epilogue stages the tile through LDS so every global store is
+// a full 16-byte row segment; tiles are renumbered so that the workgroups of
+// one XCD form a compact block of the output.
 //
-// Exact-accumulation variant (EXACT = true): gfx950's FP8 MFMA aligns the 8
-// products of each group of 8 consecutive K to the largest one and truncates
-// the others 13 bits below its exponent (measured), the analogue of the
-// limited accumulation the pages report for H800 tensor cores.  The EXACT
-// variant converts the codes exactly to BF16 (every E4M3 value is a BF16
-// value) and runs four v_mfma_f32_16x16x32_bf16 per chunk, whose products are
-// exact and whose sums are FP32; B is converted once per workgroup while it is
-// staged in LDS, A once per wave per chunk.  Same promotion, same epilogue.
-//
-// MFMA operand layout used (the same permutation of the 128 K positions for A
-// and B, which leaves every dot product unchanged): lane l supplies row l%16
-// of the 16-row slice, bytes [16g, 16g+16) and [64+16g, 64+16g+16) of the
-// chunk, g = l/16.  Result: lane l holds C[4g + r][l%16], r = 0..3.
+// Operand layout (the same permutation of the 128 K positions for A and B,
+// which leaves every dot product unchanged): lane l supplies row l%16 of the
+// 16-row slice, bytes [16g, 16g+16) and [64+16g, 64+16g+16) of the chunk,
+// g = l/16, as four quarters of 8 K.  Result: lane l holds C[4g + r][l%16].
 
 #include "device_common.h"
 #include "launch.h"
@@ -59,7 +46,7 @@ typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 
 constexpr int BK = 128;          // one chunk = one promotion interval
 constexpr int kMaxChunks = 1024; // contraction length limit: 1024 chunks of 128
-constexpr int BPITCH_X = 272;    // LDS row pitch of the BF16 B tile (exact variant)
+constexpr int BPITCH_X = 272;    // LDS row pitch of the BF16 B tile
 [[maybe_unused]] constexpr int GROUP_M = 4;  // m-tiles per band in the tile order
 
 // Tile configuration: WAVES_M x WAVES_N waves, each TM x TN MFMA sub-tiles of 16 x 16.
@@ -75,30 +62,15 @@ struct Cfg {
   static_assert(BN <= 128 && 128 % BN == 0, "a tile's columns share one 128-block");
 };
 
-#ifndef FP8Q_GEMM_CFG
-#define FP8Q_GEMM_CFG 1
-#endif
-#if FP8Q_GEMM_CFG == 0
-typedef Cfg<4, 2, 4, 4> DefaultCfg;   // 256 x 128, 8 waves of 64 x 64
-#elif FP8Q_GEMM_CFG == 1
 typedef Cfg<4, 1, 4, 8> DefaultCfg;   // 256 x 128, 4 waves of 64 x 128
-#elif FP8Q_GEMM_CFG == 2
-typedef Cfg<2, 2, 8, 4> DefaultCfg;   // 256 x 128, 4 waves of 128 x 64
-#elif FP8Q_GEMM_CFG == 3
-typedef Cfg<2, 1, 8, 8> DefaultCfg;   // 256 x 128, 2 waves of 128 x 128
-#endif
 
-// LDS of one workgroup.  Each pipeline stage has its own arrays (B tile, A
-// scales, B scales) so the compiler can tell a stage being read from the one
-// being filled by direct loads and does not wait for the latter; the epilogue
-// has its own staging area (FP32 tiles go out in two passes of half the rows).
-template <class C, int OUT_F32, bool EXACT>
+// LDS of one workgroup: two stages, each with its own arrays (BF16 B tile,
+// A scales, B scales); the epilogue has its own staging area (FP32 tiles go
+// out in two passes of half the rows).
+template <class C, int OUT_F32>
 struct Lds {
-  // FP8 tiles arrive by direct global->LDS loads: 128-byte rows, 16-byte
-  // chunks XOR-swizzled by (row & 7); BF16 tiles (exact variant) are written
-  // from registers with a padded pitch.
-  static constexpr int stage_b = C::BN * (EXACT ? BPITCH_X : BK);
-  static constexpr int stages = EXACT ? 2 : 3;  // pipeline depth (chunks in flight + 1)
+  static constexpr int stage_b = C::BN * BPITCH_X;  // BF16 rows with a padded pitch
+  static constexpr int stages = 2;                  // pipeline depth (chunks in flight + 1)
   static constexpr int epi_pitch = C::WN * (OUT_F32 ? 4 : 2) + 16;
   static constexpr int epi_passes = OUT_F32 ? 2 : 1;
   static constexpr int epi_rows = C::WM / epi_passes;
@@ -130,12 +102,12 @@ __device__ __forceinline__ v8i make_frag(uint4 lo, uint4 hi) {
   return f;
 }
 
-template <class C, int SB_MODE, int OUT_F32, bool GROUPED, bool EXACT>
+template <class C, int SB_MODE, int OUT_F32, bool GROUPED>
 __global__ __launch_bounds__(C::NT) void k_gemm(GemmArgs p) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
   constexpr int BM = C::BM, BN = C::BN, WM = C::WM, WN = C::WN, TM = C::TM, TN = C::TN, NT = C::NT;
   constexpr int UB = BN * 8 / NT;  // 16-byte B units per thread per chunk
-  typedef Lds<C, OUT_F32, EXACT> L;
+  typedef Lds<C, OUT_F32> L;
   constexpr int NS = L::stages, D = NS - 1;  // stages, prefetch distance in chunks
   constexpr int S2 = NS > 2 ? 1 : 0;           // third stage present
   __shared__ __attribute__((aligned(16))) uint8_t ldsB0[L::stage_b];
@@ -152,7 +124,7 @@ __global__ __launch_bounds__(C::NT) void k_gemm(GemmArgs p) {
   auto stB = [&](int stage) { return stage == 0 ? ldsB0 : stage == 1 ? ldsB1 : ldsB2; };
   auto stSa = [&](int stage) { return stage == 0 ? ldsSa0 : stage == 1 ? ldsSa1 : ldsSa2; };
   auto stSb = [&](int stage) { return stage == 0 ? ldsSb0 : stage == 1 ? ldsSb1 : ldsSb2; };
-  constexpr int kPitchB = EXACT ? BPITCH_X : BK;
+  constexpr int kPitchB = BPITCH_X;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -215,41 +187,26 @@ __global__ __launch_bounds__(C::NT) void k_gemm(GemmArgs p) {
     row = row < mend ? row : mend - 1;
     pa[i] = p.A + row * p.lda + 16 * g;
   }
-  // ---- B loader.  FP8 path: direct global->LDS (no registers): wave w's
-  // q-th 16-byte load lands at LDS unit (w*IB + q)*64 + lane, i.e. row
-  // unit/8, physical chunk lane%8, which holds logical chunk (lane%8)^(row&7).
-  // Exact path: unit u = tid + NT*q -> (row u/8, chunk u%8) through registers.
-  constexpr int IB = BN / (8 * C::NWAVES);   // DMA instructions per wave per chunk
+  // ---- B loader: unit u = tid + NT*q -> (row u/8, chunk u%8), through
+  // registers, converted to BF16 on the way into LDS
   const uint8_t* pb[UB];
   int lds_b[UB];
 #pragma unroll
   for (int q = 0; q < UB; ++q) {
-    if (EXACT) {
-      const int u = tid + NT * q, row = u >> 3, c = u & 7;
-      pb[q] = B + (int64_t)(n0 + row) * p.ldb + 16 * c;
-      lds_b[q] = row * kPitchB + 32 * c;
-    } else if (q < IB) {
-      const int row = (w * IB + q) * 8 + (lane >> 3);
-      const int c = (lane & 7) ^ (row & 7);
-      pb[q] = B + (int64_t)(n0 + row) * p.ldb + 16 * c;
-      lds_b[q] = (w * IB + q) * 1024;      // wave-uniform LDS base of the instruction
-    }
+    const int u = tid + NT * q, row = u >> 3, c = u & 7;
+    pb[q] = B + (int64_t)(n0 + row) * p.ldb + 16 * c;
+    lds_b[q] = row * kPitchB + 32 * c;
   }
   // ---- scale loaders.  Every thread issues the same loads (threads without a
   // scale of their own read a clamped, valid address and park the value in a
-  // spare LDS slot), so the main loop has no divergent branches and the
-  // compiler can track the prefetch loads across iterations.  FP8 path: the
-  // A scales go global->LDS with 4-byte direct loads, one per lane, by the
-  // first BM/64 waves.
-  int64_t sa_row = m0 + ((EXACT ? tid : w * 64 + lane) & (BM - 1));
+  // spare LDS slot), so the main loop has no divergent branches.
+  int64_t sa_row = m0 + (tid & (BM - 1));
   sa_row = sa_row < mend ? sa_row : mend - 1;
   const float* psa = p.sa + sa_row * p.ld_sa;
   const int lds_sa_slot = tid < BM ? tid : BM;  // BM: parking slot (never read)
   const float* psb_row = sb + (int64_t)(n0 + (tid & (BN - 1))) * p.sb_rs;
   const int lds_sb_slot = tid < BN ? tid : BN;
   const float* psb_blk = sb + (int64_t)(n0 / 128) * p.sb_rs;  // block mode: + kb * sb_cs
-  const float* psb_row_dma = sb + (int64_t)(n0 + ((w * 64 + lane) & (BN - 1))) * p.sb_rs;
-  typedef __attribute__((address_space(3))) void* lds_ptr;
 
   float acc[TM][TN][4];
 #pragma unroll
@@ -260,7 +217,7 @@ __global__ __launch_bounds__(C::NT) void k_gemm(GemmArgs p) {
       for (int r = 0; r < 4; ++r) acc[i][j][r] = 0.f;
 
   v8i abuf[NS][TM];     // A fragments of the chunks in flight, one set per stage
-  uint4 bst[UB];        // exact path: B staging registers
+  uint4 bst[UB];        // B staging registers
   float sav = 0.f, sbv = 0.f;
 
   auto load_a = [&](v8i (&a)[TM], int kb) {
@@ -272,28 +229,15 @@ __global__ __launch_bounds__(C::NT) void k_gemm(GemmArgs p) {
       a[i] = make_frag(lo, hi);
     }
   };
-  // FP8 path: issue the direct loads of chunk kb into LDS stage `stage`.
-  // Exact path: load chunk kb into registers (store_stage writes them).
+  // load chunk kb into registers (store_stage converts and writes them)
   auto load_stage = [&](int kb, int stage) {
-    if (!EXACT) {
-      uint8_t* dst = stB(stage);
+    (void)stage;
 #pragma unroll
-      for (int q = 0; q < IB; ++q)
-        __builtin_amdgcn_global_load_lds(pb[q] + (int64_t)kb * BK, (lds_ptr)(dst + lds_b[q]), 16, 0, 0);
-      // every wave issues one scale load per lane (no branch): waves past BM
-      // (or BN) re-read valid rows into parking slots
-      __builtin_amdgcn_global_load_lds(psa + kb, (lds_ptr)(stSa(stage) + w * 64), 4, 0, 0);
-      if (SB_MODE == kSbRow)
-        __builtin_amdgcn_global_load_lds(psb_row_dma + kb, (lds_ptr)(stSb(stage) + w * 64), 4, 0, 0);
-    } else {
-#pragma unroll
-      for (int q = 0; q < UB; ++q) bst[q] = *reinterpret_cast<const uint4*>(pb[q] + (int64_t)kb * BK);
-      sav = psa[kb];
-      if (SB_MODE == kSbRow) sbv = psb_row[kb];
-    }
+    for (int q = 0; q < UB; ++q) bst[q] = *reinterpret_cast<const uint4*>(pb[q] + (int64_t)kb * BK);
+    sav = psa[kb];
+    if (SB_MODE == kSbRow) sbv = psb_row[kb];
   };
   auto store_stage = [&](int stage) {
-    if (!EXACT) return;  // the direct loads already target the stage
     uint8_t* dst = stB(stage);
 #pragma unroll
     for (int q = 0; q < UB; ++q) {
@@ -317,42 +261,30 @@ __global__ __launch_bounds__(C::NT) void k_gemm(GemmArgs p) {
         sc[i][0] = s4.x; sc[i][1] = s4.y; sc[i][2] = s4.z; sc[i][3] = s4.w;
       }
     }
-    // exact variant: the wave's A fragments as BF16, four quarters of 8 K each
+    // the wave's A fragments as BF16, four quarters of 8 K each
     v8bf ax[TM][4];
-    if (EXACT) {
 #pragma unroll
-      for (int i = 0; i < TM; ++i)
+    for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int qq = 0; qq < 4; ++qq) ax[i][qq] = fp8x8_to_bf16((uint32_t)a[i][2 * qq], (uint32_t)a[i][2 * qq + 1]);
-    }
+      for (int qq = 0; qq < 4; ++qq) ax[i][qq] = fp8x8_to_bf16((uint32_t)a[i][2 * qq], (uint32_t)a[i][2 * qq + 1]);
     // Software pipeline over the TN column sub-tiles: the TM MFMAs of column
     // j+1 are issued before the promotion FMAs of column j, so the matrix core
     // works while the vector ALU scales and accumulates the previous partials.
     auto mfma_col = [&](int j, v4f (&pp)[TM]) {
       const int brow = wn * WN + 16 * j + l16;
-      if (EXACT) {
-        // quarter qq of lane group g covers K [16g + 8qq, +8) for qq < 2 and
-        // [64 + 16g + 8(qq-2), +8) for qq >= 2, matching the A fragment order
-        v8bf bx[4];
+      // quarter qq of lane group g covers K [16g + 8qq, +8) for qq < 2 and
+      // [64 + 16g + 8(qq-2), +8) for qq >= 2, matching the A fragment order
+      v8bf bx[4];
 #pragma unroll
-        for (int qq = 0; qq < 4; ++qq) {
-          const int k0 = (qq < 2 ? 0 : 64) + 16 * g + 8 * (qq & 1);
-          bx[qq] = *reinterpret_cast<const v8bf*>(bs + brow * BPITCH_X + 2 * k0);
-        }
+      for (int qq = 0; qq < 4; ++qq) {
+        const int k0 = (qq < 2 ? 0 : 64) + 16 * g + 8 * (qq & 1);
+        bx[qq] = *reinterpret_cast<const v8bf*>(bs + brow * BPITCH_X + 2 * k0);
+      }
 #pragma unroll
-        for (int i = 0; i < TM; ++i) {
-          pp[i] = v4f{0.f, 0.f, 0.f, 0.f};
+      for (int i = 0; i < TM; ++i) {
+        pp[i] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int qq = 0; qq < 4; ++qq) pp[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ax[i][qq], bx[qq], pp[i], 0, 0, 0);
-        }
-      } else {
-        const int sw = l16 & 7;               // == brow & 7
-        const uint4 lo = *reinterpret_cast<const uint4*>(bs + brow * BK + 16 * (g ^ sw));
-        const uint4 hi = *reinterpret_cast<const uint4*>(bs + brow * BK + 16 * ((4 + g) ^ sw));
-        const v8i b = make_frag(lo, hi);
-#pragma unroll
-        for (int i = 0; i < TM; ++i)
-          pp[i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[i], b, v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
+        for (int qq = 0; qq < 4; ++qq) pp[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ax[i][qq], bx[qq], pp[i], 0, 0, 0);
       }
     };
     auto promote_col = [&](int j, const v4f (&pp)[TM]) {
@@ -379,42 +311,15 @@ __global__ __launch_bounds__(C::NT) void k_gemm(GemmArgs p) {
       }
     }
     if (TN & 1) promote_col(TN - 1, pa0); else promote_col(TN - 1, pa1);
-    // Interleave: each MFMA (32 cycles on the matrix core) is followed by four
-    // promotion instructions of the previous column, so the vector ALU works
-    // while the matrix core does; B fragment reads are spread between columns.
-    if (!EXACT) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);   // scale + first B fragment reads
-      __builtin_amdgcn_sched_group_barrier(0x002, 4 * TM, 0);  // scale products
-#pragma unroll
-      for (int j = 0; j < TN; ++j) {
-#pragma unroll
-        for (int i = 0; i < TM; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-          __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);   // four VALU
-          if (i == 1) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // next B fragment
-        }
-      }
-      __builtin_amdgcn_sched_group_barrier(0x002, 4 * TM, 0);  // last column's promotion
-    }
   };
 
-  // ---- pipeline.  Chunk c lives in stage c % NS.  Iteration c issues the
-  // loads of chunk c + D (direct LDS loads for B and the scales, register
-  // loads for A), computes chunk c, waits until the direct loads of chunk c+1
-  // have landed and synchronises the workgroup.  The barrier is a bare
-  // s_barrier with compiler memory fences: __syncthreads() would also wait
-  // for every outstanding global load, i.e. drain the prefetch.
-  // Every iteration issues the same loads (past the last chunk the index is
-  // clamped, which re-reads the last chunk into a stage nobody reads again),
-  // so the instruction stream is branch-free and the wait counts are exact.
-  // VMEM instructions one iteration issues (direct loads counted only where
-  // every wave issues them): waiting for vmcnt <= kVm after an iteration's
-  // issue leaves exactly the previous chunk's A loads and this issue in flight.
-  constexpr int kVm = 4 * TM + IB + 1 + (SB_MODE == kSbRow ? 1 : 0);
-  static_assert(kVm < 64, "vmcnt range");
-  auto wait_stage = [&]() {
-    if (!EXACT) __builtin_amdgcn_s_waitcnt(0x0F70 | (kVm & 15) | ((kVm >> 4) << 14));
-  };
+  // ---- pipeline.  Chunk c lives in stage c % NS.  Iteration c loads chunk
+  // c + D into registers, computes chunk c, writes chunk c+1 (loaded the
+  // iteration before) into its stage and synchronises the workgroup.  The
+  // barrier is a bare s_barrier with compiler memory fences: __syncthreads()
+  // would also wait for every outstanding global load, i.e. drain the
+  // prefetch.  Past the last chunk the index is clamped (the last chunk is
+  // re-read into a stage nobody reads again), so every iteration is the same.
   auto block_sync = [&]() {
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS stores are done
@@ -432,11 +337,7 @@ __global__ __launch_bounds__(C::NT) void k_gemm(GemmArgs p) {
     for (int q = tid; q < nk; q += NT) ldsSbk[q] = psb_blk[(int64_t)q * p.sb_cs];
 #pragma unroll
   for (int c = 0; c < D; ++c) issue(min(c, nk - 1), c);
-  if (EXACT) store_stage(0);
-  if (!EXACT) {
-    constexpr int v0 = kVm - 2 * TM;  // chunk 1's loads may stay in flight
-    __builtin_amdgcn_s_waitcnt(0x0F70 | (v0 & 15) | ((v0 >> 4) << 14));
-  }
+  store_stage(0);
   block_sync();
 
   // The empty asm memory barriers stop the IR optimizers from moving loads of
@@ -450,8 +351,7 @@ __global__ __launch_bounds__(C::NT) void k_gemm(GemmArgs p) {
     compute(abuf[u], u, c);
     __builtin_amdgcn_sched_barrier(0);
     asm volatile("" ::: "memory");
-    if (EXACT) store_stage((u + 1) % NS);
-    wait_stage();
+    store_stage((u + 1) % NS);
     block_sync();
   };
   int kb = 0;
@@ -462,8 +362,6 @@ __global__ __launch_bounds__(C::NT) void k_gemm(GemmArgs p) {
 #pragma unroll
   for (int u = 0; u < NS - 1; ++u)
     if (kb + u < nk) step(kb + u, u);
-  // no direct load may still target LDS when the workgroup retires
-  __builtin_amdgcn_s_waitcnt(0x0F70);
 
   // ---- epilogue: stage this wave's tile in LDS (in passes of epi_rows rows),
   // then write full 16-byte row segments
@@ -514,7 +412,7 @@ __global__ __launch_bounds__(C::NT) void k_gemm(GemmArgs p) {
 #endif  // __HIP_DEVICE_COMPILE__
 }
 
-template <class C, int SB_MODE, int OUT_F32, bool GROUPED, bool EXACT>
+template <class C, int SB_MODE, int OUT_F32, bool GROUPED>
 static hipError_t launch_one(const GemmArgs& a, hipStream_t st) {
   int64_t tiles;
   const int64_t tiles_n = a.N / C::BN;
@@ -523,25 +421,26 @@ static hipError_t launch_one(const GemmArgs& a, hipStream_t st) {
   else
     tiles = ((a.M + C::BM - 1) / C::BM + a.E) * tiles_n;  // upper bound: one partial tile per expert
   if (tiles <= 0) return hipSuccess;
-  hipLaunchKernelGGL((k_gemm<C, SB_MODE, OUT_F32, GROUPED, EXACT>), dim3((uint32_t)tiles), dim3(C::NT), 0, st, a);
+  hipLaunchKernelGGL((k_gemm<C, SB_MODE, OUT_F32, GROUPED>), dim3((uint32_t)tiles), dim3(C::NT), 0, st, a);
   return hipGetLastError();
 }
 
-template <bool EXACT>
-static hipError_t launch_mode(const GemmArgs& a, hipStream_t st) {
+static hipError_t launch_exact(const GemmArgs& a, hipStream_t st) {
   typedef DefaultCfg C;
   const bool grouped = a.offsets != nullptr;
   if (a.sb_mode == kSbRow) {
     // per-column B scales: the weight-gradient product, FP32 output
-    return launch_one<C, kSbRow, 1, false, EXACT>(a, st);
+    return launch_one<C, kSbRow, 1, false>(a, st);
   }
   if (grouped)
-    return a.out_f32 ? launch_one<C, kSbBlock, 1, true, EXACT>(a, st) : launch_one<C, kSbBlock, 0, true, EXACT>(a, st);
-  return a.out_f32 ? launch_one<C, kSbBlock, 1, false, EXACT>(a, st) : launch_one<C, kSbBlock, 0, false, EXACT>(a, st);
+    return a.out_f32 ? launch_one<C, kSbBlock, 1, true>(a, st) : launch_one<C, kSbBlock, 0, true>(a, st);
+  return a.out_f32 ? launch_one<C, kSbBlock, 1, false>(a, st) : launch_one<C, kSbBlock, 0, false>(a, st);
 }
 
+// The FP8 entry points run the FP8 matrix-instruction kernel (gemm_fp8.hip);
+// the _exact ones this kernel.
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t st) {
-  return a.exact ? launch_mode<true>(a, st) : launch_gemm_fp8(a, st);
+  return a.exact ? launch_exact(a, st) : launch_gemm_fp8(a, st);
 }
 
 }  // namespace fp8q
