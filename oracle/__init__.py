@@ -42,12 +42,15 @@ Readings taken where the pages are silent:
 * Wgrad operands are grouped 1x128 along the token (contraction) axis.
 * the GEMM result is defined as the exact contraction of the dequantized
   operands; the FP32 promotion every 128 K is how a kernel approaches it.
+* Microscaling variant (``mx``): OCP MXFP8 E4M3, 1x32 blocks along the
+  contraction axis with E8M0 power-of-two scales; a comparison variant, not
+  the method.
 * MoE backward (``grouped``): an expert's tokens are quantized on their own
   for the weight gradient (no 128-token group mixes two experts), placed in
   a token-padded layout whose chunks each belong to one expert.
 """
 
-from . import e4m3, quant, gemm, grouped  # noqa: F401
+from . import e4m3, quant, gemm, grouped, mx  # noqa: F401
 from .e4m3 import decode, encode  # noqa: F401
 from .quant import (quant_act_1x128, quant_weight_128x128,  # noqa: F401
                     quant_transpose)

@@ -169,3 +169,21 @@ def test_wgrad_chunk_offset_error_is_caught(monkeypatch):
 
     monkeypatch.setattr(oracle, "grouped_wgrad_ref", shifted)
     _fails(grouped_pins.test_grouped_wgrad_closed_form)
+
+
+# ------------------------------------------------------------ microscaling
+import test_oracle_mx as mx_pins  # noqa: E402
+from oracle import mx  # noqa: E402
+
+
+def test_mx_exponent_off_by_one_is_caught(monkeypatch):
+    """E4M3's largest power of two taken as 2^7 instead of 2^8."""
+    real = mx.e8m0_of_amax
+    monkeypatch.setattr(mx, "e8m0_of_amax", lambda a: np.minimum(real(a).astype(int) + 1, 254).astype(np.uint8))
+    _fails(mx_pins.test_block_maximum_lands_in_the_top_binade)
+
+
+def test_mx_truncating_conversion_is_caught(monkeypatch):
+    real = e4m3.encode
+    monkeypatch.setattr(mx, "encode", lambda y: real(np.trunc(np.asarray(y, np.float64) * 4) / 4))
+    _fails(mx_pins.test_codes_match_brute_force, 0)
