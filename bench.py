@@ -11,7 +11,9 @@ One step = one pass of the whole hot path over one batch of synthetic inputs:
     quant_act(X) -> quant_weight(W stacked) -> grouped Fprop (bf16)
 Inputs are generated and resident in HBM before the timed region.
 
-Reported beside the step (not part of its value): the MoE layer's backward,
+Reported beside the step (not part of its value): the microscaling (MXFP8)
+variant of the linear layer's three products with its quantizers; the MoE
+layer's backward,
 dY [16384,2048] bf16 -> quant_act(dY), quant_weight(W stacked, +q_t) ->
 grouped Dgrad (bf16); grouped quant_transpose(X), (dY) -> grouped Wgrad
 (dW [32,2048,7168] fp32), timed the same way over its own passes.
@@ -33,7 +35,8 @@ if ROOT not in sys.path:
 PEAK_FP8_TFLOPS = 5000.0      # MI355X dense FP8 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-KERNEL_SOURCES = ["quant_kernels.hip", "gemm_fp8.hip", "gemm_kernels.hip", "gemm_tile.h", "device_common.h"]
+KERNEL_SOURCES = ["quant_kernels.hip", "gemm_fp8.hip", "gemm_kernels.hip", "gemm_tile.h", "device_common.h",
+                  "quant_mx.hip", "gemm_mx.hip"]
 
 
 def log(msg):
@@ -158,6 +161,41 @@ def make_dual_ops(L, dev):
         work = m * c * 4 + (m * cdiv(c, 128) + c * cdiv(m, 128)) * 4
         ops.append((f"quant_act_transpose {name}",
                     (lambda x=x, b=bufs: fq.fp8q_quant_act_transpose(x, *b)), "hbm", work))
+    return ops
+
+
+def make_mx_ops(L, dev):
+    """The linear layer's step in the microscaling variant (MXFP8 E4M3, 1x32
+    blocks along each product's contraction axis, E8M0 scales): one dual
+    quantizer per tensor (row blocks and transposed column blocks from one
+    read), then Fprop, Dgrad and Wgrad through the block-scaled MFMA GEMM."""
+    import torch
+    import fp8_fine_grained_quant_amd as fq
+
+    u8 = torch.uint8
+    e = lambda *s, dt=u8: torch.empty(*s, dtype=dt, device=dev)
+    M, K = L["x"].shape
+    N = L["w"].shape[0]
+    Q = {}
+    for name, t in (("x", L["x"]), ("w", L["w"]), ("dy", L["dy"])):
+        r, c = t.shape
+        Q[name] = (e(r, c), e(r, cdiv(c, 32)), e(c, r), e(c, cdiv(r, 32)))
+    y, dx, dw = e(M, N, dt=torch.bfloat16), e(M, K, dt=torch.bfloat16), e(N, K, dt=torch.float32)
+    qbytes = lambda r, c, es: r * c * (es + 2) + (r * cdiv(c, 32) + c * cdiv(r, 32))
+    xq, xs, xq_t, xs_t = Q["x"]
+    wq, ws, wq_t, ws_t = Q["w"]
+    dyq, dys, dyq_t, dys_t = Q["dy"]
+    ops = [
+        ("mx quant X (rows + cols)", lambda: fq.fp8q_quant_mx_transpose(L["x"], xq_t, xs_t, xq, xs), "hbm",
+         qbytes(M, K, 2)),
+        ("mx quant W (rows + cols)", lambda: fq.fp8q_quant_mx_transpose(L["w"], wq_t, ws_t, wq, ws), "hbm",
+         qbytes(N, K, 4)),
+        ("mx gemm fprop", lambda: fq.fp8q_gemm_mx(xq, xs, wq, ws, y), "mfma", 2.0 * M * N * K),
+        ("mx quant dY (rows + cols)", lambda: fq.fp8q_quant_mx_transpose(L["dy"], dyq_t, dys_t, dyq, dys), "hbm",
+         qbytes(M, N, 2)),
+        ("mx gemm dgrad", lambda: fq.fp8q_gemm_mx(dyq, dys, wq_t, ws_t, dx), "mfma", 2.0 * M * N * K),
+        ("mx gemm wgrad", lambda: fq.fp8q_gemm_mx(dyq_t, dys_t, xq_t, xs_t, dw), "mfma", 2.0 * M * N * K),
+    ]
     return ops
 
 
@@ -331,6 +369,17 @@ def main():
     log(f"dual-output quantizer: warmup {args.warmup}, timing {args.steps} passes")
     _, dkernels = time_ops(dops, args.steps, args.warmup, stream)
 
+    # the microscaling variant of the linear layer's step, beside the step
+    mops = make_mx_ops(L, dev)
+    log(f"microscaling variant: warmup {args.warmup}, timing {args.steps} passes")
+    ms_mx, mkernels = time_ops(mops, args.steps, args.warmup, stream)
+    mx_flops = sum(w for _, _, k, w in mops if k == "mfma")
+    lin = ["quant_act X", "quant_weight W (+q_t)", "gemm_fprop", "quant_act dY", "gemm_dgrad", "quant_transpose X",
+           "quant_transpose dY", "gemm_wgrad"]
+    lin_us = sum(kernels[n]["avg_us"] for n in lin)
+    lin_dual_us = lin_us - sum(kernels[f"quant_act {n}"]["avg_us"] + kernels[f"quant_transpose {n}"]["avg_us"]
+                               for n in ("X", "dY")) + sum(d["avg_us"] for d in dkernels.values())
+
     gemm_flops = sum(w for _, _, k, w in ops if k == "mfma")
     value = gemm_flops / (ms_step * 1e-3) / 1e12
     dom = max(range(len(ops)), key=lambda i: kernels[names[i]]["avg_us"])
@@ -388,6 +437,15 @@ def main():
             "kernels": dkernels,
             "separate_us": {n: round(kernels[f"quant_act {n}"]["avg_us"] + kernels[f"quant_transpose {n}"]["avg_us"],
                                      2) for n in ("X", "dY")},
+        },
+        "microscaling_variant": {
+            "workload": "the linear layer's Fprop+Dgrad+Wgrad (shapes as the step) in MXFP8 E4M3: 1x32 blocks "
+                        "along each product's contraction axis, E8M0 scales applied by the block-scaled MFMA; "
+                        "one dual quantizer per tensor",
+            "ms_per_pass": round(ms_mx, 4),
+            "gemm_tflops": round(mx_flops / (ms_mx * 1e-3) / 1e12, 2),
+            "method_linear_layer_us": {"as_step": round(lin_us, 2), "with_dual_quantizers": round(lin_dual_us, 2)},
+            "kernels": mkernels,
         },
         "cpu_baseline": cpu,
     }

@@ -15,13 +15,17 @@ tensors in place of pointer + leading dimension):
     fp8q_gemm_dgrad(dyq, dys, wq_t, ws, dx)
     fp8q_gemm_wgrad(dyq_t, dys_t, xq_t, xs_t, dw, accumulate=False)
     fp8q_grouped_gemm(xq, xs, wq, ws, offsets, y)
+    fp8q_quant_mx_1x32(x, q, s)                        # microscaling variant
+    fp8q_quant_mx_transpose(x, q_t, s_t, q=None, s=None)
+    fp8q_gemm_mx(aq, as_, bq, bs, c, accumulate=False)
 
 Each GEMM also takes exact=True, which calls the *_exact entry point (BF16
 matrix instruction on exactly converted codes: the exact-accumulation variant).
 
 Convenience wrappers that allocate the outputs: quant_act_1x128,
 quant_weight_128x128, quant_transpose, gemm_fprop, gemm_dgrad, gemm_wgrad,
-grouped_gemm.
+grouped_gemm, quant_mx, quant_mx_transpose, gemm_mx (and those of the MoE
+backward and the dual-output quantizer).
 """
 
 import ctypes
@@ -39,7 +43,8 @@ EXPORTS = ["fp8q_status_string", "fp8q_quant_act_1x128", "fp8q_quant_weight_128x
            "fp8q_quant_transpose", "fp8q_gemm_fprop", "fp8q_gemm_dgrad", "fp8q_gemm_wgrad",
            "fp8q_grouped_gemm", "fp8q_gemm_fprop_exact", "fp8q_gemm_dgrad_exact", "fp8q_gemm_wgrad_exact",
            "fp8q_grouped_gemm_exact", "fp8q_quant_transpose_grouped", "fp8q_grouped_gemm_dgrad",
-           "fp8q_grouped_gemm_wgrad", "fp8q_quant_act_transpose"]
+           "fp8q_grouped_gemm_wgrad", "fp8q_quant_act_transpose", "fp8q_quant_mx_1x32",
+           "fp8q_quant_mx_transpose", "fp8q_gemm_mx"]
 
 
 class Fp8qError(RuntimeError):
@@ -73,6 +78,9 @@ def load_library(path=LIB_PATH):
         "fp8q_quant_act_transpose": ([P, I32, I64, I64, I64, P, I64, P, I64, P, I64, P, I64, P], I32),
         "fp8q_grouped_gemm_dgrad": ([P, P, P, P, P, I64, I64, I64, I64, P, I32, I64, P], I32),
         "fp8q_grouped_gemm_wgrad": ([P, P, P, P, P, I64, I64, I64, I64, I64, P, I32, P], I32),
+        "fp8q_quant_mx_1x32": ([P, I32, I64, I64, I64, P, I64, P, I64, P], I32),
+        "fp8q_quant_mx_transpose": ([P, I32, I64, I64, I64, P, I64, P, I64, P, I64, P, I64, P], I32),
+        "fp8q_gemm_mx": ([P, P, I64, I64, P, P, I64, I64, I64, I64, I64, P, I32, I64, I32, P], I32),
     }
     for name in ["fp8q_gemm_fprop", "fp8q_gemm_dgrad", "fp8q_gemm_wgrad", "fp8q_grouped_gemm"]:
         sig[name + "_exact"] = sig[name]
@@ -261,6 +269,39 @@ def fp8q_grouped_gemm_wgrad(dyq_t, dys_t, xq_t, xs_t, offsets, m_total, dw, accu
            "fp8q_grouped_gemm_wgrad")
 
 
+def fp8q_quant_mx_1x32(x, q, s, stream=None):
+    _on_gpu(x, q, s)
+    rows, cols = x.shape
+    _check(load_library().fp8q_quant_mx_1x32(_ptr(x), _dtype_code(x), rows, cols, _ld(x), _ptr(q), _ld(q),
+                                              _ptr(s), _ld(s), _stream(stream)),
+           "fp8q_quant_mx_1x32")
+
+
+def fp8q_quant_mx_transpose(x, q_t, s_t, q=None, s=None, stream=None):
+    _on_gpu(x, q_t, s_t, q, s)
+    rows, cols = x.shape
+    ldq = _ld(q) if q is not None else 0
+    lds = _ld(s) if s is not None else 0
+    _check(load_library().fp8q_quant_mx_transpose(_ptr(x), _dtype_code(x), rows, cols, _ld(x), _ptr(q_t),
+                                                   _ld(q_t), _ptr(s_t), _ld(s_t), _ptr(q), ldq, _ptr(s), lds,
+                                                   _stream(stream)),
+           "fp8q_quant_mx_transpose")
+
+
+def fp8q_gemm_mx(aq, as_, bq, bs, c, accumulate=False, stream=None):
+    """C [M, N] (= or +=) A . B^T; aq [M, K], as_ [M, >= K/32], bq [N, K],
+    bs [N, >= K/32] (uint8 codes and E8M0 bytes, rows may be padded)."""
+    _on_gpu(aq, as_, bq, bs, c)
+    m, k = aq.shape
+    n = bq.shape[0]
+    if bq.shape[1] != k:
+        raise ValueError("A and B share the contraction length")
+    _check(load_library().fp8q_gemm_mx(_ptr(aq), _ptr(as_), _ld(aq), _ld(as_), _ptr(bq), _ptr(bs), _ld(bq),
+                                        _ld(bs), m, n, k, _ptr(c), _dtype_code(c), _ld(c), int(bool(accumulate)),
+                                        _stream(stream)),
+           "fp8q_gemm_mx")
+
+
 # ---------------------------------------------------------------- convenience
 def _cdiv(a, b):
     return (a + b - 1) // b
@@ -355,3 +396,36 @@ def quant_act_transpose(x, stream=None):
     s_t = torch.empty((cols, _cdiv(rows, 128)), dtype=torch.float32, device=x.device)
     fp8q_quant_act_transpose(x, q, s, q_t, s_t, stream)
     return q, s, q_t, s_t
+
+
+def quant_mx(x, stream=None):
+    """MXFP8 along rows: (q [rows, cols], s [rows, ceil(cols/32)] E8M0 bytes)."""
+    rows, cols = x.shape
+    q = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
+    s = torch.empty((rows, _cdiv(cols, 32)), dtype=torch.uint8, device=x.device)
+    fp8q_quant_mx_1x32(x, q, s, stream)
+    return q, s
+
+
+def quant_mx_transpose(x, dual=False, stream=None):
+    """MXFP8 along columns, transposed: (q_t, s_t), or with dual=True
+    (q, s, q_t, s_t) from one read of x."""
+    rows, cols = x.shape
+    q_t = torch.empty((cols, rows), dtype=torch.uint8, device=x.device)
+    s_t = torch.empty((cols, _cdiv(rows, 32)), dtype=torch.uint8, device=x.device)
+    if not dual:
+        fp8q_quant_mx_transpose(x, q_t, s_t, stream=stream)
+        return q_t, s_t
+    q = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
+    s = torch.empty((rows, _cdiv(cols, 32)), dtype=torch.uint8, device=x.device)
+    fp8q_quant_mx_transpose(x, q_t, s_t, q, s, stream=stream)
+    return q, s, q_t, s_t
+
+
+def gemm_mx(aq, as_, bq, bs, out_dtype=torch.bfloat16, c=None, stream=None):
+    """A . B^T of MX operands; with c given (FP32), adds into it."""
+    accumulate = c is not None
+    if c is None:
+        c = torch.empty((aq.shape[0], bq.shape[0]), dtype=out_dtype, device=aq.device)
+    fp8q_gemm_mx(aq, as_, bq, bs, c, accumulate, stream)
+    return c

@@ -28,7 +28,7 @@ constexpr int64_t kMaxContraction = 1024 * 128;  // the GEMM keeps one scale per
 // out_len bytes per row, scale array of scale_rows x scale_cols with stride
 // ld_s.
 fp8q_status check_quant(const void* in, int in_es, int64_t rows, int64_t cols, int64_t ld_in,
-                        const void* out, int64_t ld_out, int64_t out_len, const float* s, int64_t ld_s,
+                        const void* out, int64_t ld_out, int64_t out_len, const void* s, int64_t ld_s,
                         int64_t scale_cols) {
   if (rows < 0 || cols < 0 || rows > kMaxDim || cols > kMaxDim) return FP8Q_ERR_SHAPE;
   if (rows == 0 || cols == 0) return FP8Q_OK;
@@ -316,6 +316,62 @@ fp8q_status fp8q_grouped_gemm_exact(const uint8_t* xq, const float* xs, const ui
                                     const int32_t* offsets, int64_t E, int64_t M_total, int64_t N, int64_t K,
                                     void* y, fp8q_dtype yt, int64_t ld_y, hipStream_t stream) {
   return fp8q_grouped_gemm_impl(1, xq, xs, wq, ws, offsets, E, M_total, N, K, y, yt, ld_y, stream);
+}
+
+}  // extern "C"
+
+extern "C" {
+
+fp8q_status fp8q_quant_mx_1x32(const void* x, fp8q_dtype xt, int64_t rows, int64_t cols, int64_t ld_x, uint8_t* q,
+                               int64_t ld_q, uint8_t* s, int64_t ld_s, hipStream_t stream) {
+  if (!valid_dtype(xt)) return FP8Q_ERR_DTYPE;
+  const fp8q_status c = check_quant(x, esize(xt), rows, cols, ld_x, q, ld_q, cols, s, ld_s, cdiv(cols, 32));
+  if (c != FP8Q_OK || rows == 0 || cols == 0) return c;
+  if (rows * cdiv(cols, 128) > kMaxGroups) return FP8Q_ERR_SHAPE;
+  return launched(fp8q::launch_quant_mx(x, xt == FP8Q_BF16, rows, cols, ld_x, q, ld_q, s, ld_s, stream));
+}
+
+fp8q_status fp8q_quant_mx_transpose(const void* x, fp8q_dtype xt, int64_t rows, int64_t cols, int64_t ld_x,
+                                    uint8_t* q_t, int64_t ld_qt, uint8_t* s_t, int64_t ld_st, uint8_t* q,
+                                    int64_t ld_q, uint8_t* s, int64_t ld_s, hipStream_t stream) {
+  if (!valid_dtype(xt)) return FP8Q_ERR_DTYPE;
+  if ((q == nullptr) != (s == nullptr)) return FP8Q_ERR_NULL;
+  fp8q_status c = check_quant(x, esize(xt), rows, cols, ld_x, q_t, ld_qt, rows, s_t, ld_st, cdiv(rows, 32));
+  if (c != FP8Q_OK || rows == 0 || cols == 0) return c;
+  if (q) {
+    c = check_quant(x, esize(xt), rows, cols, ld_x, q, ld_q, cols, s, ld_s, cdiv(cols, 32));
+    if (c != FP8Q_OK) return c;
+  }
+  if (cdiv(rows, 128) > 65535) return FP8Q_ERR_SHAPE;
+  return launched(fp8q::launch_quant_mx_transpose(x, xt == FP8Q_BF16, rows, cols, ld_x, q_t, ld_qt, s_t, ld_st, q,
+                                                  ld_q, s, ld_s, stream));
+}
+
+fp8q_status fp8q_gemm_mx(const uint8_t* aq, const uint8_t* as, int64_t lda, int64_t ld_sa, const uint8_t* bq,
+                         const uint8_t* bs, int64_t ldb, int64_t ld_sb, int64_t M, int64_t N, int64_t K, void* c,
+                         fp8q_dtype ct, int64_t ld_c, int accumulate, hipStream_t stream) {
+  if (M < 0 || N < 0 || K < 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim) return FP8Q_ERR_SHAPE;
+  if (N % 128 != 0 || K % 128 != 0 || K > kMaxContraction) return FP8Q_ERR_SHAPE;
+  if (accumulate != 0 && accumulate != 1) return FP8Q_ERR_SHAPE;
+  if (!valid_dtype(ct)) return FP8Q_ERR_DTYPE;
+  if (accumulate && ct != FP8Q_F32) return FP8Q_ERR_DTYPE;
+  if (M == 0 || N == 0) return FP8Q_OK;
+  if (K == 0) return FP8Q_ERR_SHAPE;
+  if (!aq || !as || !bq || !bs) return FP8Q_ERR_NULL;
+  const fp8q_status st = check_gemm_out(c, ct, ld_c, N);
+  if (st != FP8Q_OK) return st;
+  if (lda < K || ldb < K || ld_sa < K / 32 || ld_sb < K / 32) return FP8Q_ERR_STRIDE;
+  if (!aligned16(aq) || !aligned16(bq) || lda % 16 != 0 || ldb % 16 != 0) return FP8Q_ERR_ALIGN;
+  if (!aligned4(as) || !aligned4(bs) || ld_sa % 4 != 0 || ld_sb % 4 != 0) return FP8Q_ERR_ALIGN;
+  // the kernel's buffer descriptors address one tile's rows with 32-bit offsets
+  if (256 * lda > INT32_MAX || 128 * ldb > INT32_MAX) return FP8Q_ERR_SHAPE;
+  fp8q::MxArgs a{};
+  a.g.A = aq; a.g.B = bq; a.g.C = c;
+  a.g.lda = lda; a.g.ldb = ldb; a.g.ldc = ld_c;
+  a.g.M = M; a.g.N = N; a.g.K = K;
+  a.g.out_f32 = ct == FP8Q_F32; a.g.accumulate = accumulate;
+  a.sa = as; a.sb = bs; a.ld_sa = ld_sa; a.ld_sb = ld_sb;
+  return launched(fp8q::launch_gemm_mx(a, stream));
 }
 
 }  // extern "C"

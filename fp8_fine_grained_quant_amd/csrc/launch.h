@@ -64,4 +64,25 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t st);
 // the FP8 matrix-instruction kernel (a.exact == 0)
 hipError_t launch_gemm_fp8(const GemmArgs& a, hipStream_t st);
 
+// Microscaling (MXFP8 E4M3) quantizers: one E8M0 scale byte per 32
+// consecutive elements, along rows (quant_mx) or along columns with the
+// codes transposed (quant_mx_transpose; q, s optional row outputs of the same
+// read, NULL to skip).
+hipError_t launch_quant_mx(const void* x, bool x_bf16, int64_t rows, int64_t cols, int64_t ld_x, uint8_t* q,
+                           int64_t ld_q, uint8_t* s, int64_t ld_s, hipStream_t st);
+hipError_t launch_quant_mx_transpose(const void* x, bool x_bf16, int64_t rows, int64_t cols, int64_t ld_x,
+                                     uint8_t* q_t, int64_t ld_qt, uint8_t* s_t, int64_t ld_st, uint8_t* q,
+                                     int64_t ld_q, uint8_t* s, int64_t ld_s, hipStream_t st);
+
+// MX GEMM: C = A . B^T, both operands blocked along K with E8M0 bytes
+// sa[m*ld_sa + k/32], sb[n*ld_sb + k/32] (strides in bytes).  g carries A, B,
+// C, their strides, M, N, K, out_f32 and accumulate; its scale fields are unused.
+struct MxArgs {
+  GemmArgs g;
+  const uint8_t* sa;
+  const uint8_t* sb;
+  int64_t ld_sa, ld_sb;
+};
+hipError_t launch_gemm_mx(const MxArgs& a, hipStream_t st);
+
 }  // namespace fp8q

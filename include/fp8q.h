@@ -275,6 +275,65 @@ fp8q_status fp8q_grouped_gemm_exact(const uint8_t* xq, const float* xs, const ui
                                     const int32_t* offsets, int64_t E, int64_t M_total, int64_t N, int64_t K,
                                     void* y, fp8q_dtype yt, int64_t ld_y, hipStream_t stream);
 
+/*
+ * Microscaling variant (MXFP8 with E4M3 elements, OCP Microscaling v1.0).
+ * The pages set the method's FP32 group scales against the small-group
+ * power-of-two scaling that newer tensor cores support natively (the
+ * innerforce.co.kr excerpt, paragraph on Figure 7 (a)); gfx950's counterpart
+ * is the block-scaled matrix instruction.  Numerics differ from the method:
+ *   block : 32 consecutive elements along the contraction axis, for BOTH
+ *           GEMM operands (so every operand of the three products is
+ *           quantized along its own contraction axis, see fp8q_gemm_mx);
+ *   scale : one E8M0 byte per block, e = clamp(floor(log2 amax) - 8 + 127,
+ *           0, 254), value 2^(e - 127); an all-zero block has e = 0;
+ *   codes : E4M3FN(x / 2^(e - 127)), round-to-nearest-even, saturating at
+ *           +-448, the sign of zero kept.
+ * Scale arrays hold bytes; `ld_s`-type strides are in bytes.
+ */
+
+/*
+ * 1x32 MX quantization along rows.
+ *   x : [rows, cols] BF16 or FP32, stride ld_x (16-byte aligned rows)
+ *   q : [rows, cols] codes, stride ld_q (multiple of 16)
+ *   s : [rows, ceil(cols/32)] E8M0 bytes, stride ld_s >= ceil(cols/32)
+ * A trailing partial block uses the elements present.  Any rows, cols >= 0.
+ */
+fp8q_status fp8q_quant_mx_1x32(const void* x, fp8q_dtype xt, int64_t rows, int64_t cols, int64_t ld_x, uint8_t* q,
+                               int64_t ld_q, uint8_t* s, int64_t ld_s, hipStream_t stream);
+
+/*
+ * MX quantization along columns, codes written transposed: the 1x32 rule
+ * applied to x^T (a block is 32 consecutive rows of one column).
+ *   q_t : [cols, rows] codes, q_t[c, r] = code of x[r, c], stride ld_qt >= rows
+ *   s_t : [cols, ceil(rows/32)] E8M0 bytes, stride ld_st
+ *   q, s : optional (both NULL, or both set): the fp8q_quant_mx_1x32 outputs
+ *          of the same x, produced from the same single read of x.
+ * Rules: ceil(rows/128) <= 65535.
+ */
+fp8q_status fp8q_quant_mx_transpose(const void* x, fp8q_dtype xt, int64_t rows, int64_t cols, int64_t ld_x,
+                                    uint8_t* q_t, int64_t ld_qt, uint8_t* s_t, int64_t ld_st, uint8_t* q,
+                                    int64_t ld_q, uint8_t* s, int64_t ld_s, hipStream_t stream);
+
+/*
+ * MX GEMM: C[M,N] (= or +=) A[M,K] . B[N,K]^T with both operands MX-quantized
+ * along K.  Fprop: A = X, B = W (fp8q_quant_mx_1x32 of each).  Dgrad: A = dY,
+ * B = the q_t / s_t of fp8q_quant_mx_transpose(W).  Wgrad: A = q_t of dY,
+ * B = q_t of X (both from fp8q_quant_mx_transpose), K = tokens.
+ *   aq : [M, K] codes, stride lda >= K (multiple of 16, aq 16-byte aligned)
+ *   as : [M, K/32] E8M0 bytes, stride ld_sa >= K/32, ld_sa % 4 == 0, 4-byte
+ *        aligned (16-byte aligned rows load faster)
+ *   bq, bs : [N, K], [N, K/32], the same rules with ldb, ld_sb
+ *   c  : [M, N] of type ct, stride ld_c (rules as fp8q_gemm_fprop's y)
+ *   accumulate : 0 stores, 1 adds to c (FP32 output only)
+ * The scales are applied by the matrix instruction to every product, which
+ * it accumulates in FP32 (within each group of 8 consecutive K, 14 bits below
+ * the largest product are kept, as for the FP8 entry points).
+ * Rules: K % 128 == 0, N % 128 == 0, K <= 131072, any M >= 0.
+ */
+fp8q_status fp8q_gemm_mx(const uint8_t* aq, const uint8_t* as, int64_t lda, int64_t ld_sa, const uint8_t* bq,
+                         const uint8_t* bs, int64_t ldb, int64_t ld_sb, int64_t M, int64_t N, int64_t K, void* c,
+                         fp8q_dtype ct, int64_t ld_c, int accumulate, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -46,8 +46,9 @@ def test_every_kernel_launch_stub_is_defined(lib):
     out = subprocess.run(["nm", "-D", fq.LIB_PATH], capture_output=True, text=True).stdout
     undefined = [l for l in out.splitlines() if " U " in l and "__device_stub__" in l]
     assert not undefined, undefined[:3]
-    # 3 quantizers (+1 grouped transpose) + 6 FP8 GEMM and 5 exact GEMM instantiations
-    assert sum(1 for l in out.splitlines() if "__device_stub__" in l) >= 15
+    # quantizers (1x128, 128x128, transposing, grouped, dual; MX rows and
+    # transposing), FP8, exact and MX GEMM instantiations
+    assert sum(1 for l in out.splitlines() if "__device_stub__" in l) >= 25
 
 
 def test_status_strings(lib):
@@ -115,6 +116,31 @@ def test_grouped_backward_argument_errors(lib):
     assert gw(A16, A16, A16, A16, A16, 4, 300, 128, 200, 768, A16, 0, None) == SHAPE   # K % 128
     assert gw(A16, A16, A16, A16, A16, 4, 300, 128, 256, 768, A16, 2, None) == SHAPE   # accumulate flag
     assert gw(A16, A16, A16, A16, A16, 4, 300, 0, 256, 768, A16, 0, None) == OK        # N = 0
+
+
+def test_mx_argument_errors(lib):
+    q = lib.fp8q_quant_mx_1x32
+    assert q(A16, 0, 4, 128, 128, A16, 128, A16, 3, None) == STRIDE       # ld_s < 4 blocks
+    assert q(A16, 0, 4, 100, 100, A16, 112, A16, 4, None) == ALIGN        # 200-byte rows
+    assert q(A16, 2, 4, 128, 128, A16, 128, A16, 4, None) == DTYPE
+    assert q(A16, 0, 0, 128, 128, None, 128, None, 4, None) == OK         # empty: no-op
+    t = lib.fp8q_quant_mx_transpose
+    assert t(A16, 0, 300, 64, 64, A16, 304, A16, 9, None, 0, None, 0, None) == STRIDE    # ld_st < 10
+    assert t(A16, 0, 300, 64, 64, A16, 304, A16, 10, A16, 64, None, 0, None) == NULL     # q without s
+    assert t(A16, 0, 300, 64, 64, A16, 304, A16, 10, A16, 64, A16, 1, None) == STRIDE    # ld_s < 2
+    g = lib.fp8q_gemm_mx
+    #        aq   as   lda  ldsa bq   bs   ldb  ldsb M   N    K    c    ct ldc acc
+    assert g(A16, A16, 256, 8, A16, A16, 256, 8, 64, 128, 200, A16, 0, 128, 0, None) == SHAPE   # K % 128
+    assert g(A16, A16, 256, 8, A16, A16, 256, 8, 64, 100, 256, A16, 0, 128, 0, None) == SHAPE   # N % 128
+    assert g(A16, A16, 256, 8, A16, A16, 256, 8, 64, 128, 256, A16, 0, 128, 1, None) == DTYPE   # += into BF16
+    assert g(A16, A16, 256, 8, A16, A16, 256, 8, 64, 128, 256, A16, 1, 128, 2, None) == SHAPE   # flag
+    assert g(A16, A16, 256, 7, A16, A16, 256, 8, 64, 128, 256, A16, 0, 128, 0, None) == STRIDE  # ld_sa < K/32
+    assert g(A16, A16, 248, 8, A16, A16, 256, 8, 64, 128, 256, A16, 0, 128, 0, None) == STRIDE  # lda < K
+    assert g(A16, A16, 264, 8, A16, A16, 256, 8, 64, 128, 256, A16, 0, 128, 0, None) == ALIGN   # lda % 16
+    assert g(A16, A16, 256, 10, A16, A16, 256, 8, 64, 128, 256, A16, 0, 128, 0, None) == ALIGN  # ld_sa % 4
+    assert g(A16, A16 + 2, 256, 8, A16, A16, 256, 8, 64, 128, 256, A16, 0, 128, 0, None) == ALIGN
+    assert g(A16, None, 256, 8, A16, A16, 256, 8, 64, 128, 256, A16, 0, 128, 0, None) == NULL
+    assert g(A16, A16, 256, 8, A16, A16, 256, 8, 0, 128, 256, None, 0, 128, 0, None) == OK      # M = 0
 
 
 def test_binding_refuses_cpu_tensors():
