@@ -188,20 +188,29 @@ __global__ __launch_bounds__(256) void k_quant_mx_t(const typename In::elem* __r
       if ((c8 & 3) == 0) s[(int64_t)r * ld_s + (c0 >> 5)] = (uint8_t)byte;
     }
   }
-  const bool block_present = bi * 128 + wv * 32 < rows;  // this wave's 32-row block has rows
-  const bool full_r = r0 + 8 <= rows;
-  const int oc0 = bi * 128 + rblk * 8;  // output token column of this thread's rows
+  // column maxima over the wave's 32 rows: all 16 cross-lane exchanges are
+  // issued before any of them is waited for
+  uint32_t m[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     uint32_t a = 0;
 #pragma unroll
     for (int i = 0; i < 8; ++i) a = max(a, abs_bits(v[i][e]));
-    a = max(a, (uint32_t)__shfl_xor((int)a, 16));
-    a = max(a, (uint32_t)__shfl_xor((int)a, 32));
+    m[e] = a;
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) m[e] = max(m[e], (uint32_t)__shfl_xor((int)m[e], 16));
+#pragma unroll
+  for (int e = 0; e < 8; ++e) m[e] = max(m[e], (uint32_t)__shfl_xor((int)m[e], 32));
+  const bool block_present = bi * 128 + wv * 32 < rows;  // this wave's 32-row block has rows
+  const bool full_r = r0 + 8 <= rows;
+  const int oc0 = bi * 128 + rblk * 8;  // output token column of this thread's rows
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
     const int c = c0 + e;
-    if (c >= cols) continue;
+    if (c >= cols) break;
     float iv;
-    const uint32_t byte = mx_scale(a, iv);
+    const uint32_t byte = mx_scale(m[e], iv);
     if ((t & 63) < 16 && block_present) st[(int64_t)c * ld_st + bi * 4 + wv] = (uint8_t)byte;
     const uint32_t d0 = pack4_e4m3(v[0][e] * iv, v[1][e] * iv, v[2][e] * iv, v[3][e] * iv);
     const uint32_t d1 = pack4_e4m3(v[4][e] * iv, v[5][e] * iv, v[6][e] * iv, v[7][e] * iv);
