@@ -18,18 +18,27 @@
 namespace fp8q {
 
 // Non-temporal choices per access (see ld_stream16): the weight loads and
-// row codes (long streams of full segments) are non-temporal; the transposed
-// codes (short scattered segments) stay cached so that neighbouring segments
-// merge in L2; the activation quantizer uses plain accesses throughout.
-constexpr int kNtWeightLoad = 1, kNtWeightStore = 1, kNtWeightTStore = 0, kNtTransStore = 0;
+// row codes (long streams of full segments) and the activation quantizer's
+// loads and codes are non-temporal; the transposers read non-temporally but
+// keep their transposed codes (short scattered segments) cached so that
+// neighbouring segments merge in L2.  Measured on MI355X with inputs that are
+// not cache-resident, as in a training step.
+constexpr int kNtWeightLoad = 1, kNtWeightStore = 1, kNtWeightTStore = 0, kNtTransLoad = 1, kNtTransStore = 0;
+constexpr int kNtAct = 1;
 
 // ---------------------------------------------------------------------------
 // 1x128 activation tiles: 16 lanes (one DPP row) own one group, 8 elements per
 // lane; a wave covers 4 consecutive groups per step and U steps, so each lane
-// keeps U 16-byte loads in flight.
-constexpr int kActU = 4;
+// keeps U 16-byte loads in flight.  Two steps per wave measured fastest for
+// 25-360 MB tensors: more waves, each short, keep the read and write streams
+// overlapped better than fewer, longer ones.
+//
+// FLAT: the tensor is dense (cols a multiple of 128, ld_x = ld_q = cols,
+// ld_s = cols/128), so group g starts at element 128 g of x and q and its
+// scale is s[g]; no row/column split is needed.
+constexpr int kActU = 2;
 
-template <class In>
+template <class In, bool FLAT>
 __global__ __launch_bounds__(256) void k_quant_act(const typename In::elem* __restrict__ x, int64_t ld_x,
                                                    uint8_t* __restrict__ q, int64_t ld_q,
                                                    float* __restrict__ s, int64_t ld_s,
@@ -46,14 +55,17 @@ __global__ __launch_bounds__(256) void k_quant_act(const typename In::elem* __re
     gcol[u] = 0;
 #pragma unroll
     for (int e = 0; e < 8; ++e) v[u][e] = 0.f;
-    if (g < total) {
+    if (FLAT && g < total) {
+      grow[u] = g;
+      In::template load8<kNtAct>(x + (int64_t)g * 128 + lig * 8, v[u]);
+    } else if (g < total) {
       const int r = g / ngr, j = g - r * ngr;
       const int c0 = j * 128 + lig * 8;
       grow[u] = r;
       gcol[u] = c0;
       const typename In::elem* p = x + (int64_t)r * ld_x + c0;
       if (c0 + 8 <= cols) {
-        In::template load8<0>(p, v[u]);
+        In::template load8<kNtAct>(p, v[u]);
       } else {
 #pragma unroll
         for (int e = 0; e < 8; ++e)
@@ -73,10 +85,15 @@ __global__ __launch_bounds__(256) void k_quant_act(const typename In::elem* __re
     group_scale(__uint_as_float(m), sc, inv);
     const uint32_t w0 = pack4_e4m3(v[u][0] * inv, v[u][1] * inv, v[u][2] * inv, v[u][3] * inv);
     const uint32_t w1 = pack4_e4m3(v[u][4] * inv, v[u][5] * inv, v[u][6] * inv, v[u][7] * inv);
+    if (FLAT) {
+      st_stream8<kNtAct>(q + (int64_t)r * 128 + lig * 8, w0, w1);
+      if (lig == 0) s[r] = sc;
+      continue;
+    }
     const int c0 = gcol[u];
     uint8_t* qp = q + (int64_t)r * ld_q + c0;
     if (c0 + 8 <= cols) {
-      *reinterpret_cast<uint2*>(qp) = make_uint2(w0, w1);
+      st_stream8<kNtAct>(qp, w0, w1);
     } else {
 #pragma unroll
       for (int e = 0; e < 8; ++e)
@@ -92,12 +109,25 @@ hipError_t launch_quant_act(const void* x, bool x_bf16, int64_t rows, int64_t co
   const int64_t total = rows * ngr;
   const int64_t waves = (total + 4 * kActU - 1) / (4 * kActU);
   const int64_t blocks = (waves + 3) / 4;
-  if (x_bf16)
-    hipLaunchKernelGGL(k_quant_act<BF16In>, dim3((uint32_t)blocks), dim3(256), 0, st,
-                       (const uint16_t*)x, ld_x, q, ld_q, s, ld_s, (int)cols, (int)ngr, (int)total);
-  else
-    hipLaunchKernelGGL(k_quant_act<F32In>, dim3((uint32_t)blocks), dim3(256), 0, st,
-                       (const float*)x, ld_x, q, ld_q, s, ld_s, (int)cols, (int)ngr, (int)total);
+  const bool flat = cols % 128 == 0 && ld_x == cols && ld_q == cols && ld_s == ngr;
+  const dim3 grid((uint32_t)blocks), block(256);
+  if (x_bf16) {
+    const uint16_t* xb = (const uint16_t*)x;
+    if (flat)
+      hipLaunchKernelGGL((k_quant_act<BF16In, true>), grid, block, 0, st, xb, ld_x, q, ld_q, s, ld_s, (int)cols,
+                         (int)ngr, (int)total);
+    else
+      hipLaunchKernelGGL((k_quant_act<BF16In, false>), grid, block, 0, st, xb, ld_x, q, ld_q, s, ld_s, (int)cols,
+                         (int)ngr, (int)total);
+  } else {
+    const float* xf = (const float*)x;
+    if (flat)
+      hipLaunchKernelGGL((k_quant_act<F32In, true>), grid, block, 0, st, xf, ld_x, q, ld_q, s, ld_s, (int)cols,
+                         (int)ngr, (int)total);
+    else
+      hipLaunchKernelGGL((k_quant_act<F32In, false>), grid, block, 0, st, xf, ld_x, q, ld_q, s, ld_s, (int)cols,
+                         (int)ngr, (int)total);
+  }
   return hipGetLastError();
 }
 
@@ -224,7 +254,10 @@ hipError_t launch_quant_weight(const void* w, bool w_bf16, int64_t rows, int64_t
 // D (dual output): the same tile also yields the 1x128 row quantization -- a
 // tile's 128 channels of one token are exactly one 1x128 group -- so X is
 // read once for both the row codes q [rows, cols] and the transposed ones.
-template <class In, bool G, bool D>
+//
+// F (full tiles, not grouped): rows and cols are multiples of 128, so every
+// tile is whole and the per-row and per-column bounds checks drop out.
+template <class In, bool G, bool D, bool F>
 __global__ __launch_bounds__(256) void k_quant_transpose(const typename In::elem* __restrict__ x, int64_t ld_x,
                                                          int rows, int cols,
                                                          uint8_t* __restrict__ qt, int64_t ld_qt,
@@ -262,10 +295,10 @@ __global__ __launch_bounds__(256) void k_quant_transpose(const typename In::elem
     const int r = r0 + i;
 #pragma unroll
     for (int e = 0; e < 8; ++e) v[i][e] = 0.f;
-    if (r < rhi) {
+    if (F || r < rhi) {
       const typename In::elem* p = x + (int64_t)r * ld_x + c0;
-      if (c0 + 8 <= cols) {
-        In::template load8<0>(p, v[i]);
+      if (F || c0 + 8 <= cols) {
+        In::template load8<kNtTransLoad>(p, v[i]);
       } else {
 #pragma unroll
         for (int e = 0; e < 8; ++e)
@@ -282,13 +315,13 @@ __global__ __launch_bounds__(256) void k_quant_transpose(const typename In::elem
       for (int e = 0; e < 8; ++e) a = max(a, abs_bits(v[i][e]));
       a = row16_max_u32(a);
       const int r = r0 + i;
-      if (r >= rows) continue;
+      if (!F && r >= rows) continue;
       float sc, iv;
       group_scale(__uint_as_float(a), sc, iv);
       const uint32_t w0 = pack4_e4m3(v[i][0] * iv, v[i][1] * iv, v[i][2] * iv, v[i][3] * iv);
       const uint32_t w1 = pack4_e4m3(v[i][4] * iv, v[i][5] * iv, v[i][6] * iv, v[i][7] * iv);
       uint8_t* qp = q + (int64_t)r * ld_q + c0;
-      if (c0 + 8 <= cols) {
+      if (F || c0 + 8 <= cols) {
         *reinterpret_cast<uint2*>(qp) = make_uint2(w0, w1);
       } else {
 #pragma unroll
@@ -321,15 +354,15 @@ __global__ __launch_bounds__(256) void k_quant_transpose(const typename In::elem
     const uint32_t a = max(max(red[0][cl], red[1][cl]), max(red[2][cl], red[3][cl]));
     float sc;
     group_scale(__uint_as_float(a), sc, inv[e]);
-    if (rblk == 0 && c0 + e < cols) st[(int64_t)(c0 + e) * ld_st + bi] = sc;
+    if (rblk == 0 && (F || c0 + e < cols)) st[(int64_t)(c0 + e) * ld_st + bi] = sc;
   }
   // grouped: rows past the expert's end are padding, stored as code 0 (their
   // values were loaded as 0)
-  const bool full_r = G || r0 + 8 <= rows;
+  const bool full_r = F || G || r0 + 8 <= rows;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     const int c = c0 + e;
-    if (c >= cols) break;
+    if (!F && c >= cols) break;
     const uint32_t d0 = pack4_e4m3(v[0][e] * inv[e], v[1][e] * inv[e], v[2][e] * inv[e], v[3][e] * inv[e]);
     const uint32_t d1 = pack4_e4m3(v[4][e] * inv[e], v[5][e] * inv[e], v[6][e] * inv[e], v[7][e] * inv[e]);
     uint8_t* tp = qt + (int64_t)c * ld_qt + oc0;
@@ -343,28 +376,36 @@ __global__ __launch_bounds__(256) void k_quant_transpose(const typename In::elem
   }
 }
 
+template <class In, bool D>
+static void launch_transpose_tiles(const void* x, int64_t rows, int64_t cols, int64_t ld_x, uint8_t* q_t,
+                                   int64_t ld_qt, float* s_t, int64_t ld_st, uint8_t* q, int64_t ld_q, float* s,
+                                   int64_t ld_s, hipStream_t st) {
+  typedef typename In::elem T;
+  const dim3 grid((uint32_t)((cols + 127) / 128), (uint32_t)((rows + 127) / 128));
+  if (rows % 128 == 0 && cols % 128 == 0)
+    hipLaunchKernelGGL((k_quant_transpose<In, false, D, true>), grid, dim3(256), 0, st, (const T*)x, ld_x, (int)rows,
+                       (int)cols, q_t, ld_qt, s_t, ld_st, nullptr, 0, q, ld_q, s, ld_s);
+  else
+    hipLaunchKernelGGL((k_quant_transpose<In, false, D, false>), grid, dim3(256), 0, st, (const T*)x, ld_x,
+                       (int)rows, (int)cols, q_t, ld_qt, s_t, ld_st, nullptr, 0, q, ld_q, s, ld_s);
+}
+
 hipError_t launch_quant_transpose(const void* x, bool x_bf16, int64_t rows, int64_t cols, int64_t ld_x,
                                   uint8_t* q_t, int64_t ld_qt, float* s_t, int64_t ld_st, hipStream_t st) {
-  const dim3 grid((uint32_t)((cols + 127) / 128), (uint32_t)((rows + 127) / 128));
   if (x_bf16)
-    hipLaunchKernelGGL((k_quant_transpose<BF16In, false, false>), grid, dim3(256), 0, st, (const uint16_t*)x, ld_x,
-                       (int)rows, (int)cols, q_t, ld_qt, s_t, ld_st, nullptr, 0, nullptr, 0, nullptr, 0);
+    launch_transpose_tiles<BF16In, false>(x, rows, cols, ld_x, q_t, ld_qt, s_t, ld_st, nullptr, 0, nullptr, 0, st);
   else
-    hipLaunchKernelGGL((k_quant_transpose<F32In, false, false>), grid, dim3(256), 0, st, (const float*)x, ld_x,
-                       (int)rows, (int)cols, q_t, ld_qt, s_t, ld_st, nullptr, 0, nullptr, 0, nullptr, 0);
+    launch_transpose_tiles<F32In, false>(x, rows, cols, ld_x, q_t, ld_qt, s_t, ld_st, nullptr, 0, nullptr, 0, st);
   return hipGetLastError();
 }
 
 hipError_t launch_quant_act_transpose(const void* x, bool x_bf16, int64_t rows, int64_t cols, int64_t ld_x,
                                       uint8_t* q, int64_t ld_q, float* s, int64_t ld_s, uint8_t* q_t,
                                       int64_t ld_qt, float* s_t, int64_t ld_st, hipStream_t st) {
-  const dim3 grid((uint32_t)((cols + 127) / 128), (uint32_t)((rows + 127) / 128));
   if (x_bf16)
-    hipLaunchKernelGGL((k_quant_transpose<BF16In, false, true>), grid, dim3(256), 0, st, (const uint16_t*)x, ld_x,
-                       (int)rows, (int)cols, q_t, ld_qt, s_t, ld_st, nullptr, 0, q, ld_q, s, ld_s);
+    launch_transpose_tiles<BF16In, true>(x, rows, cols, ld_x, q_t, ld_qt, s_t, ld_st, q, ld_q, s, ld_s, st);
   else
-    hipLaunchKernelGGL((k_quant_transpose<F32In, false, true>), grid, dim3(256), 0, st, (const float*)x, ld_x,
-                       (int)rows, (int)cols, q_t, ld_qt, s_t, ld_st, nullptr, 0, q, ld_q, s, ld_s);
+    launch_transpose_tiles<F32In, true>(x, rows, cols, ld_x, q_t, ld_qt, s_t, ld_st, q, ld_q, s, ld_s, st);
   return hipGetLastError();
 }
 
@@ -374,10 +415,10 @@ hipError_t launch_quant_transpose_grouped(const void* x, bool x_bf16, int64_t ro
   // one block per padded 128-token chunk of the capacity 128*(rows/128 + E)
   const dim3 grid((uint32_t)((cols + 127) / 128), (uint32_t)(rows / 128 + E));
   if (x_bf16)
-    hipLaunchKernelGGL((k_quant_transpose<BF16In, true, false>), grid, dim3(256), 0, st, (const uint16_t*)x, ld_x,
+    hipLaunchKernelGGL((k_quant_transpose<BF16In, true, false, false>), grid, dim3(256), 0, st, (const uint16_t*)x, ld_x,
                        (int)rows, (int)cols, q_t, ld_qt, s_t, ld_st, offsets, (int)E, nullptr, 0, nullptr, 0);
   else
-    hipLaunchKernelGGL((k_quant_transpose<F32In, true, false>), grid, dim3(256), 0, st, (const float*)x, ld_x,
+    hipLaunchKernelGGL((k_quant_transpose<F32In, true, false, false>), grid, dim3(256), 0, st, (const float*)x, ld_x,
                        (int)rows, (int)cols, q_t, ld_qt, s_t, ld_st, offsets, (int)E, nullptr, 0, nullptr, 0);
   return hipGetLastError();
 }

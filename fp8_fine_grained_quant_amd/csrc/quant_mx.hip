@@ -49,8 +49,10 @@ __device__ __forceinline__ uint32_t mx_scale(uint32_t amax_bits, float& inv) {
 // ---------------------------------------------------------------------------
 // 1x32 blocks along rows: 16 lanes (one DPP row) cover 128 consecutive columns
 // of one row, 8 elements per lane, so each DPP quad is one 32-block; a wave
-// covers 4 such 128-column spans per step and U steps.
-constexpr int kMxU = 4;
+// covers 4 such 128-column spans per step and U steps.  Inputs are read
+// non-temporally (each byte once; measured faster for tensors that are not
+// cache-resident).
+constexpr int kMxU = 2;
 
 template <class In>
 __global__ __launch_bounds__(256) void k_quant_mx(const typename In::elem* __restrict__ x, int64_t ld_x,
@@ -76,7 +78,7 @@ __global__ __launch_bounds__(256) void k_quant_mx(const typename In::elem* __res
       gcol[u] = c0;
       const typename In::elem* p = x + (int64_t)r * ld_x + c0;
       if (c0 + 8 <= cols) {
-        In::template load8<0>(p, v[u]);
+        In::template load8<1>(p, v[u]);
       } else {
 #pragma unroll
         for (int e = 0; e < 8; ++e)
@@ -156,7 +158,7 @@ __global__ __launch_bounds__(256) void k_quant_mx_t(const typename In::elem* __r
     if (r < rows) {
       const typename In::elem* p = x + (int64_t)r * ld_x + c0;
       if (c0 + 8 <= cols) {
-        In::template load8<0>(p, v[i]);
+        In::template load8<1>(p, v[i]);
       } else {
 #pragma unroll
         for (int e = 0; e < 8; ++e)

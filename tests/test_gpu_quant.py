@@ -83,6 +83,29 @@ def test_act_edge_shapes_with_guards(shape, dtype):
     assert torch.all(sbuf[:rows, (cols + 127) // 128:] == -7.0) and torch.all(sbuf[rows] == -7.0)
 
 
+@pytest.mark.parametrize("shape", [(1, 128), (3, 384), (257, 1024), (129, 2048), (7, 7168)])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_act_dense_shapes_with_guards(shape, dtype):
+    """Dense tensors (row stride = cols, a multiple of 128) take the flat
+    indexing path; group counts that do not fill the last wave check its tail."""
+    rows, cols = shape
+    a = synth.general(rows, cols, seed=rows * 7 + cols, kind="t3", outlier_frac=0.01, outlier_mul=300.0)
+    x_cpu = torch.from_numpy(a.astype(np.float32)).to(dtype)
+    xbuf = torch.full((rows + 1, cols), 5.0, dtype=dtype, device=DEV)
+    xbuf[:rows] = gpu(x_cpu)
+    x = xbuf[:rows]
+    g = cols // 128
+    qbuf = torch.full((rows + 1, cols), 0xA5, dtype=torch.uint8, device=DEV)
+    sbuf = torch.full((rows + 1, g), -7.0, dtype=torch.float32, device=DEV)
+    q, s = qbuf[:rows], sbuf[:rows]
+    fq.fp8q_quant_act_1x128(x, q, s)
+    torch.cuda.synchronize()
+    qo, so = oracle.quant_act_1x128(f32(x_cpu))
+    assert_bytes_equal(np_u8(q), qo, f"{shape} codes")
+    assert_scales_equal(s.cpu().numpy(), so, f"{shape} scales")
+    assert torch.all(qbuf[rows] == 0xA5) and torch.all(sbuf[rows] == -7.0)
+
+
 def test_act_special_groups():
     x = np.zeros((8, 512), np.float32)
     x[1, :] = -0.0                                       # signed zeros
