@@ -257,6 +257,13 @@ hipError_t launch_quant_weight(const void* w, bool w_bf16, int64_t rows, int64_t
 //
 // F (full tiles, not grouped): rows and cols are multiples of 128, so every
 // tile is whole and the per-row and per-column bounds checks drop out.
+//
+// The transposed codes of a tile that spans 128 whole tokens are staged in
+// LDS (one 128-byte row per channel), so that every global store writes 16
+// bytes and 8 lanes together one whole 128-byte q_t row segment: written
+// straight from registers, each segment would arrive as four 32-byte pieces
+// from four waves (measured 26.5 -> 22 us for X [4096,7168], 95 -> 80 us for
+// [16384,7168]).
 template <class In, bool G, bool D, bool F>
 __global__ __launch_bounds__(256) void k_quant_transpose(const typename In::elem* __restrict__ x, int64_t ld_x,
                                                          int rows, int cols,
@@ -266,6 +273,7 @@ __global__ __launch_bounds__(256) void k_quant_transpose(const typename In::elem
                                                          uint8_t* __restrict__ q, int64_t ld_q,
                                                          float* __restrict__ s, int64_t ld_s) {
   __shared__ uint32_t red[4][128];
+  __shared__ __attribute__((aligned(16))) uint8_t tq[128 * 128];  // [channel][token] codes of the tile
   const int t = threadIdx.x;
   const int c8 = t & 15, rblk = t >> 4;
   const int bi = blockIdx.y, bj = blockIdx.x;
@@ -358,7 +366,32 @@ __global__ __launch_bounds__(256) void k_quant_transpose(const typename In::elem
   }
   // grouped: rows past the expert's end are padding, stored as code 0 (their
   // values were loaded as 0)
-  const bool full_r = F || G || r0 + 8 <= rows;
+  if (F || G || rlo + 128 <= rows) {
+    // LDS: channel cl's 128 token codes at tq[128 cl]; its 8-byte token chunk
+    // k at slot k ^ (2 (c8 & 7)), which spreads one wave's writes over the
+    // banks and keeps chunk pairs (2k, 2k+1) adjacent and in order
+    const int swz = 2 * (c8 & 7);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t d0 = pack4_e4m3(v[0][e] * inv[e], v[1][e] * inv[e], v[2][e] * inv[e], v[3][e] * inv[e]);
+      const uint32_t d1 = pack4_e4m3(v[4][e] * inv[e], v[5][e] * inv[e], v[6][e] * inv[e], v[7][e] * inv[e]);
+      *reinterpret_cast<uint2*>(tq + (c8 * 8 + e) * 128 + (rblk ^ swz) * 8) = make_uint2(d0, d1);
+    }
+    __syncthreads();
+    // lane t writes bytes [16 k, 16 k + 16) of channel 32 pass + t/8, k = t%8
+    const int k16 = t & 7;
+#pragma unroll
+    for (int pass = 0; pass < 4; ++pass) {
+      const int cl = pass * 32 + (t >> 3);
+      const int c = bj * 128 + cl;
+      if (!F && c >= cols) break;  // channels ascend with the pass
+      const u32x4 w = *reinterpret_cast<const u32x4*>(tq + cl * 128 + (k16 ^ ((cl >> 3) & 7)) * 16);
+      st_stream16<kNtTransStore>(qt + (int64_t)c * ld_qt + bi * 128 + k16 * 16, w[0], w[1], w[2], w[3]);
+    }
+    return;
+  }
+  // a partial last token tile: each channel's 8 codes straight from registers
+  const bool full_r = r0 + 8 <= rows;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     const int c = c0 + e;
