@@ -157,6 +157,7 @@ __global__ __launch_bounds__(256) void k_quant_weight(const typename In::elem* _
                                                       uint8_t* __restrict__ qt, int64_t ld_qt,
                                                       float* __restrict__ s, int64_t ld_s) {
   __shared__ uint32_t red[4];
+  __shared__ __attribute__((aligned(16))) uint8_t tq[128 * 128];  // [column][row] codes of the block
   const int t = threadIdx.x;
   const int c4 = t & 31, rb = t >> 5;
   const int bi = blockIdx.y, bj = blockIdx.x;
@@ -209,7 +210,32 @@ __global__ __launch_bounds__(256) void k_quant_weight(const typename In::elem* _
     }
   }
   if (qt == nullptr) return;
-  // transposed codes: 16 consecutive rows of one column -> 16 bytes of q_t
+  // transposed codes: 16 consecutive rows of one column -> 16 bytes of q_t.
+  // A block of 128 whole rows stages them in LDS (column cl's 128 row codes
+  // at tq[128 cl], 16-byte row chunk k at slot k ^ ((cl / 4) % 8)), so that 8
+  // lanes write each 128-byte q_t row segment together instead of four waves
+  // writing 32 bytes of it each.
+  if (bi * 128 + 128 <= rows) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      uint32_t d[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        d[k] = pack4_e4m3(v[4 * k][e] * inv, v[4 * k + 1][e] * inv, v[4 * k + 2][e] * inv, v[4 * k + 3][e] * inv);
+      *reinterpret_cast<u32x4*>(tq + (c4 * 4 + e) * 128 + (rb ^ (c4 & 7)) * 16) = u32x4{d[0], d[1], d[2], d[3]};
+    }
+    __syncthreads();
+    const int k16 = t & 7;
+#pragma unroll
+    for (int pass = 0; pass < 4; ++pass) {
+      const int cl = pass * 32 + (t >> 3);
+      const int c = bj * 128 + cl;
+      if (c >= cols) break;  // columns ascend with the pass
+      const u32x4 w4 = *reinterpret_cast<const u32x4*>(tq + cl * 128 + (k16 ^ ((cl >> 2) & 7)) * 16);
+      st_stream16<kNtWeightTStore>(qt + (int64_t)c * ld_qt + bi * 128 + k16 * 16, w4[0], w4[1], w4[2], w4[3]);
+    }
+    return;
+  }
   const bool full_r = r0 + 16 <= rows;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {

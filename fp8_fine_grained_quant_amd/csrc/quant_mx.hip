@@ -131,8 +131,8 @@ hipError_t launch_quant_mx(const void* x, bool x_bf16, int64_t rows, int64_t col
 // of 8 consecutive columns (8*(t%16) ..), so wave w holds rows
 // [32w, 32w + 32) of the tile: a column's 32-block is reduced over the four
 // lanes l%16 + 16k of one wave (xor 16, xor 32), without LDS.  Each column's
-// 8 codes are converted pairwise down the column and leave as one 8-byte
-// segment of the q_t row.
+// 8 codes are converted pairwise down the column into an LDS copy of the
+// tile's transposed codes, which leaves as whole 128-byte q_t row segments.
 //
 // D (dual output): the tile's rows also yield the 1x32 row blocks (a DPP
 // quad of lanes spans 32 consecutive columns of one row), so x is read once
@@ -144,6 +144,7 @@ __global__ __launch_bounds__(256) void k_quant_mx_t(const typename In::elem* __r
                                                     uint8_t* __restrict__ st, int64_t ld_st,
                                                     uint8_t* __restrict__ q, int64_t ld_q,
                                                     uint8_t* __restrict__ s, int64_t ld_s) {
+  __shared__ __attribute__((aligned(16))) uint8_t tq[128 * 128];  // [channel][token] codes of the tile
   const int t = threadIdx.x, wv = t >> 6;
   const int c8 = t & 15, rblk = t >> 4;
   const int bi = blockIdx.y, bj = blockIdx.x;
@@ -207,6 +208,12 @@ __global__ __launch_bounds__(256) void k_quant_mx_t(const typename In::elem* __r
   const bool block_present = bi * 128 + wv * 32 < rows;  // this wave's 32-row block has rows
   const bool full_r = r0 + 8 <= rows;
   const int oc0 = bi * 128 + rblk * 8;  // output token column of this thread's rows
+  // A tile of 128 whole tokens stages its transposed codes in LDS (channel
+  // cl's 128 token codes at tq[128 cl], 8-byte token chunk k at slot
+  // k ^ (2 (c8 & 7))) so that 8 lanes write each 128-byte q_t row segment
+  // together; a partial last token tile stores from registers.
+  const bool staged = bi * 128 + 128 <= rows;
+  const int swz = 2 * (c8 & 7);
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     const int c = c0 + e;
@@ -216,6 +223,10 @@ __global__ __launch_bounds__(256) void k_quant_mx_t(const typename In::elem* __r
     if ((t & 63) < 16 && block_present) st[(int64_t)c * ld_st + bi * 4 + wv] = (uint8_t)byte;
     const uint32_t d0 = pack4_e4m3(v[0][e] * iv, v[1][e] * iv, v[2][e] * iv, v[3][e] * iv);
     const uint32_t d1 = pack4_e4m3(v[4][e] * iv, v[5][e] * iv, v[6][e] * iv, v[7][e] * iv);
+    if (staged) {
+      *reinterpret_cast<uint2*>(tq + (c8 * 8 + e) * 128 + (rblk ^ swz) * 8) = make_uint2(d0, d1);
+      continue;
+    }
     uint8_t* tp = qt + (int64_t)c * ld_qt + oc0;
     if (full_r) {
       *reinterpret_cast<uint2*>(tp) = make_uint2(d0, d1);
@@ -224,6 +235,18 @@ __global__ __launch_bounds__(256) void k_quant_mx_t(const typename In::elem* __r
       for (int i = 0; i < 8; ++i)
         if (r0 + i < rows) tp[i] = (uint8_t)((((i < 4) ? d0 : d1) >> (8 * (i & 3))) & 0xFF);
     }
+  }
+  if (!staged) return;
+  __syncthreads();
+  // lane t writes bytes [16 k, 16 k + 16) of channel 32 pass + t/8, k = t%8
+  const int k16 = t & 7;
+#pragma unroll
+  for (int pass = 0; pass < 4; ++pass) {
+    const int cl = pass * 32 + (t >> 3);
+    const int c = bj * 128 + cl;
+    if (c >= cols) break;  // channels ascend with the pass
+    const u32x4 w = *reinterpret_cast<const u32x4*>(tq + cl * 128 + (k16 ^ ((cl >> 3) & 7)) * 16);
+    *reinterpret_cast<u32x4*>(qt + (int64_t)c * ld_qt + bi * 128 + k16 * 16) = w;
   }
 }
 
