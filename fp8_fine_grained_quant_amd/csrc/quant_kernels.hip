@@ -17,14 +17,17 @@
 
 namespace fp8q {
 
-// Non-temporal choices per access (see ld_stream16): the weight loads and
-// row codes (long streams of full segments) and the activation quantizer's
-// loads and codes are non-temporal; the transposers read non-temporally but
-// keep their transposed codes (short scattered segments) cached so that
-// neighbouring segments merge in L2.  Measured on MI355X with inputs that are
-// not cache-resident, as in a training step.
-constexpr int kNtWeightLoad = 1, kNtWeightStore = 1, kNtWeightTStore = 0, kNtTransLoad = 1, kNtTransStore = 0;
-constexpr int kNtAct = 1;
+// Non-temporal choices per access (see ld_stream16).  Inputs are read once,
+// non-temporally.  Row codes of up to kNtCodeBytes are written cached: the
+// GEMM that consumes them runs next and finds them in the 256 MB MALL
+// (written non-temporally, X's 29 MB of codes cost Fprop 5-6 us of its 62).
+// Larger code arrays (the MoE layer's activations and stacked experts) are
+// written non-temporally, which measured faster for them and for the grouped
+// GEMM after them.  Measured on MI355X with inputs that are not
+// cache-resident, as in a training step.
+constexpr int kNtWeightLoad = 1, kNtWeightTStore = 0, kNtTransLoad = 1, kNtTransStore = 0;
+constexpr int kNtActLoad = 1;
+constexpr int64_t kNtCodeBytes = 64ll << 20;
 
 // ---------------------------------------------------------------------------
 // 1x128 activation tiles: 16 lanes (one DPP row) own one group, 8 elements per
@@ -38,7 +41,7 @@ constexpr int kNtAct = 1;
 // scale is s[g]; no row/column split is needed.
 constexpr int kActU = 2;
 
-template <class In, bool FLAT>
+template <class In, bool FLAT, int NTS>
 __global__ __launch_bounds__(256) void k_quant_act(const typename In::elem* __restrict__ x, int64_t ld_x,
                                                    uint8_t* __restrict__ q, int64_t ld_q,
                                                    float* __restrict__ s, int64_t ld_s,
@@ -57,7 +60,7 @@ __global__ __launch_bounds__(256) void k_quant_act(const typename In::elem* __re
     for (int e = 0; e < 8; ++e) v[u][e] = 0.f;
     if (FLAT && g < total) {
       grow[u] = g;
-      In::template load8<kNtAct>(x + (int64_t)g * 128 + lig * 8, v[u]);
+      In::template load8<kNtActLoad>(x + (int64_t)g * 128 + lig * 8, v[u]);
     } else if (g < total) {
       const int r = g / ngr, j = g - r * ngr;
       const int c0 = j * 128 + lig * 8;
@@ -65,7 +68,7 @@ __global__ __launch_bounds__(256) void k_quant_act(const typename In::elem* __re
       gcol[u] = c0;
       const typename In::elem* p = x + (int64_t)r * ld_x + c0;
       if (c0 + 8 <= cols) {
-        In::template load8<kNtAct>(p, v[u]);
+        In::template load8<kNtActLoad>(p, v[u]);
       } else {
 #pragma unroll
         for (int e = 0; e < 8; ++e)
@@ -86,14 +89,14 @@ __global__ __launch_bounds__(256) void k_quant_act(const typename In::elem* __re
     const uint32_t w0 = pack4_e4m3(v[u][0] * inv, v[u][1] * inv, v[u][2] * inv, v[u][3] * inv);
     const uint32_t w1 = pack4_e4m3(v[u][4] * inv, v[u][5] * inv, v[u][6] * inv, v[u][7] * inv);
     if (FLAT) {
-      st_stream8<kNtAct>(q + (int64_t)r * 128 + lig * 8, w0, w1);
+      st_stream8<NTS>(q + (int64_t)r * 128 + lig * 8, w0, w1);
       if (lig == 0) s[r] = sc;
       continue;
     }
     const int c0 = gcol[u];
     uint8_t* qp = q + (int64_t)r * ld_q + c0;
     if (c0 + 8 <= cols) {
-      st_stream8<kNtAct>(qp, w0, w1);
+      st_stream8<NTS>(qp, w0, w1);
     } else {
 #pragma unroll
       for (int e = 0; e < 8; ++e)
@@ -110,24 +113,19 @@ hipError_t launch_quant_act(const void* x, bool x_bf16, int64_t rows, int64_t co
   const int64_t waves = (total + 4 * kActU - 1) / (4 * kActU);
   const int64_t blocks = (waves + 3) / 4;
   const bool flat = cols % 128 == 0 && ld_x == cols && ld_q == cols && ld_s == ngr;
+  const bool nt = rows * cols > kNtCodeBytes;
   const dim3 grid((uint32_t)blocks), block(256);
+  const int c = (int)cols, ng = (int)ngr, tot = (int)total;
+#define FP8Q_ACT(T, F, N) \
+  hipLaunchKernelGGL((k_quant_act<T, F, N>), grid, block, 0, st, (const T::elem*)x, ld_x, q, ld_q, s, ld_s, c, ng, tot)
   if (x_bf16) {
-    const uint16_t* xb = (const uint16_t*)x;
-    if (flat)
-      hipLaunchKernelGGL((k_quant_act<BF16In, true>), grid, block, 0, st, xb, ld_x, q, ld_q, s, ld_s, (int)cols,
-                         (int)ngr, (int)total);
-    else
-      hipLaunchKernelGGL((k_quant_act<BF16In, false>), grid, block, 0, st, xb, ld_x, q, ld_q, s, ld_s, (int)cols,
-                         (int)ngr, (int)total);
+    if (flat) { if (nt) FP8Q_ACT(BF16In, true, 1); else FP8Q_ACT(BF16In, true, 0); }
+    else { if (nt) FP8Q_ACT(BF16In, false, 1); else FP8Q_ACT(BF16In, false, 0); }
   } else {
-    const float* xf = (const float*)x;
-    if (flat)
-      hipLaunchKernelGGL((k_quant_act<F32In, true>), grid, block, 0, st, xf, ld_x, q, ld_q, s, ld_s, (int)cols,
-                         (int)ngr, (int)total);
-    else
-      hipLaunchKernelGGL((k_quant_act<F32In, false>), grid, block, 0, st, xf, ld_x, q, ld_q, s, ld_s, (int)cols,
-                         (int)ngr, (int)total);
+    if (flat) { if (nt) FP8Q_ACT(F32In, true, 1); else FP8Q_ACT(F32In, true, 0); }
+    else { if (nt) FP8Q_ACT(F32In, false, 1); else FP8Q_ACT(F32In, false, 0); }
   }
+#undef FP8Q_ACT
   return hipGetLastError();
 }
 
@@ -150,7 +148,7 @@ __device__ __forceinline__ void load4<BF16In>(const uint16_t* p, float v[4]) {
   v[2] = bf16_to_f32(u.y & 0xFFFFu); v[3] = bf16_to_f32(u.y >> 16);
 }
 
-template <class In>
+template <class In, int NTS>
 __global__ __launch_bounds__(256) void k_quant_weight(const typename In::elem* __restrict__ w, int64_t ld_w,
                                                       int rows, int cols,
                                                       uint8_t* __restrict__ q, int64_t ld_q,
@@ -202,7 +200,7 @@ __global__ __launch_bounds__(256) void k_quant_weight(const typename In::elem* _
     const uint32_t wd = pack4_e4m3(v[i][0] * inv, v[i][1] * inv, v[i][2] * inv, v[i][3] * inv);
     uint8_t* qp = q + (int64_t)r * ld_q + c0;
     if (full_c) {
-      st_stream4<kNtWeightStore>(qp, wd);
+      st_stream4<NTS>(qp, wd);
     } else {
 #pragma unroll
       for (int e = 0; e < 4; ++e)
@@ -260,12 +258,24 @@ hipError_t launch_quant_weight(const void* w, bool w_bf16, int64_t rows, int64_t
                                uint8_t* q, int64_t ld_q, uint8_t* q_t, int64_t ld_qt,
                                float* s, int64_t ld_s, hipStream_t st) {
   const dim3 grid((uint32_t)((cols + 127) / 128), (uint32_t)((rows + 127) / 128));
-  if (w_bf16)
-    hipLaunchKernelGGL(k_quant_weight<BF16In>, grid, dim3(256), 0, st, (const uint16_t*)w, ld_w, (int)rows,
-                       (int)cols, q, ld_q, q_t, ld_qt, s, ld_s);
-  else
-    hipLaunchKernelGGL(k_quant_weight<F32In>, grid, dim3(256), 0, st, (const float*)w, ld_w, (int)rows,
-                       (int)cols, q, ld_q, q_t, ld_qt, s, ld_s);
+  const bool nt = rows * cols > kNtCodeBytes;
+  if (w_bf16) {
+    const uint16_t* wb = (const uint16_t*)w;
+    if (nt)
+      hipLaunchKernelGGL((k_quant_weight<BF16In, 1>), grid, dim3(256), 0, st, wb, ld_w, (int)rows, (int)cols, q,
+                         ld_q, q_t, ld_qt, s, ld_s);
+    else
+      hipLaunchKernelGGL((k_quant_weight<BF16In, 0>), grid, dim3(256), 0, st, wb, ld_w, (int)rows, (int)cols, q,
+                         ld_q, q_t, ld_qt, s, ld_s);
+  } else {
+    const float* wf = (const float*)w;
+    if (nt)
+      hipLaunchKernelGGL((k_quant_weight<F32In, 1>), grid, dim3(256), 0, st, wf, ld_w, (int)rows, (int)cols, q,
+                         ld_q, q_t, ld_qt, s, ld_s);
+    else
+      hipLaunchKernelGGL((k_quant_weight<F32In, 0>), grid, dim3(256), 0, st, wf, ld_w, (int)rows, (int)cols, q,
+                         ld_q, q_t, ld_qt, s, ld_s);
+  }
   return hipGetLastError();
 }
 
