@@ -198,6 +198,25 @@ def test_weight_without_transpose_and_stacked_experts():
         assert_scales_equal(sg[i], so, f"expert {i} scales")
 
 
+def test_weight_stacked_experts_above_64mb_with_transpose():
+    """Code arrays above 64 MB are written non-temporally: 5 stacked experts
+    of [2048, 7168] (73 M codes), with the transposed codes, against the
+    oracle on the first and last expert."""
+    rng = np.random.Generator(np.random.PCG64(78))
+    e, n, k = 5, 2048, 7168
+    w_cpu = torch.from_numpy((rng.standard_normal((e, n, k), dtype=np.float32) * np.float32(0.02)))
+    w = gpu(w_cpu).reshape(e * n, k)
+    q, s, q_t = fq.quant_weight_128x128(w)
+    torch.cuda.synchronize()
+    qg, sg = np_u8(q).reshape(e, n, k), s.cpu().numpy().reshape(e, n // 128, k // 128)
+    for i in (0, e - 1):
+        log(f"stacked expert {i} of {e}")
+        qo, so, qto = oracle.quant_weight_128x128(w_cpu[i].numpy())
+        assert_bytes_equal(qg[i], qo, f"expert {i} codes")
+        assert_scales_equal(sg[i], so, f"expert {i} scales")
+        assert_bytes_equal(np_u8(q_t[:, i * n:(i + 1) * n]), qto, f"expert {i} transposed codes")
+
+
 # ------------------------------------------------------------- quant transpose
 def _check_transpose(x_cpu, what, cols=None):
     x = gpu(x_cpu)
