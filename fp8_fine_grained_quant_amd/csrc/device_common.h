@@ -78,9 +78,10 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 // Streaming accesses: every input byte is read once and every output byte
 // written once.
 // NT = 1 marks the access non-temporal.  Measured on MI355X: it pays for
-// long streams written or read in full 64-byte-plus segments (the stacked
-// expert weights), and loses for tensors that fit the 256 MB MALL or for
-// scattered short stores, so each kernel picks per access.
+// inputs read once and for long output streams written in full segments (the
+// stacked expert weights), and loses for outputs that the next kernel reads
+// (they would have stayed in the 256 MB MALL) and for scattered short stores,
+// so each kernel picks per access.
 template <int NT>
 __device__ __forceinline__ u32x4 ld_stream16(const void* p) {
   if (NT) return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
