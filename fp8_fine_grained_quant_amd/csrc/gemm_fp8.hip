@@ -43,6 +43,9 @@
 // the 16-row slice, bytes [16g, 16g+16) and [64+16g, 64+16g+16) of the chunk,
 // g = l/16.  Result: lane l holds C[4g + r][l%16], r = 0..3.
 
+#include <stdlib.h>
+#include <string.h>
+
 #include "device_common.h"
 #include "gemm_tile.h"
 #include "launch.h"
@@ -411,6 +414,240 @@ __global__ __launch_bounds__(kNT) void k_gemm_fp8(GemmArgs p) {
 #endif  // __HIP_DEVICE_COMPILE__
 }
 
+// ---------------------------------------------------------------------------
+// Wide tile: 256 x 256 outputs per workgroup, eight waves (two per SIMD).
+//
+// Each wave runs exactly the 64 x 128 strip of k_gemm_fp8 above (the same
+// MFMAs, promotion order and epilogue), wave w at rows 64 (w % 4) and columns
+// 128 (w / 4) of the tile, so the output is bit-identical; only the data
+// movement differs:
+//   * a chunk's global -> LDS bytes (A 32 KB + B 32 KB) now feed twice the
+//     MFMAs (a third fewer bytes per FLOP), and two waves per SIMD issue LDS
+//     fragment reads (measured: one wave per SIMD gets ~40 B/ns of them);
+//   * two chunks of A and two of B fit in LDS (4 x 32 KB), each in its own
+//     LDS object.  A chunk's A fragments move to registers at the end of the
+//     previous chunk, so A region c%2 is free from the first barrier of chunk
+//     c on and receives chunk c+2 there (about 1.7 chunk times to land); B
+//     region c%2 is read until the chunk's seventh column and receives chunk
+//     c+2 in the last column (about one chunk time to land).  With A and B in
+//     one 64 KB stage per chunk instead, the loads had under one chunk time
+//     and the kernel ran 25% slower than the 256 x 128 one.
+// Block-scaled B and 16-byte row-scale blocks only (Fprop, Dgrad and their
+// grouped forms); used when the tile count fills the chip (see
+// launch_gemm_fp8).  Measured on MI355X: 16384 x 2048 x 7168 284 -> 206 us,
+// 4096 x 7168 x 2048 81 -> 69 us, the 32-expert grouped Fprop 409 -> 296 us.
+constexpr int kWBN = 256, kWNT = 512;
+constexpr int kWIA = kBM * kBK / (16 * kWNT);  // 16-byte A loads per lane per chunk (4)
+constexpr int kWIB = kWBN * kBK / (16 * kWNT);  // 16-byte B loads per lane per chunk (4)
+constexpr int kWDmaA = kWIA + 1;               // A loads and the row-scale load
+constexpr int kWFirstSlot = kTM, kWDmaSlots = 20;
+static_assert(kWIB == kTM, "one B load per slot of the last column");
+static_assert(kWDmaA <= kWDmaSlots && kWFirstSlot + kWDmaSlots <= kTM * (kTN - 1), "A loads between the barriers");
+static_assert(4 * kBM * kBK + 4 * 2 * kMaxChunks + 4 * 2 * 256 * 4 + 1024 <= 160 * 1024, "LDS of one CU");
+
+template <int OUT_F32, bool GROUPED>
+__global__ __launch_bounds__(kWNT) void k_gemm_fp8_wide(GemmArgs p) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __shared__ __attribute__((aligned(16))) uint8_t sa0[kBM * kBK];
+  __shared__ __attribute__((aligned(16))) uint8_t sa1[kBM * kBK];
+  __shared__ __attribute__((aligned(16))) uint8_t sb0[kWBN * kBK];
+  __shared__ __attribute__((aligned(16))) uint8_t sb1[kWBN * kBK];
+  __shared__ __attribute__((aligned(16))) float sbk_all[2 * kMaxChunks];  // B block scales: [half][chunk]
+  __shared__ __attribute__((aligned(16))) float scA[2 * 256 * 4];         // row scales, 2 blocks of 4 chunks
+  __shared__ __attribute__((aligned(16))) uint8_t dmy[1024];              // target of count-keeping loads
+
+  TileCoord tc;
+  if (!tile_coord<kBM, kWBN, GROUPED>(p, tc)) return;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wr = w & 3, wc = w >> 2;  // the wave's 64-row strip and 128-column half
+  const int l16 = lane & 15, g = lane >> 4;
+  const int nk = (int)(p.K / kBK);
+  const uint8_t* Bp = p.B + (GROUPED ? (int64_t)tc.e * p.b_estride : 0);
+  const float* sbp = p.sb + (GROUPED ? (int64_t)tc.e * p.sb_estride : 0);
+  const int rows = (int)min(tc.mend - tc.m0, (int64_t)kBM);  // valid rows of the tile, >= 1
+
+  // direct-load sources, range-checked as in k_gemm_fp8
+  const __amdgpu_buffer_rsrc_t rA = make_rsrc(p.A + tc.m0 * p.lda, (uint32_t)(rows * p.lda));
+  const __amdgpu_buffer_rsrc_t rB = make_rsrc(Bp + (int64_t)tc.n0 * p.ldb, (uint32_t)(kWBN * p.ldb));
+  const __amdgpu_buffer_rsrc_t rSa = make_rsrc(p.sa + tc.m0 * p.ld_sa, (uint32_t)(rows * p.ld_sa * 4));
+  const int r8 = lane >> 3, lc = (lane & 7) ^ r8;
+  const uint32_t voffA = (uint32_t)((w * kWIA * 8 + r8) * p.lda + 16 * lc);
+  const uint32_t voffB = (uint32_t)((w * kWIB * 8 + r8) * p.ldb + 16 * lc);
+  const uint32_t stepA = (uint32_t)(8 * p.lda), stepB = (uint32_t)(8 * p.ldb);
+  const uint32_t voffSa = (uint32_t)(min(wr * 64 + lane, rows - 1) * p.ld_sa * 4);
+
+  // d-th A-side load of chunk kb into A region `ar` (d == kWIA: waves 0-3 load
+  // the row scales of the 4-chunk block that starts at kb; every other wave
+  // and chunk issues an out-of-range load, so each chunk issues kWDmaA loads)
+  auto issue_a = [&](int kb, uint8_t* ar, int d) {
+    if (d < kWIA) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, (lds_ptr)(ar + (w * kWIA + d) * 1024), 16, voffA + d * stepA,
+                                               (uint32_t)kb * kBK, 0, 0);
+    } else {
+      const bool real = w < 4 && (kb & 3) == 0;
+      uint8_t* dst = real ? reinterpret_cast<uint8_t*>(scA) + ((kb >> 2) & 1) * 4096 + w * 1024 : dmy;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rSa, (lds_ptr)dst, 16, voffSa, real ? (uint32_t)kb * 4 : 0x40000000u,
+                                               0, 0);
+    }
+  };
+  auto issue_b = [&](int kb, uint8_t* br, int q) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, (lds_ptr)(br + (w * kWIB + q) * 1024), 16, voffB + q * stepB,
+                                             (uint32_t)kb * kBK, 0, 0);
+  };
+  constexpr int kWaitA = 0x0F70 | kWDmaA;  // vmcnt(kWDmaA): all but the latest chunk's A-side loads
+
+  const int sw = l16 & 7;
+  const int offLo = l16 * kBK + 16 * (g ^ sw);
+  const int offHi = l16 * kBK + 16 * ((4 + g) ^ sw);
+  auto rdA = [&](const uint8_t* ar, int i) -> v8i {
+    const uint8_t* base = ar + (wr * 64 + 16 * i) * kBK;
+    return make_frag(*reinterpret_cast<const uint4*>(base + offLo), *reinterpret_cast<const uint4*>(base + offHi));
+  };
+  auto rdB = [&](const uint8_t* br, int j) -> v8i {
+    const uint8_t* base = br + (wc * 128 + 16 * j) * kBK;
+    return make_frag(*reinterpret_cast<const uint4*>(base + offLo), *reinterpret_cast<const uint4*>(base + offHi));
+  };
+  const int rowSa = wr * 64 + 16 * (l16 >> 2) + 4 * g + (l16 & 3);
+  auto rdSa = [&](int kb) -> float { return scA[((kb >> 2) & 1) * 1024 + rowSa * 4 + (kb & 3)]; };
+
+  float acc[kTM][kTN][4];
+#pragma unroll
+  for (int i = 0; i < kTM; ++i)
+#pragma unroll
+    for (int j = 0; j < kTN; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[i][j][r] = 0.f;
+
+  v8i a[kTM];        // A fragments of the current chunk
+  v8i bring[2];      // B fragments: this column's and the next one's
+  v4f pp[kTM];       // MFMA partials, ring indexed by slot % 4
+  float sc[kTM][4];  // row scales times the block's B scale
+  float sa_nx = 0.f, sbk_nx = 1.f;
+  auto promote = [&](int i, int j) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc[i][j][r] = __builtin_fmaf(pp[i][r], sc[i][r], acc[i][j][r]);
+  };
+  auto load_sc = [&](int i) {
+    switch (i) {
+      case 0: row_scales<0>(sa_nx, sbk_nx, sc[0]); break;
+      case 1: row_scales<1>(sa_nx, sbk_nx, sc[1]); break;
+      case 2: row_scales<2>(sa_nx, sbk_nx, sc[2]); break;
+      default: row_scales<3>(sa_nx, sbk_nx, sc[3]); break;
+    }
+  };
+  auto mfma = [&](const v8i& x, const v8i& y) -> v4f {
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(x, y, v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
+  };
+  auto fence = [] { asm volatile("" ::: "memory"); };
+
+  // ---- prologue: both halves' block B scales of every chunk to LDS; A(0),
+  // B(0), A(1), B(1) in flight in that order; chunk 0 published
+  {
+    const float* psb = sbp + (int64_t)(tc.n0 / 128) * p.sb_rs;
+    for (int q = tid; q < 2 * nk; q += kWNT) sbk_all[q] = psb[(int64_t)(q / nk) * p.sb_rs + (int64_t)(q % nk) * p.sb_cs];
+  }
+  fence();
+#pragma unroll
+  for (int d = 0; d < kWDmaA; ++d) issue_a(0, sa0, d);
+#pragma unroll
+  for (int q = 0; q < kWIB; ++q) issue_b(0, sb0, q);
+#pragma unroll
+  for (int d = 0; d < kWDmaA; ++d) issue_a(min(1, nk - 1), sa1, d);
+#pragma unroll
+  for (int q = 0; q < kWIB; ++q) issue_b(min(1, nk - 1), sb1, q);
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (kWDmaA + kWIB));  // A(0), B(0) landed
+  __builtin_amdgcn_s_waitcnt(0xC07F);                  // lgkmcnt(0): the block scales are written
+  __builtin_amdgcn_s_barrier();
+  fence();
+#pragma unroll
+  for (int i = 0; i < kTM; ++i) {
+    a[i] = rdA(sa0, i);
+    if (i == 0) sa_nx = rdSa(0);
+    pp[i] = v4f{0.f, 0.f, 0.f, 0.f};
+  }
+  bring[0] = rdB(sb0, 0);
+  sbk_nx = sbk_all[wc * nk];
+#pragma unroll
+  for (int i = 0; i < kTM; ++i) load_sc(i);
+
+  // ---- one chunk (regions u = c % 2 hold chunk c; 1-u hold or receive c+1)
+  auto step = [&](int c, auto U) {
+    constexpr int u = decltype(U)::value;
+    uint8_t* const acur = u == 0 ? sa0 : sa1;
+    uint8_t* const anxt = u == 0 ? sa1 : sa0;
+    uint8_t* const bcur = u == 0 ? sb0 : sb1;
+    uint8_t* const bnxt = u == 0 ? sb1 : sb0;
+    const int c2 = min(c + 2, nk - 1);  // past the end, the last chunk again (same counts)
+#pragma unroll
+    for (int j = 0; j < kTN; ++j) {
+      const v8i bj = bring[j & 1];
+      if (j + 1 < kTN) bring[(j + 1) & 1] = rdB(bcur, j + 1);
+      else bring[0] = rdB(bnxt, 0);
+      fence();
+#pragma unroll
+      for (int i = 0; i < kTM; ++i) {
+        const int t = kTM * j + i;
+        pp[i] = mfma(a[i], bj);
+        if (t >= kSkew) {
+          const int tp = t - kSkew;
+          promote(tp % kTM, tp / kTM);
+        } else {
+          promote(t + 1, kTN - 1);
+          load_sc(t + 1);
+        }
+        if (t >= kWFirstSlot && t < kWFirstSlot + kWDmaSlots) {
+#pragma unroll
+          for (int d = 0; d < kWDmaA; ++d)
+            if (kWFirstSlot + (d * kWDmaSlots) / kWDmaA == t) issue_a(c2, acur, d);
+        }
+        if (j == kTN - 1) {
+          issue_b(c2, bcur, i);
+          a[i] = rdA(anxt, i);
+          if (i == 0) {
+            sa_nx = rdSa(min(c + 1, nk - 1));
+            sbk_nx = sbk_all[wc * nk + min(c + 1, nk - 1)];
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (j == 0) {
+        // every wave holds A(c) in registers: A region u may take A(c+2)
+        __builtin_amdgcn_s_waitcnt(0xC07F);
+        __builtin_amdgcn_s_barrier();
+        fence();
+      }
+      if (j == kTN - 2) {
+        // every wave has read B(c)'s last column (B region u may take B(c+2)),
+        // and A(c+1), B(c+1) have landed
+        __builtin_amdgcn_s_waitcnt(0xC07F);
+        __builtin_amdgcn_s_waitcnt(kWaitA);
+        __builtin_amdgcn_s_barrier();
+        fence();
+      }
+    }
+    load_sc(0);
+  };
+
+  int c = 0;
+  for (; c + 2 <= nk; c += 2) {
+    step(c, IC<0>());
+    step(c + 1, IC<1>());
+  }
+  if (c < nk) step(c, IC<0>());
+#pragma unroll
+  for (int i = 1; i < kTM; ++i) promote(i, kTN - 1);
+
+  // ---- epilogue: two waves' 12 KB staging areas in each 32 KB region
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  fence();
+  uint8_t* const ep = (w >> 1) == 0 ? sa0 : (w >> 1) == 1 ? sa1 : (w >> 1) == 2 ? sb0 : sb1;
+  store_tile<kTM, kTN, OUT_F32, OUT_F32 ? 16 : 32>(acc, ep + (w & 1) * 12288, p, tc.m0 + wr * 64, tc.mend,
+                                                 tc.n0 + wc * 128, lane);
+#endif  // __HIP_DEVICE_COMPILE__
+}
+
 namespace {
 
 template <int SB_MODE, int OUT_F32, bool GROUPED, bool KG = false, bool SC4 = false>
@@ -426,11 +663,44 @@ hipError_t launch_one(const GemmArgs& a, hipStream_t st) {
 
 }  // namespace
 
+// Tile choice for block-scaled products.  A 256 x 256 tile takes about 1.3x
+// the time of a 256 x 128 one (measured) for twice the work, so it wins
+// whenever it makes more than one tile per two compute units: below that the
+// 256 x 128 grid also finishes in one round and keeps every unit busy.
+// Grouped launches estimate the tile count from the total rows.  The
+// environment variable FP8Q_GEMM_TILE = "256x128" or "256x256" overrides the
+// choice (both tiles give bit-identical results), for tests and measurement.
+static bool use_wide_tile(const GemmArgs& a) {
+  if (a.out_f32 && a.offsets != nullptr) return false;  // no FP32-output grouped instantiation
+  if (const char* f = getenv("FP8Q_GEMM_TILE")) {
+    if (!strcmp(f, "256x128")) return false;
+    if (!strcmp(f, "256x256")) return true;
+  }
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    cus = 256;
+  const int64_t tiles = ((a.M + kBM - 1) / kBM) * (a.N / kWBN);
+  return 2 * tiles > cus;
+}
+
 hipError_t launch_gemm_fp8(const GemmArgs& a, hipStream_t st) {
   const bool sc4 = a.ld_sa % 4 == 0 && (reinterpret_cast<uintptr_t>(a.sa) & 15) == 0;
   if (a.sb_mode == kSbRow) {  // weight gradients: FP32 out (row scales 128 B per row: no gain from blocks)
     if (a.k_grouped) return launch_one<kSbRow, 1, true, true>(a, st);
     return launch_one<kSbRow, 1, false>(a, st);
+  }
+  // the 256 x 256 tile when it leaves no more than half of the chip idle
+  if (sc4 && a.N % kWBN == 0 && use_wide_tile(a)) {
+    const int64_t tn = a.N / kWBN, tm = (a.M + kBM - 1) / kBM;
+    const int64_t tiles = a.offsets != nullptr ? (tm + a.E) * tn : tm * tn;  // grouped: upper bound
+    if (a.offsets != nullptr)
+      hipLaunchKernelGGL((k_gemm_fp8_wide<0, true>), dim3((uint32_t)tiles), dim3(kWNT), 0, st, a);
+    else if (a.out_f32)
+      hipLaunchKernelGGL((k_gemm_fp8_wide<1, false>), dim3((uint32_t)tiles), dim3(kWNT), 0, st, a);
+    else
+      hipLaunchKernelGGL((k_gemm_fp8_wide<0, false>), dim3((uint32_t)tiles), dim3(kWNT), 0, st, a);
+    return hipGetLastError();
   }
   // row scales in 16-byte blocks of 4 chunks when every scale row is 16-byte aligned
   if (a.offsets != nullptr) {
