@@ -648,6 +648,230 @@ __global__ __launch_bounds__(kWNT) void k_gemm_fp8_wide(GemmArgs p) {
 #endif  // __HIP_DEVICE_COMPILE__
 }
 
+// Wide tile for the weight gradients (one B scale per output column per
+// chunk, FP32 output, optionally C +=): the same schedule as k_gemm_fp8_wide.
+// Each chunk's 256 row scales ride with its A loads and its 256 column
+// scales with its B loads, 4 bytes per lane, into 2 KB beside each region
+// (waves 4-7 write a spare copy so every wave issues the same loads).  KG:
+// the grouped contraction (per-expert token chunks, per-expert output), as
+// in k_gemm_fp8.
+constexpr int kWRowPad = 2048;
+
+template <bool KG>
+__global__ __launch_bounds__(kWNT) void k_gemm_fp8_wide_row(GemmArgs p) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  constexpr int RA = kBM * kBK, RB = kWBN * kBK;  // scale areas start after the codes
+  __shared__ __attribute__((aligned(16))) uint8_t sa0[RA + kWRowPad];
+  __shared__ __attribute__((aligned(16))) uint8_t sa1[RA + kWRowPad];
+  __shared__ __attribute__((aligned(16))) uint8_t sb0[RB + kWRowPad];
+  __shared__ __attribute__((aligned(16))) uint8_t sb1[RB + kWRowPad];
+
+  TileCoord tc;
+  if (!tile_coord<kBM, kWBN, KG>(p, tc)) return;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wr = w & 3, wc = w >> 2;
+  const int l16 = lane & 15, g = lane >> 4;
+  int nk = (int)(p.K / kBK), cb = 0;
+  if (KG) {
+    const int lo = p.offsets[tc.e], hi = p.offsets[tc.e + 1];
+    nk = (hi - lo + kBK - 1) / kBK;
+    cb = lo / kBK + tc.e;
+  }
+  GemmArgs po = p;
+  if (KG) po.C = reinterpret_cast<float*>(p.C) + (int64_t)tc.e * p.c_estride;
+  const int rows = (int)min(tc.mend - tc.m0, (int64_t)kBM);
+
+  float acc[kTM][kTN][4];
+#pragma unroll
+  for (int i = 0; i < kTM; ++i)
+#pragma unroll
+    for (int j = 0; j < kTN; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[i][j][r] = 0.f;
+  uint8_t* const ep = (w >> 1) == 0 ? sa0 : (w >> 1) == 1 ? sa1 : (w >> 1) == 2 ? sb0 : sb1;
+  if (KG && nk == 0) {
+    // an expert without tokens: its gradient is zero
+    if (!p.accumulate)
+      store_tile<kTM, kTN, 1, 16>(acc, ep + (w & 1) * 12288, po, tc.m0 + wr * 64, tc.mend, tc.n0 + wc * 128, lane);
+    return;
+  }
+
+  const __amdgpu_buffer_rsrc_t rA = make_rsrc(p.A + tc.m0 * p.lda, (uint32_t)(rows * p.lda));
+  const __amdgpu_buffer_rsrc_t rB = make_rsrc(p.B + (int64_t)tc.n0 * p.ldb, (uint32_t)(kWBN * p.ldb));
+  const __amdgpu_buffer_rsrc_t rSa = make_rsrc(p.sa + tc.m0 * p.ld_sa, (uint32_t)(rows * p.ld_sa * 4));
+  const __amdgpu_buffer_rsrc_t rSb = make_rsrc(p.sb + (int64_t)tc.n0 * p.sb_rs, (uint32_t)(kWBN * p.sb_rs * 4));
+  const int r8 = lane >> 3, lc = (lane & 7) ^ r8;
+  const uint32_t voffA = (uint32_t)((w * kWIA * 8 + r8) * p.lda + 16 * lc);
+  const uint32_t voffB = (uint32_t)((w * kWIB * 8 + r8) * p.ldb + 16 * lc);
+  const uint32_t stepA = (uint32_t)(8 * p.lda), stepB = (uint32_t)(8 * p.ldb);
+  // lane (w, l): row scale of row 64 (w % 4) + l (clamped to a valid row),
+  // column scale of column 64 w + l (mod 256)
+  const uint32_t voffSa = (uint32_t)(min(wr * 64 + lane, rows - 1) * p.ld_sa * 4);
+  const uint32_t voffSb = (uint32_t)(((w * 64 + lane) & (kWBN - 1)) * p.sb_rs * 4);
+
+  auto issue_a = [&](int kb, uint8_t* ar, int d) {
+    kb += cb;
+    if (d < kWIA)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, (lds_ptr)(ar + (w * kWIA + d) * 1024), 16, voffA + d * stepA,
+                                               (uint32_t)kb * kBK, 0, 0);
+    else
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rSa, (lds_ptr)(ar + RA + w * 256), 4, voffSa, (uint32_t)kb * 4, 0, 0);
+  };
+  auto issue_b = [&](int kb, uint8_t* br, int q) {
+    kb += cb;
+    if (q < kWIB)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, (lds_ptr)(br + (w * kWIB + q) * 1024), 16, voffB + q * stepB,
+                                               (uint32_t)kb * kBK, 0, 0);
+    else
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rSb, (lds_ptr)(br + RB + w * 256), 4, voffSb, (uint32_t)kb * 4, 0, 0);
+  };
+  constexpr int kDmaB = kWIB + 1;
+  constexpr int kWaitA = 0x0F70 | kWDmaA;
+
+  const int sw = l16 & 7;
+  const int offLo = l16 * kBK + 16 * (g ^ sw);
+  const int offHi = l16 * kBK + 16 * ((4 + g) ^ sw);
+  auto rdA = [&](const uint8_t* ar, int i) -> v8i {
+    const uint8_t* base = ar + (wr * 64 + 16 * i) * kBK;
+    return make_frag(*reinterpret_cast<const uint4*>(base + offLo), *reinterpret_cast<const uint4*>(base + offHi));
+  };
+  auto rdB = [&](const uint8_t* br, int j) -> v8i {
+    const uint8_t* base = br + (wc * 128 + 16 * j) * kBK;
+    return make_frag(*reinterpret_cast<const uint4*>(base + offLo), *reinterpret_cast<const uint4*>(base + offHi));
+  };
+  // row scale: lane (l16, g) holds row 16 (l16 / 4) + 4 g + l16 % 4 of its
+  // wave's strip (row_scales broadcasts); column scale of column 16 j + l16
+  const int rowSa = wr * 64 + 16 * (l16 >> 2) + 4 * g + (l16 & 3);
+  auto rdSa = [&](const uint8_t* ar) -> float { return *reinterpret_cast<const float*>(ar + RA + 4 * rowSa); };
+  auto rdSb = [&](const uint8_t* br, int j) -> float {
+    return *reinterpret_cast<const float*>(br + RB + 4 * (wc * 128 + 16 * j + l16));
+  };
+
+  v8i a[kTM];
+  v8i bring[2];
+  v4f pp[kTM];
+  float sc[kTM][4];       // row scales in use
+  float sa_nx = 0.f;      // the next chunk's row scale, as read
+  float sbc_prev = 0.f;   // column scale of the previous chunk's last column
+  float sbc_first = 0.f;  // column scale of this chunk's column 0
+  auto promote = [&](int i, int j, float sbc) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc[i][j][r] = __builtin_fmaf(pp[i][r], sc[i][r] * sbc, acc[i][j][r]);
+  };
+  auto load_sc = [&](int i) {
+    switch (i) {
+      case 0: row_scales<0>(sa_nx, 1.f, sc[0]); break;
+      case 1: row_scales<1>(sa_nx, 1.f, sc[1]); break;
+      case 2: row_scales<2>(sa_nx, 1.f, sc[2]); break;
+      default: row_scales<3>(sa_nx, 1.f, sc[3]); break;
+    }
+  };
+  auto mfma = [&](const v8i& x, const v8i& y) -> v4f {
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(x, y, v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
+  };
+  auto fence = [] { asm volatile("" ::: "memory"); };
+
+  // ---- prologue: A(0), B(0), A(1), B(1) in flight in that order; chunk 0 published
+#pragma unroll
+  for (int d = 0; d < kWDmaA; ++d) issue_a(0, sa0, d);
+#pragma unroll
+  for (int q = 0; q < kDmaB; ++q) issue_b(0, sb0, q);
+#pragma unroll
+  for (int d = 0; d < kWDmaA; ++d) issue_a(min(1, nk - 1), sa1, d);
+#pragma unroll
+  for (int q = 0; q < kDmaB; ++q) issue_b(min(1, nk - 1), sb1, q);
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (kWDmaA + kDmaB));
+  __builtin_amdgcn_s_barrier();
+  fence();
+#pragma unroll
+  for (int i = 0; i < kTM; ++i) {
+    a[i] = rdA(sa0, i);
+    pp[i] = v4f{0.f, 0.f, 0.f, 0.f};
+  }
+  sa_nx = rdSa(sa0);
+  bring[0] = rdB(sb0, 0);
+  sbc_first = rdSb(sb0, 0);
+#pragma unroll
+  for (int i = 0; i < kTM; ++i) load_sc(i);
+
+  auto step = [&](int c, auto U) {
+    constexpr int u = decltype(U)::value;
+    uint8_t* const acur = u == 0 ? sa0 : sa1;
+    uint8_t* const anxt = u == 0 ? sa1 : sa0;
+    uint8_t* const bcur = u == 0 ? sb0 : sb1;
+    uint8_t* const bnxt = u == 0 ? sb1 : sb0;
+    const int c2 = min(c + 2, nk - 1);
+    float sbc[kTN + 1];  // this chunk's column scales, [kTN] = the next chunk's column 0
+    sbc[0] = sbc_first;
+#pragma unroll
+    for (int j = 0; j < kTN; ++j) {
+      const v8i bj = bring[j & 1];
+      if (j + 1 < kTN) {
+        bring[(j + 1) & 1] = rdB(bcur, j + 1);
+        sbc[j + 1] = rdSb(bcur, j + 1);
+      } else {
+        bring[0] = rdB(bnxt, 0);
+        sbc[kTN] = rdSb(bnxt, 0);
+      }
+      fence();
+#pragma unroll
+      for (int i = 0; i < kTM; ++i) {
+        const int t = kTM * j + i;
+        pp[i] = mfma(a[i], bj);
+        if (t >= kSkew) {
+          const int tp = t - kSkew;
+          promote(tp % kTM, tp / kTM, sbc[tp / kTM]);
+        } else {
+          promote(t + 1, kTN - 1, sbc_prev);
+          load_sc(t + 1);
+        }
+        if (t >= kWFirstSlot && t < kWFirstSlot + kWDmaSlots) {
+#pragma unroll
+          for (int d = 0; d < kWDmaA; ++d)
+            if (kWFirstSlot + (d * kWDmaSlots) / kWDmaA == t) issue_a(c2, acur, d);
+        }
+        if (j == kTN - 1) {
+          issue_b(c2, bcur, i);
+          if (i == kTM - 1) issue_b(c2, bcur, kWIB);  // the column scales
+          a[i] = rdA(anxt, i);
+          if (i == 0) sa_nx = rdSa(anxt);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (j == 0) {
+        __builtin_amdgcn_s_waitcnt(0xC07F);
+        __builtin_amdgcn_s_barrier();
+        fence();
+      }
+      if (j == kTN - 2) {
+        __builtin_amdgcn_s_waitcnt(0xC07F);
+        __builtin_amdgcn_s_waitcnt(kWaitA);
+        __builtin_amdgcn_s_barrier();
+        fence();
+      }
+    }
+    load_sc(0);
+    sbc_prev = sbc[kTN - 1];
+    sbc_first = sbc[kTN];
+  };
+
+  int c = 0;
+  for (; c + 2 <= nk; c += 2) {
+    step(c, IC<0>());
+    step(c + 1, IC<1>());
+  }
+  if (c < nk) step(c, IC<0>());
+#pragma unroll
+  for (int i = 1; i < kTM; ++i) promote(i, kTN - 1, sbc_prev);
+
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  __builtin_amdgcn_s_barrier();
+  fence();
+  store_tile<kTM, kTN, 1, 16>(acc, ep + (w & 1) * 12288, po, tc.m0 + wr * 64, tc.mend, tc.n0 + wc * 128, lane);
+#endif  // __HIP_DEVICE_COMPILE__
+}
+
 namespace {
 
 template <int SB_MODE, int OUT_F32, bool GROUPED, bool KG = false, bool SC4 = false>
@@ -671,7 +895,7 @@ hipError_t launch_one(const GemmArgs& a, hipStream_t st) {
 // environment variable FP8Q_GEMM_TILE = "256x128" or "256x256" overrides the
 // choice (both tiles give bit-identical results), for tests and measurement.
 static bool use_wide_tile(const GemmArgs& a) {
-  if (a.out_f32 && a.offsets != nullptr) return false;  // no FP32-output grouped instantiation
+  if (a.N % kWBN != 0) return false;
   if (const char* f = getenv("FP8Q_GEMM_TILE")) {
     if (!strcmp(f, "256x128")) return false;
     if (!strcmp(f, "256x256")) return true;
@@ -687,11 +911,20 @@ static bool use_wide_tile(const GemmArgs& a) {
 hipError_t launch_gemm_fp8(const GemmArgs& a, hipStream_t st) {
   const bool sc4 = a.ld_sa % 4 == 0 && (reinterpret_cast<uintptr_t>(a.sa) & 15) == 0;
   if (a.sb_mode == kSbRow) {  // weight gradients: FP32 out (row scales 128 B per row: no gain from blocks)
+    if (use_wide_tile(a)) {
+      const int64_t tn = a.N / kWBN, tm = (a.M + kBM - 1) / kBM;
+      if (a.k_grouped)
+        hipLaunchKernelGGL((k_gemm_fp8_wide_row<true>), dim3((uint32_t)(a.E * tm * 8 * ((tn + 7) / 8))),
+                           dim3(kWNT), 0, st, a);
+      else
+        hipLaunchKernelGGL((k_gemm_fp8_wide_row<false>), dim3((uint32_t)(tm * tn)), dim3(kWNT), 0, st, a);
+      return hipGetLastError();
+    }
     if (a.k_grouped) return launch_one<kSbRow, 1, true, true>(a, st);
     return launch_one<kSbRow, 1, false>(a, st);
   }
   // the 256 x 256 tile when it leaves no more than half of the chip idle
-  if (sc4 && a.N % kWBN == 0 && use_wide_tile(a)) {
+  if (sc4 && !(a.out_f32 && a.offsets != nullptr) && use_wide_tile(a)) {  // no FP32-output grouped instantiation
     const int64_t tn = a.N / kWBN, tm = (a.M + kBM - 1) / kBM;
     const int64_t tiles = a.offsets != nullptr ? (tm + a.E) * tn : tm * tn;  // grouped: upper bound
     if (a.offsets != nullptr)

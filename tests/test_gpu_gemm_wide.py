@@ -95,3 +95,34 @@ def test_wide_tile_against_oracle_ragged():
     wo, wso, _ = oracle.quant_weight_128x128(f32(w))
     y_ref, s_ref = oracle.fprop_ref(xo, xso, wo, wso)
     check_gemm(f32(y), y_ref, s_ref, False, "wide fprop 300x512x640", False, nk=k // 128)
+
+
+@pytest.mark.parametrize("t,n,k", [(128, 256, 256), (640, 512, 768), (4096, 2048, 7168)])
+@pytest.mark.parametrize("accumulate", [False, True])
+def test_wgrad_tiles_agree(t, n, k, accumulate):
+    """dW [n, k] (=|+=) dY^T . X over t tokens: one B scale per output column."""
+    log(f"wgrad T={t} {n}x{k} accumulate={accumulate}")
+    x = synth.to_bf16(synth.general(t, k, seed=t + k, kind="t3", outlier_frac=0.002, outlier_mul=30.0))
+    dy = synth.to_bf16(synth.general(t, n, seed=t + n + 1, kind="t3", outlier_frac=0.01, outlier_mul=100.0))
+    xq_t, xs_t = fq.quant_transpose(gpu(x))
+    dyq_t, dys_t = fq.quant_transpose(gpu(dy))
+    base = torch.from_numpy(synth.general(n, k, seed=5).astype(np.float32))
+
+    def run():
+        dw = gpu(base.clone()) if accumulate else None
+        return fq.gemm_wgrad(dyq_t, dys_t, xq_t, xs_t, dw)
+
+    _same_bits(run, f"wgrad T={t} {n}x{k}")
+
+
+@pytest.mark.parametrize("total,e,n,k", [(700, 5, 256, 512), (3000, 8, 512, 1024)])
+def test_grouped_wgrad_tiles_agree(total, e, n, k):
+    """Grouped Wgrad: ragged per-expert token chunks, an empty expert (its
+    gradient written as zeros), per-expert outputs."""
+    log(f"grouped wgrad {total} tokens, {e} experts, {n}x{k}")
+    xm, _, off = synth.small_moe(total, e, n, k, seed=total + 2 * e)
+    dym = synth.to_bf16(synth.general(total, n, seed=total + 3, kind="t3"))
+    offg = gpu(off)
+    xq_t, xs_t = fq.quant_transpose_grouped(gpu(xm), offg)
+    dyq_t, dys_t = fq.quant_transpose_grouped(gpu(dym), offg)
+    _same_bits(lambda: fq.grouped_gemm_wgrad(dyq_t, dys_t, xq_t, xs_t, offg, total), "grouped wgrad")
