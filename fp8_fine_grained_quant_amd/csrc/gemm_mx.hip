@@ -30,6 +30,9 @@
 // therefore passes byte g of the row's 4-byte scale word of the chunk,
 // shifted down to bits [7:0] (operand select 0).
 
+#include <stdlib.h>
+#include <string.h>
+
 #include "device_common.h"
 #include "gemm_tile.h"
 #include "launch.h"
@@ -291,6 +294,209 @@ __global__ __launch_bounds__(kNT) void k_gemm_mx(MxArgs p) {
 #endif  // __HIP_DEVICE_COMPILE__
 }
 
+// ---------------------------------------------------------------------------
+// Wide tile: 256 x 256 outputs, eight waves (two per SIMD), each the 64 x 128
+// strip above, so results are bit-identical to k_gemm_mx.  A and B live in
+// separate LDS regions, two chunks each: A region c%2 takes A(c+2) as soon as
+// every wave holds A(c) in registers (first barrier of chunk c), B region c%2
+// takes B(c+2) in the last column, after every wave has read B(c) -- the same
+// schedule as the FP8 kernel's wide tile.  The chunk's B scale words ride
+// with its B loads ([half][l16][j] words beside the B region); the A scale
+// words travel in the 4-chunk ring (16-byte aligned scale rows only).
+constexpr int kWBN = 256, kWNT = 512;
+constexpr int kWIA = kBM * kBK / (16 * kWNT);  // 4
+constexpr int kWIB = kWBN * kBK / (16 * kWNT);  // 4
+constexpr int kWDmaA = kWIA + 1, kWDmaB = kWIB + 1;
+constexpr int kWFirstSlot = kTM, kWDmaSlots = 20;
+constexpr int kWScB = 2048;  // bytes beside each B region: 256 scale words (+ a spare copy)
+static_assert(kWIB == kTM && kWDmaA <= kWDmaSlots && kWFirstSlot + kWDmaSlots <= kTM * (kTN - 1), "schedule");
+
+template <int OUT_F32>
+__global__ __launch_bounds__(kWNT) void k_gemm_mx_wide(MxArgs p) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  constexpr int RA = kBM * kBK, RB = kWBN * kBK;
+  __shared__ __attribute__((aligned(16))) uint8_t sa0[RA];
+  __shared__ __attribute__((aligned(16))) uint8_t sa1[RA];
+  __shared__ __attribute__((aligned(16))) uint8_t sb0[RB + kWScB];
+  __shared__ __attribute__((aligned(16))) uint8_t sb1[RB + kWScB];
+  __shared__ __attribute__((aligned(16))) uint32_t scA[2 * 256 * 4];
+  __shared__ __attribute__((aligned(16))) uint8_t dmy[1024];
+
+  const GemmArgs& q = p.g;
+  TileCoord tc;
+  tile_coord<kBM, kWBN, false>(q, tc);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wr = w & 3, wc = w >> 2;
+  const int l16 = lane & 15, g = lane >> 4;
+  const int nk = (int)(q.K / kBK);
+  const int rows = (int)min(tc.mend - tc.m0, (int64_t)kBM);
+
+  const __amdgpu_buffer_rsrc_t rA = make_rsrc(q.A + tc.m0 * q.lda, (uint32_t)(rows * q.lda));
+  const __amdgpu_buffer_rsrc_t rB = make_rsrc(q.B + (int64_t)tc.n0 * q.ldb, (uint32_t)(kWBN * q.ldb));
+  const __amdgpu_buffer_rsrc_t rSa = make_rsrc(p.sa + tc.m0 * p.ld_sa, (uint32_t)(rows * p.ld_sa));
+  const __amdgpu_buffer_rsrc_t rSb = make_rsrc(p.sb + (int64_t)tc.n0 * p.ld_sb, (uint32_t)(kWBN * p.ld_sb));
+  const int r8 = lane >> 3, lc = (lane & 7) ^ r8;
+  const uint32_t voffA = (uint32_t)((w * kWIA * 8 + r8) * q.lda + 16 * lc);
+  const uint32_t voffB = (uint32_t)((w * kWIB * 8 + r8) * q.ldb + 16 * lc);
+  const uint32_t stepA = (uint32_t)(8 * q.lda), stepB = (uint32_t)(8 * q.ldb);
+  // A scales: lane (w, l), w < 4, fetches row 64w + l (clamped to a valid
+  // row).  B scales: lane L = 64w + l (L < 256, w < 4) fetches the word of
+  // column 128 (L / 128) + 16 ((L % 128) % 8) + (L % 128) / 8 into word L, so
+  // each half's words land as [l16][j]; waves 4-7 write a spare copy.
+  const uint32_t voffSa = (uint32_t)(min(wr * 64 + lane, rows - 1) * p.ld_sa);
+  const int Lb = (w * 64 + lane) & (kWBN - 1), Lh = Lb & 127;
+  const uint32_t voffSb = (uint32_t)((128 * (Lb >> 7) + 16 * (Lh & 7) + (Lh >> 3)) * p.ld_sb);
+
+  auto issue_a = [&](int kb, uint8_t* ar, int d) {
+    if (d < kWIA) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, (lds_ptr)(ar + (w * kWIA + d) * 1024), 16, voffA + d * stepA,
+                                               (uint32_t)kb * kBK, 0, 0);
+    } else {
+      const bool real = w < 4 && (kb & 3) == 0;
+      uint8_t* dst = real ? reinterpret_cast<uint8_t*>(scA) + ((kb >> 2) & 1) * 4096 + w * 1024 : dmy;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rSa, (lds_ptr)dst, 16, voffSa, real ? (uint32_t)kb * 4 : 0x40000000u,
+                                               0, 0);
+    }
+  };
+  auto issue_b = [&](int kb, uint8_t* br, int qq) {
+    if (qq < kWIB)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, (lds_ptr)(br + (w * kWIB + qq) * 1024), 16, voffB + qq * stepB,
+                                               (uint32_t)kb * kBK, 0, 0);
+    else
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rSb, (lds_ptr)(br + RB + w * 256), 4, voffSb, (uint32_t)kb * 4, 0, 0);
+  };
+  constexpr int kWaitA = 0x0F70 | kWDmaA;
+
+  const int sw = l16 & 7;
+  const int offLo = l16 * kBK + 16 * (g ^ sw);
+  const int offHi = l16 * kBK + 16 * ((4 + g) ^ sw);
+  auto rdA = [&](const uint8_t* ar, int i) -> v8i {
+    const uint8_t* base = ar + (wr * 64 + 16 * i) * kBK;
+    return make_frag(*reinterpret_cast<const uint4*>(base + offLo), *reinterpret_cast<const uint4*>(base + offHi));
+  };
+  auto rdB = [&](const uint8_t* br, int j) -> v8i {
+    const uint8_t* base = br + (wc * 128 + 16 * j) * kBK;
+    return make_frag(*reinterpret_cast<const uint4*>(base + offLo), *reinterpret_cast<const uint4*>(base + offHi));
+  };
+  const uint32_t sh = 8 * g;
+  auto rdSa = [&](int kb, int i) -> int {
+    const int row = wr * 64 + 16 * i + l16;
+    return (int)(scA[((kb >> 2) & 1) * 1024 + row * 4 + (kb & 3)] >> sh);
+  };
+  auto rdSb = [&](const uint8_t* br, int (&out)[kTN]) {
+    const uint8_t* base = br + RB + 512 * wc + 32 * l16;
+    const uint4 lo = *reinterpret_cast<const uint4*>(base);
+    const uint4 hi = *reinterpret_cast<const uint4*>(base + 16);
+    out[0] = (int)(lo.x >> sh); out[1] = (int)(lo.y >> sh); out[2] = (int)(lo.z >> sh); out[3] = (int)(lo.w >> sh);
+    out[4] = (int)(hi.x >> sh); out[5] = (int)(hi.y >> sh); out[6] = (int)(hi.z >> sh); out[7] = (int)(hi.w >> sh);
+  };
+
+  v4f acc[kTM][kTN];
+#pragma unroll
+  for (int i = 0; i < kTM; ++i)
+#pragma unroll
+    for (int j = 0; j < kTN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+  v8i a[kTM];
+  v8i bring[2];
+  int sa[kTM], sb[kTN];
+  auto fence = [] { asm volatile("" ::: "memory"); };
+
+#pragma unroll
+  for (int d = 0; d < kWDmaA; ++d) issue_a(0, sa0, d);
+#pragma unroll
+  for (int qq = 0; qq < kWDmaB; ++qq) issue_b(0, sb0, qq);
+#pragma unroll
+  for (int d = 0; d < kWDmaA; ++d) issue_a(min(1, nk - 1), sa1, d);
+#pragma unroll
+  for (int qq = 0; qq < kWDmaB; ++qq) issue_b(min(1, nk - 1), sb1, qq);
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (kWDmaA + kWDmaB));  // A(0), B(0) landed
+  __builtin_amdgcn_s_barrier();
+  fence();
+#pragma unroll
+  for (int i = 0; i < kTM; ++i) {
+    a[i] = rdA(sa0, i);
+    sa[i] = rdSa(0, i);
+  }
+  bring[0] = rdB(sb0, 0);
+  rdSb(sb0, sb);
+
+  auto step = [&](int c, auto U) {
+    constexpr int u = decltype(U)::value;
+    uint8_t* const acur = u == 0 ? sa0 : sa1;
+    uint8_t* const anxt = u == 0 ? sa1 : sa0;
+    uint8_t* const bcur = u == 0 ? sb0 : sb1;
+    uint8_t* const bnxt = u == 0 ? sb1 : sb0;
+    const int c2 = min(c + 2, nk - 1);
+    int sb_nx[kTN];
+#pragma unroll
+    for (int j = 0; j < kTN; ++j) {
+      const v8i bj = bring[j & 1];
+      if (j + 1 < kTN) {
+        bring[(j + 1) & 1] = rdB(bcur, j + 1);
+      } else {
+        bring[0] = rdB(bnxt, 0);
+        rdSb(bnxt, sb_nx);
+      }
+      fence();
+#pragma unroll
+      for (int i = 0; i < kTM; ++i) {
+        const int t = kTM * j + i;
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[i], bj, acc[i][j], 0, 0, 0, sa[i], 0, sb[j]);
+        if (t >= kWFirstSlot && t < kWFirstSlot + kWDmaSlots) {
+#pragma unroll
+          for (int d = 0; d < kWDmaA; ++d)
+            if (kWFirstSlot + (d * kWDmaSlots) / kWDmaA == t) issue_a(c2, acur, d);
+        }
+        if (j == kTN - 1) {
+          issue_b(c2, bcur, i);
+          if (i == kTM - 1) issue_b(c2, bcur, kWIB);  // the B scale words
+          a[i] = rdA(anxt, i);
+          sa[i] = rdSa(min(c + 1, nk - 1), i);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (j == 0) {
+        // every wave holds A(c) in registers: A region u may take A(c+2)
+        __builtin_amdgcn_s_waitcnt(0xC07F);
+        __builtin_amdgcn_s_barrier();
+        fence();
+      }
+      if (j == kTN - 2) {
+        // every wave has read B(c) and its scale words; A(c+1), B(c+1) landed
+        __builtin_amdgcn_s_waitcnt(0xC07F);
+        __builtin_amdgcn_s_waitcnt(kWaitA);
+        __builtin_amdgcn_s_barrier();
+        fence();
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kTN; ++j) sb[j] = sb_nx[j];
+  };
+
+  int c = 0;
+  for (; c + 2 <= nk; c += 2) {
+    step(c, IC<0>());
+    step(c + 1, IC<1>());
+  }
+  if (c < nk) step(c, IC<0>());
+
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  fence();
+  float out[kTM][kTN][4];
+#pragma unroll
+  for (int i = 0; i < kTM; ++i)
+#pragma unroll
+    for (int j = 0; j < kTN; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) out[i][j][r] = acc[i][j][r];
+  uint8_t* const ep = (w >> 1) == 0 ? sa0 : (w >> 1) == 1 ? sa1 : (w >> 1) == 2 ? sb0 : sb1;
+  store_tile<kTM, kTN, OUT_F32, OUT_F32 ? 16 : 32>(out, ep + (w & 1) * 12288, q, tc.m0 + wr * 64, tc.mend,
+                                                 tc.n0 + wc * 128, lane);
+#endif  // __HIP_DEVICE_COMPILE__
+}
+
 namespace {
 
 template <int OUT_F32, bool SC4>
@@ -303,8 +509,32 @@ hipError_t launch_mx(const MxArgs& a, hipStream_t st) {
 
 }  // namespace
 
+// The 256 x 256 tile when its grid has more tiles than half the compute
+// units (the rule and the FP8Q_GEMM_TILE override of the FP8 GEMM).
+static bool use_wide_mx(const MxArgs& a) {
+  if (a.g.N % kWBN != 0) return false;
+  if (const char* f = getenv("FP8Q_GEMM_TILE")) {
+    if (!strcmp(f, "256x128")) return false;
+    if (!strcmp(f, "256x256")) return true;
+  }
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    cus = 256;
+  return 2 * ((a.g.M + kBM - 1) / kBM) * (a.g.N / kWBN) > cus;
+}
+
 hipError_t launch_gemm_mx(const MxArgs& a, hipStream_t st) {
   const bool sc4 = a.ld_sa % 16 == 0 && (reinterpret_cast<uintptr_t>(a.sa) & 15) == 0;
+  if (sc4 && use_wide_mx(a)) {
+    const int64_t tiles = ((a.g.M + kBM - 1) / kBM) * (a.g.N / kWBN);
+    if (tiles <= 0) return hipSuccess;
+    if (a.g.out_f32)
+      hipLaunchKernelGGL((k_gemm_mx_wide<1>), dim3((uint32_t)tiles), dim3(kWNT), 0, st, a);
+    else
+      hipLaunchKernelGGL((k_gemm_mx_wide<0>), dim3((uint32_t)tiles), dim3(kWNT), 0, st, a);
+    return hipGetLastError();
+  }
   if (sc4) return a.g.out_f32 ? launch_mx<1, true>(a, st) : launch_mx<0, true>(a, st);
   return a.g.out_f32 ? launch_mx<1, false>(a, st) : launch_mx<0, false>(a, st);
 }

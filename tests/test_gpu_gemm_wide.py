@@ -126,3 +126,24 @@ def test_grouped_wgrad_tiles_agree(total, e, n, k):
     xq_t, xs_t = fq.quant_transpose_grouped(gpu(xm), offg)
     dyq_t, dys_t = fq.quant_transpose_grouped(gpu(dym), offg)
     _same_bits(lambda: fq.grouped_gemm_wgrad(dyq_t, dys_t, xq_t, xs_t, offg, total), "grouped wgrad")
+
+
+@pytest.mark.parametrize("m,n,k", [(300, 256, 512), (1000, 1024, 2048), (4096, 7168, 2048)])
+@pytest.mark.parametrize("out", ["bf16", "f32_accumulate"])
+def test_mx_tiles_agree(m, n, k, out):
+    """The microscaling GEMM's two tiles: bit-identical outputs (BF16, and
+    FP32 accumulated into an existing C).  K is a multiple of 512 so the
+    scale rows are 16-byte aligned, which the 256 x 256 tile needs."""
+    log(f"mx gemm {m}x{n}x{k} {out}")
+    a = synth.to_bf16(synth.general(m, k, seed=m + k, kind="t3", outlier_frac=0.002, outlier_mul=30.0))
+    b = torch.from_numpy((synth.general(n, k, seed=n + k + 1) * 0.02).astype(np.float32))
+    aq, as_ = fq.quant_mx(gpu(a))
+    bq, bs = fq.quant_mx(gpu(b))
+    base = torch.from_numpy(synth.general(m, n, seed=9).astype(np.float32))
+
+    def run():
+        if out == "bf16":
+            return fq.gemm_mx(aq, as_, bq, bs)
+        return fq.gemm_mx(aq, as_, bq, bs, c=gpu(base.clone()))
+
+    _same_bits(run, f"mx {m}x{n}x{k}")
