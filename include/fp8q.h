@@ -39,6 +39,13 @@
  *     until the work enqueued on `stream` has completed.
  *   - Work is enqueued asynchronously on `stream` (NULL = the default
  *     stream).  Results are deterministic (no atomics, no split-K).
+ *   - The FP8 and MX GEMMs pick a 256x128 or a 256x256 workgroup tile by
+ *     problem size (the wide one when its grid has more tiles than half the
+ *     device's compute units and the output width is a multiple of 256).
+ *     Both run the same arithmetic in the same order, so the choice never
+ *     changes a result bit.  The environment variable FP8Q_GEMM_TILE =
+ *     "256x128" or "256x256" overrides the choice (read at each call), for
+ *     tests and measurement.
  *   - Arguments are validated on the host before anything is enqueued; a bad
  *     argument returns its status and enqueues nothing.  A zero-size call is
  *     a no-op returning FP8Q_OK.  A launch failure reported by the HIP runtime
