@@ -877,7 +877,7 @@ namespace {
 template <int SB_MODE, int OUT_F32, bool GROUPED, bool KG = false, bool SC4 = false>
 hipError_t launch_one(const GemmArgs& a, hipStream_t st) {
   const int64_t tiles_n = a.N / kBN, tiles_m = (a.M + kBM - 1) / kBM;
-  const int64_t tiles = KG ? a.E * tiles_m * 8 * ((tiles_n + 7) / 8)    // every expert: 8 XCD slices
+  const int64_t tiles = KG ? a.E * 8 * ((tiles_m * tiles_n + 7) / 8)  // every expert: 8 XCD shares
                         : GROUPED ? (tiles_m + a.E) * tiles_n             // upper bound: a partial tile per expert
                                   : tiles_m * tiles_n;
   if (tiles <= 0) return hipSuccess;
@@ -914,7 +914,7 @@ hipError_t launch_gemm_fp8(const GemmArgs& a, hipStream_t st) {
     if (use_wide_tile(a)) {
       const int64_t tn = a.N / kWBN, tm = (a.M + kBM - 1) / kBM;
       if (a.k_grouped)
-        hipLaunchKernelGGL((k_gemm_fp8_wide_row<true>), dim3((uint32_t)(a.E * tm * 8 * ((tn + 7) / 8))),
+        hipLaunchKernelGGL((k_gemm_fp8_wide_row<true>), dim3((uint32_t)(a.E * 8 * ((tm * tn + 7) / 8))),
                            dim3(kWNT), 0, st, a);
       else
         hipLaunchKernelGGL((k_gemm_fp8_wide_row<false>), dim3((uint32_t)(tm * tn)), dim3(kWNT), 0, st, a);

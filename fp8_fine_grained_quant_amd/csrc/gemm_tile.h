@@ -44,22 +44,26 @@ __device__ __forceinline__ bool tile_coord(const GemmArgs& p, TileCoord& tc) {
   if (p.k_grouped) {
     // grouped contraction: every expert owns a full M x N grid of tiles, and
     // tiles of different experts differ in work (the expert's token count).
-    // Each XCD takes an equal slice of every expert: n-tiles
-    // [xcd*nx, xcd*nx + nx) with all m-tiles, walked expert by expert with
-    // the m-tiles innermost, so the XCD reads each of its X^T column blocks
-    // once and shares the expert's dY^T rows among its workgroups.  (Taking
-    // the experts in turns tile by tile instead measured 1.6x slower: the
-    // XCD's L2 then holds no expert's operands long enough.)
+    // Each XCD takes an equal share of every expert: the expert's tiles in
+    // n-major order (m-tiles innermost) are cut into 8 contiguous runs whose
+    // lengths differ by at most one, run x on XCD x, walked expert by expert,
+    // so an XCD reads about 1/8 of each expert's X^T column blocks once and
+    // shares the expert's dY^T rows among its workgroups.  (Taking the
+    // experts in turns tile by tile instead measured 1.6x slower: the XCD's
+    // L2 then holds no expert's operands long enough.  Whole n-slices per
+    // XCD leave an XCD idle when the n-tile count is not a multiple of 8, as
+    // with 28 tiles of 256 columns.)
     const int tiles_m = (int)((p.M + BM - 1) / BM);
-    const int nx = (tiles_n + 7) / 8;
-    const int per_ex = tiles_m * nx;
-    const int e = (bid >> 3) / per_ex;
+    const int per_ex = tiles_m * tiles_n;
+    const int slots = (per_ex + 7) / 8;  // workgroups per expert per XCD
+    const int e = (bid >> 3) / slots;
     if (e >= (int)p.E) return false;
-    const int tl = (bid >> 3) - e * per_ex;
-    const int n = xcd * nx + tl / tiles_m;
-    if (n >= tiles_n) return false;
-    tc.m0 = (int64_t)(tl % tiles_m) * BM;
-    tc.n0 = n * BN;
+    const int tl = (bid >> 3) - e * slots;
+    const int q = per_ex >> 3, r = per_ex & 7;
+    if (tl >= q + (xcd < r ? 1 : 0)) return false;
+    const int t = xcd * q + min(xcd, r) + tl;
+    tc.m0 = (int64_t)(t % tiles_m) * BM;
+    tc.n0 = (t / tiles_m) * BN;
     tc.mend = p.M;
     tc.e = e;
     return true;
