@@ -693,7 +693,7 @@ __global__ __launch_bounds__(kWNT) void k_gemm_fp8_wide_row(GemmArgs p) {
   if (KG && nk == 0) {
     // an expert without tokens: its gradient is zero
     if (!p.accumulate)
-      store_tile<kTM, kTN, 1, 16>(acc, ep + (w & 1) * 12288, po, tc.m0 + wr * 64, tc.mend, tc.n0 + wc * 128, lane);
+      store_tile<kTM, kTN, 1, 16, 1>(acc, ep + (w & 1) * 12288, po, tc.m0 + wr * 64, tc.mend, tc.n0 + wc * 128, lane);
     return;
   }
 
@@ -868,7 +868,7 @@ __global__ __launch_bounds__(kWNT) void k_gemm_fp8_wide_row(GemmArgs p) {
   __builtin_amdgcn_s_waitcnt(0x0F70);
   __builtin_amdgcn_s_barrier();
   fence();
-  store_tile<kTM, kTN, 1, 16>(acc, ep + (w & 1) * 12288, po, tc.m0 + wr * 64, tc.mend, tc.n0 + wc * 128, lane);
+  store_tile<kTM, kTN, 1, 16, 1>(acc, ep + (w & 1) * 12288, po, tc.m0 + wr * 64, tc.mend, tc.n0 + wc * 128, lane);
 #endif  // __HIP_DEVICE_COMPILE__
 }
 

@@ -88,12 +88,17 @@ __device__ __forceinline__ bool tile_coord(const GemmArgs& p, TileCoord& tc) {
   return true;
 }
 
+// NTS = 1 writes non-temporally: for outputs that are written once and read
+// much later (the weight gradients), so they do not fill the caches with
+// dirty lines that the kernels after them must write back (measured:
+// grouped Wgrad 796 -> 618 us, and the kernel after it 521 -> 465 us).
+//
 // Writes one wave's WM x WN accumulator block (MFMA 16x16 result layout:
 // lane l holds rows 4*(l/16) + r, column l%16 of each sub-tile) to C, staged
 // through the wave's private LDS region `ep` in passes of ER rows so that
 // every global access is a full 16-byte row segment.  Rows at or beyond
 // `mend` are not written.
-template <int TM, int TN, int OUT_F32, int ER>
+template <int TM, int TN, int OUT_F32, int ER, int NTS = 0>
 __device__ __forceinline__ void store_tile(const float (&acc)[TM][TN][4], uint8_t* ep, const GemmArgs& p,
                                            int64_t row0, int64_t mend, int col0, int lane) {
   constexpr int WM = 16 * TM, WN = 16 * TN;
@@ -137,7 +142,7 @@ __device__ __forceinline__ void store_tile(const float (&acc)[TM][TN][4], uint8_
         f.x += o.x; f.y += o.y; f.z += o.z; f.w += o.w;
         *reinterpret_cast<float4*>(dst) = f;
       } else {
-        *reinterpret_cast<uint4*>(dst) = v;
+        st_stream16<NTS>(dst, v.x, v.y, v.z, v.w);
       }
     }
   }
