@@ -68,7 +68,17 @@ __device__ __forceinline__ bool tile_coord(const GemmArgs& p, TileCoord& tc) {
     tc.e = e;
     return true;
   }
-  // grouped rows: walk the experts' tile counts; tiles never straddle experts
+  // grouped rows: tiles never straddle experts.  The grid is sized for the
+  // worst case (a partial m-tile per expert), so the real tiles are counted
+  // first and cut into 8 contiguous runs of near-equal length, run x on XCD x
+  // (cutting the whole grid instead left the last XCDs without work: 616 real
+  // tiles of 768 slots filled XCDs 0-5 and part of 6).
+  int64_t total = 0;
+  for (int e = 0; e < (int)p.E; ++e) total += (p.offsets[e + 1] - p.offsets[e] + BM - 1) / BM;
+  total *= tiles_n;
+  const int64_t q = total >> 3, rem = total & 7, slot = bid >> 3;
+  if (slot >= q + (xcd < rem ? 1 : 0)) return false;
+  const int64_t tg = xcd * q + min((int64_t)xcd, rem) + slot;
   int64_t base = 0, lo = 0, hi = 0, mt = 0;
   int e = 0;
   for (; e < (int)p.E; ++e) {
@@ -76,11 +86,11 @@ __device__ __forceinline__ bool tile_coord(const GemmArgs& p, TileCoord& tc) {
     hi = p.offsets[e + 1];
     mt = (hi - lo + BM - 1) / BM;
     const int64_t cnt = mt * tiles_n;
-    if (t < base + cnt) break;
+    if (tg < base + cnt) break;
     base += cnt;
   }
   if (e >= (int)p.E) return false;
-  const int64_t local = t - base;
+  const int64_t local = tg - base;
   tc.m0 = lo + (local % mt) * BM;
   tc.n0 = (int)(local / mt) * BN;
   tc.mend = hi;
