@@ -86,7 +86,12 @@ def test_gemm_argument_errors(lib):
     assert fp(A16, A16, A16, A16, 64, 128, 256, A16, 0, 132, None) == ALIGN  # 264-byte rows
     assert fp(A16 + 8, A16, A16, A16, 64, 128, 256, A16, 0, 128, None) == ALIGN
     assert fp(A16, A16, A16, A16, 0, 128, 256, None, 0, 128, None) == OK     # M = 0
+    kmax = 1024 * 128  # every chunk's block scale is kept in LDS
+    assert fp(A16, A16, A16, A16, 64, 128, kmax + 128, A16, 0, 128, None) == SHAPE
+    assert fp(A16, A16, A16, A16, 64, 256, kmax + 128, A16, 0, 256, None) == SHAPE
     dg = lib.fp8q_gemm_dgrad
+    assert dg(A16, A16, A16, A16, 64, kmax + 128, 256, A16, 0, 256, None) == SHAPE
+    assert lib.fp8q_gemm_wgrad(A16, A16, A16, A16, kmax + 128, 64, 256, A16, 256, 0, None) == SHAPE
     assert dg(A16, A16, A16, A16, 64, 200, 256, A16, 0, 256, None) == SHAPE  # contraction % 128
     wg = lib.fp8q_gemm_wgrad
     assert wg(A16, A16, A16, A16, 200, 64, 256, A16, 256, 0, None) == SHAPE  # T % 128

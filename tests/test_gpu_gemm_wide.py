@@ -147,3 +147,19 @@ def test_mx_tiles_agree(m, n, k, out):
         return fq.gemm_mx(aq, as_, bq, bs, c=gpu(base.clone()))
 
     _same_bits(run, f"mx {m}x{n}x{k}")
+
+
+def test_max_contraction_both_tiles():
+    """The longest contraction a GEMM accepts (1024 chunks of 128): both
+    tiles keep every chunk's block scales in LDS.  Bitwise agreement of the
+    two tiles, and sampled rows against the oracle."""
+    m, n, k = 300, 512, 1024 * 128
+    log(f"fprop {m}x{n}x{k}")
+    x, w, xq, xs, wq, ws, _ = _operands(m, n, k, seed=1234)
+    _same_bits(lambda: fq.gemm_fprop(xq, xs, wq, ws, out_dtype=torch.float32), "fprop max K")
+    rows = np.array([0, 1, 150, 255, 256, 299])
+    y = _with_tile("256x256", lambda: fq.gemm_fprop(xq, xs, wq, ws, out_dtype=torch.float32))
+    xo, xso = oracle.quant_act_1x128(f32(x[torch.from_numpy(rows)]))
+    wo, wso, _ = oracle.quant_weight_128x128(f32(w))
+    y_ref, s_ref = oracle.fprop_ref(xo, xso, wo, wso)
+    check_gemm(f32(y)[rows], y_ref, s_ref, False, "wide fprop max K", False, nk=k // 128)
