@@ -200,14 +200,16 @@ def make_mx_ops(L, dev):
 
 
 def time_ops(ops, steps, warmup, stream, flush=None):
-    """Run `warmup` untimed passes, then `steps` passes with HIP events around
-    every launch on `stream`; returns (ms per pass, per-kernel summaries).
+    """Run `warmup` untimed passes, then time `steps` passes back to back
+    (HIP events on `stream` before the first and after the last launch only),
+    then `steps` more passes with HIP events around every launch for the
+    per-kernel breakdown; returns (ms per pass, per-kernel summaries).
 
     flush: a callable run before every pass, outside the timed launches (a
     read of a buffer larger than the 256 MB MALL), for sections whose
     whole working set would otherwise stay cache-resident from pass to pass,
-    unlike in a training step.  The pass time is then the mean over passes of
-    first launch start to last launch end."""
+    unlike in a training step.  The pass time is then the mean over the
+    instrumented passes of first launch start to last launch end."""
     import torch
 
     for _ in range(warmup):
@@ -219,8 +221,19 @@ def time_ops(ops, steps, warmup, stream, flush=None):
     ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in ops]
           for _ in range(steps)]
     t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ms_pass = None
+    if not flush:
+        # the passes back to back, with no instrumentation between launches
+        torch.cuda.synchronize()
+        t_start.record(stream)
+        for s in range(steps):
+            for _, fn, _, _ in ops:
+                fn()
+        t_end.record(stream)
+        torch.cuda.synchronize()
+        ms_pass = t_start.elapsed_time(t_end) / steps
+    # the per-kernel breakdown: the same passes again, with HIP events around every launch
     torch.cuda.synchronize()
-    t_start.record(stream)
     for s in range(steps):
         if flush:
             flush()
@@ -228,12 +241,9 @@ def time_ops(ops, steps, warmup, stream, flush=None):
             ev[s][i][0].record(stream)
             fn()
             ev[s][i][1].record(stream)
-    t_end.record(stream)
     torch.cuda.synchronize()
     if flush:
         ms_pass = sum(ev[s][0][0].elapsed_time(ev[s][-1][1]) for s in range(steps)) / steps
-    else:
-        ms_pass = t_start.elapsed_time(t_end) / steps
     kernels = {}
     for i, (name, _, kind, work) in enumerate(ops):
         times = sorted(ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(steps))
