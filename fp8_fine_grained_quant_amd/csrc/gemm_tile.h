@@ -56,9 +56,14 @@ __device__ __forceinline__ bool tile_coord(const GemmArgs& p, TileCoord& tc) {
     const int tiles_m = (int)((p.M + BM - 1) / BM);
     const int per_ex = tiles_m * tiles_n;
     const int slots = (per_ex + 7) / 8;  // workgroups per expert per XCD
-    const int e = (bid >> 3) / slots;
-    if (e >= (int)p.E) return false;
-    const int tl = (bid >> 3) - e * slots;
+    const int ew = (bid >> 3) / slots;   // position in this XCD's walk over the experts
+    if (ew >= (int)p.E) return false;
+    const int tl = (bid >> 3) - ew * slots;
+    // each XCD starts its walk E/8 experts after the previous one, so that
+    // at any moment the XCDs work on different experts (some storing a small
+    // expert's gradient while others compute a large one's; measured 626 ->
+    // 618 us for the 32-expert weight gradient)
+    const int e = (int)((ew + (int64_t)xcd * ((p.E + 7) / 8)) % p.E);
     const int q = per_ex >> 3, r = per_ex & 7;
     if (tl >= q + (xcd < r ? 1 : 0)) return false;
     const int t = xcd * q + min(xcd, r) + tl;
