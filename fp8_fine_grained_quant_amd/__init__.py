@@ -18,13 +18,14 @@ tensors in place of pointer + leading dimension):
     fp8q_quant_mx_1x32(x, q, s)                        # microscaling variant
     fp8q_quant_mx_transpose(x, q_t, s_t, q=None, s=None)
     fp8q_gemm_mx(aq, as_, bq, bs, c, accumulate=False)
+    fp8q_grouped_gemm_mx(xq, xs, wq, ws, offsets, y)
 
 Each GEMM also takes exact=True, which calls the *_exact entry point (BF16
 matrix instruction on exactly converted codes: the exact-accumulation variant).
 
 Convenience wrappers that allocate the outputs: quant_act_1x128,
 quant_weight_128x128, quant_transpose, gemm_fprop, gemm_dgrad, gemm_wgrad,
-grouped_gemm, quant_mx, quant_mx_transpose, gemm_mx (and those of the MoE
+grouped_gemm, quant_mx, quant_mx_transpose, gemm_mx, grouped_gemm_mx (and those of the MoE
 backward and the dual-output quantizer).
 """
 
@@ -44,7 +45,7 @@ EXPORTS = ["fp8q_status_string", "fp8q_quant_act_1x128", "fp8q_quant_weight_128x
            "fp8q_grouped_gemm", "fp8q_gemm_fprop_exact", "fp8q_gemm_dgrad_exact", "fp8q_gemm_wgrad_exact",
            "fp8q_grouped_gemm_exact", "fp8q_quant_transpose_grouped", "fp8q_grouped_gemm_dgrad",
            "fp8q_grouped_gemm_wgrad", "fp8q_quant_act_transpose", "fp8q_quant_mx_1x32",
-           "fp8q_quant_mx_transpose", "fp8q_gemm_mx"]
+           "fp8q_quant_mx_transpose", "fp8q_gemm_mx", "fp8q_grouped_gemm_mx"]
 
 
 class Fp8qError(RuntimeError):
@@ -81,6 +82,7 @@ def load_library(path=LIB_PATH):
         "fp8q_quant_mx_1x32": ([P, I32, I64, I64, I64, P, I64, P, I64, P], I32),
         "fp8q_quant_mx_transpose": ([P, I32, I64, I64, I64, P, I64, P, I64, P, I64, P, I64, P], I32),
         "fp8q_gemm_mx": ([P, P, I64, I64, P, P, I64, I64, I64, I64, I64, P, I32, I64, I32, P], I32),
+        "fp8q_grouped_gemm_mx": ([P, P, P, P, P, I64, I64, I64, I64, P, I32, I64, P], I32),
     }
     for name in ["fp8q_gemm_fprop", "fp8q_gemm_dgrad", "fp8q_gemm_wgrad", "fp8q_grouped_gemm"]:
         sig[name + "_exact"] = sig[name]
@@ -302,6 +304,22 @@ def fp8q_gemm_mx(aq, as_, bq, bs, c, accumulate=False, stream=None):
            "fp8q_gemm_mx")
 
 
+def fp8q_grouped_gemm_mx(xq, xs, wq, ws, offsets, y, stream=None):
+    """Y [M_total, N] = per expert X rows . W_e^T; xq [M_total, K], xs [M_total, K/32],
+    wq [E, N, K], ws [E, N, K/32] (uint8 codes and E8M0 bytes, contiguous)."""
+    _on_gpu(xq, xs, wq, ws, offsets, y)
+    _contig(xq, xs, wq, ws, offsets)
+    if offsets.dtype != torch.int32:
+        raise TypeError("offsets are int32")
+    m_total, k = xq.shape
+    e, n, _ = wq.shape
+    if wq.shape[2] != k or tuple(xs.shape) != (m_total, k // 32) or tuple(ws.shape) != (e, n, k // 32):
+        raise ValueError("grouped MX operands: xq [M, K], xs [M, K/32], wq [E, N, K], ws [E, N, K/32]")
+    _check(load_library().fp8q_grouped_gemm_mx(_ptr(xq), _ptr(xs), _ptr(wq), _ptr(ws), _ptr(offsets), e, m_total,
+                                                n, k, _ptr(y), _dtype_code(y), _ld(y), _stream(stream)),
+           "fp8q_grouped_gemm_mx")
+
+
 # ---------------------------------------------------------------- convenience
 def _cdiv(a, b):
     return (a + b - 1) // b
@@ -429,3 +447,10 @@ def gemm_mx(aq, as_, bq, bs, out_dtype=torch.bfloat16, c=None, stream=None):
         c = torch.empty((aq.shape[0], bq.shape[0]), dtype=out_dtype, device=aq.device)
     fp8q_gemm_mx(aq, as_, bq, bs, c, accumulate, stream)
     return c
+
+
+def grouped_gemm_mx(xq, xs, wq, ws, offsets, out_dtype=torch.bfloat16, stream=None):
+    """Grouped (MoE) MX Fprop: rows [o_e, o_{e+1}) of the output are X[o_e:o_{e+1}] . W_e^T."""
+    y = torch.empty((xq.shape[0], wq.shape[1]), dtype=out_dtype, device=xq.device)
+    fp8q_grouped_gemm_mx(xq, xs, wq, ws, offsets, y, stream)
+    return y

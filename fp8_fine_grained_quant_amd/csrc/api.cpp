@@ -374,4 +374,30 @@ fp8q_status fp8q_gemm_mx(const uint8_t* aq, const uint8_t* as, int64_t lda, int6
   return launched(fp8q::launch_gemm_mx(a, stream));
 }
 
+fp8q_status fp8q_grouped_gemm_mx(const uint8_t* xq, const uint8_t* xs, const uint8_t* wq, const uint8_t* ws,
+                                 const int32_t* offsets, int64_t E, int64_t M_total, int64_t N, int64_t K, void* y,
+                                 fp8q_dtype yt, int64_t ld_y, hipStream_t stream) {
+  if (E < 1 || E > 65536) return FP8Q_ERR_SHAPE;
+  if (M_total < 0 || N < 0 || K < 0 || M_total > kMaxDim || N > kMaxDim || K > kMaxDim) return FP8Q_ERR_SHAPE;
+  if (N % 128 != 0 || K % 128 != 0 || K > kMaxContraction) return FP8Q_ERR_SHAPE;
+  if (!valid_dtype(yt)) return FP8Q_ERR_DTYPE;
+  if (M_total == 0 || N == 0) return FP8Q_OK;
+  if (K == 0) return FP8Q_ERR_SHAPE;
+  if (!xq || !xs || !wq || !ws || !offsets) return FP8Q_ERR_NULL;
+  const fp8q_status c = check_gemm_out(y, yt, ld_y, N);
+  if (c != FP8Q_OK) return c;
+  // scale rows are K/32 bytes, a multiple of 4 since K % 128 == 0
+  if (!aligned16(xq) || !aligned16(wq) || !aligned4(xs) || !aligned4(ws) || !aligned4(offsets))
+    return FP8Q_ERR_ALIGN;
+  if (((M_total + 255) / 256 + E) * (N / 128) > kMaxGroups) return FP8Q_ERR_SHAPE;
+  fp8q::MxArgs a{};
+  a.g.A = xq; a.g.B = wq; a.g.C = y;
+  a.g.lda = K; a.g.ldb = K; a.g.ldc = ld_y;
+  a.g.M = M_total; a.g.N = N; a.g.K = K;
+  a.g.out_f32 = yt == FP8Q_F32; a.g.accumulate = 0;
+  a.g.offsets = offsets; a.g.E = E; a.g.b_estride = N * K;
+  a.sa = xs; a.sb = ws; a.ld_sa = K / 32; a.ld_sb = K / 32; a.sb_estride = N * (K / 32);
+  return launched(fp8q::launch_gemm_mx(a, stream));
+}
+
 }  // extern "C"

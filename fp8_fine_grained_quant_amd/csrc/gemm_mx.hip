@@ -83,7 +83,10 @@ struct IC {
 
 }  // namespace
 
-template <int OUT_F32, bool SC4>
+// GROUPED: rows grouped by expert (g.offsets, g.E), tiles never straddle
+// experts, and expert e's B codes and scales start g.b_estride and
+// sb_estride bytes after expert e-1's.
+template <int OUT_F32, bool SC4, bool GROUPED>
 __global__ __launch_bounds__(kNT) void k_gemm_mx(MxArgs p) {
 #if defined(__HIP_DEVICE_COMPILE__)
   typedef MxStage<SC4> S;
@@ -95,7 +98,9 @@ __global__ __launch_bounds__(kNT) void k_gemm_mx(MxArgs p) {
 
   const GemmArgs& q = p.g;
   TileCoord tc;
-  tile_coord<kBM, kBN, false>(q, tc);
+  if (!tile_coord<kBM, kBN, GROUPED>(q, tc)) return;
+  const uint8_t* Bp = q.B + (GROUPED ? (int64_t)tc.e * q.b_estride : 0);
+  const uint8_t* sbp = p.sb + (GROUPED ? (int64_t)tc.e * p.sb_estride : 0);
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -106,9 +111,9 @@ __global__ __launch_bounds__(kNT) void k_gemm_mx(MxArgs p) {
   // Buffer ranges: A and its scales cover the tile's valid rows only (a row
   // past them reads nothing), B and its scales the tile's 128 rows.
   const __amdgpu_buffer_rsrc_t rA = make_rsrc(q.A + tc.m0 * q.lda, (uint32_t)(rows * q.lda));
-  const __amdgpu_buffer_rsrc_t rB = make_rsrc(q.B + (int64_t)tc.n0 * q.ldb, (uint32_t)(kBN * q.ldb));
+  const __amdgpu_buffer_rsrc_t rB = make_rsrc(Bp + (int64_t)tc.n0 * q.ldb, (uint32_t)(kBN * q.ldb));
   const __amdgpu_buffer_rsrc_t rSa = make_rsrc(p.sa + tc.m0 * p.ld_sa, (uint32_t)(rows * p.ld_sa));
-  const __amdgpu_buffer_rsrc_t rSb = make_rsrc(p.sb + (int64_t)tc.n0 * p.ld_sb, (uint32_t)(kBN * p.ld_sb));
+  const __amdgpu_buffer_rsrc_t rSb = make_rsrc(sbp + (int64_t)tc.n0 * p.ld_sb, (uint32_t)(kBN * p.ld_sb));
   // Wave w's d-th 16-byte load of a tile fills LDS bytes [(w*I + d)*1024, +1024):
   // rows (w*I + d)*8 + lane/8, physical piece lane%8 = logical piece (lane%8) ^ (row%8).
   const int r8 = lane >> 3, lc = (lane & 7) ^ r8;
@@ -499,11 +504,13 @@ __global__ __launch_bounds__(kWNT) void k_gemm_mx_wide(MxArgs p) {
 
 namespace {
 
-template <int OUT_F32, bool SC4>
+template <int OUT_F32, bool SC4, bool GROUPED = false>
 hipError_t launch_mx(const MxArgs& a, hipStream_t st) {
-  const int64_t tiles = ((a.g.M + kBM - 1) / kBM) * (a.g.N / kBN);
+  const int64_t tiles_m = (a.g.M + kBM - 1) / kBM, tiles_n = a.g.N / kBN;
+  // grouped: an upper bound (a partial m-tile per expert); the kernel counts the real tiles
+  const int64_t tiles = GROUPED ? (tiles_m + a.g.E) * tiles_n : tiles_m * tiles_n;
   if (tiles <= 0) return hipSuccess;
-  hipLaunchKernelGGL((k_gemm_mx<OUT_F32, SC4>), dim3((uint32_t)tiles), dim3(kNT), 0, st, a);
+  hipLaunchKernelGGL((k_gemm_mx<OUT_F32, SC4, GROUPED>), dim3((uint32_t)tiles), dim3(kNT), 0, st, a);
   return hipGetLastError();
 }
 
@@ -526,6 +533,10 @@ static bool use_wide_mx(const MxArgs& a) {
 
 hipError_t launch_gemm_mx(const MxArgs& a, hipStream_t st) {
   const bool sc4 = a.ld_sa % 16 == 0 && (reinterpret_cast<uintptr_t>(a.sa) & 15) == 0;
+  if (a.g.offsets != nullptr) {  // grouped rows: the 256 x 128 tile
+    if (sc4) return a.g.out_f32 ? launch_mx<1, true, true>(a, st) : launch_mx<0, true, true>(a, st);
+    return a.g.out_f32 ? launch_mx<1, false, true>(a, st) : launch_mx<0, false, true>(a, st);
+  }
   if (sc4 && use_wide_mx(a)) {
     const int64_t tiles = ((a.g.M + kBM - 1) / kBM) * (a.g.N / kWBN);
     if (tiles <= 0) return hipSuccess;

@@ -82,6 +82,7 @@ struct MxArgs {
   const uint8_t* sa;
   const uint8_t* sb;
   int64_t ld_sa, ld_sb;
+  int64_t sb_estride;  // grouped: bytes between experts' B scales (g.b_estride for the codes)
 };
 hipError_t launch_gemm_mx(const MxArgs& a, hipStream_t st);
 

@@ -341,6 +341,29 @@ fp8q_status fp8q_gemm_mx(const uint8_t* aq, const uint8_t* as, int64_t lda, int6
                          const uint8_t* bs, int64_t ldb, int64_t ld_sb, int64_t M, int64_t N, int64_t K, void* c,
                          fp8q_dtype ct, int64_t ld_c, int accumulate, hipStream_t stream);
 
+/*
+ * Grouped (MoE) MX Fprop: fp8q_gemm_mx per expert over grouped rows, as
+ * fp8q_grouped_gemm does for the FP32-scaled codes (the MoE layers' GEMMs
+ * run in FP8 like the dense ones, the innerforce.co.kr excerpt of the
+ * DeepSeek-V3 report, the FP8 framework paragraph; the expert layout is this
+ * library's own).  For every expert e, rows [o_e, o_{e+1}) of Y are
+ * X[o_e:o_{e+1}, :] . W_e^T, each product scaled by its two E8M0 scales.
+ *   xq : [M_total, K] codes,    xs : [M_total, K/32] E8M0 bytes (contiguous)
+ *   wq : [E, N, K] codes,       ws : [E, N, K/32] E8M0 bytes (contiguous)
+ *   offsets : DEVICE int32 [E+1], as for fp8q_grouped_gemm (never read on
+ *             the host; malformed offsets are undefined behaviour)
+ *   y  : [M_total, N] of type yt, row stride ld_y
+ * Each output element takes the same instructions in the same order as in
+ * fp8q_gemm_mx on that expert's rows, so the two agree bit for bit.
+ * Rules: K % 128 == 0, N % 128 == 0, K <= 131072, 1 <= E <= 65536, any
+ * M_total >= 0; xq, wq 16-byte aligned, xs, ws 4-byte aligned (16-byte
+ * aligned scale rows, i.e. K % 512 == 0, load faster).  Experts with no rows
+ * are skipped; no host synchronisation happens.
+ */
+fp8q_status fp8q_grouped_gemm_mx(const uint8_t* xq, const uint8_t* xs, const uint8_t* wq, const uint8_t* ws,
+                                 const int32_t* offsets, int64_t E, int64_t M_total, int64_t N, int64_t K, void* y,
+                                 fp8q_dtype yt, int64_t ld_y, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -146,6 +146,17 @@ def test_mx_argument_errors(lib):
     assert g(A16, A16 + 2, 256, 8, A16, A16, 256, 8, 64, 128, 256, A16, 0, 128, 0, None) == ALIGN
     assert g(A16, None, 256, 8, A16, A16, 256, 8, 64, 128, 256, A16, 0, 128, 0, None) == NULL
     assert g(A16, A16, 256, 8, A16, A16, 256, 8, 0, 128, 256, None, 0, 128, 0, None) == OK      # M = 0
+    gg = lib.fp8q_grouped_gemm_mx
+    #         xq   xs   wq   ws   off  E  M   N    K    y    yt ldy
+    assert gg(A16, A16, A16, A16, A16, 0, 64, 128, 256, A16, 0, 128, None) == SHAPE     # E = 0
+    assert gg(A16, A16, A16, A16, A16, 4, 64, 100, 256, A16, 0, 128, None) == SHAPE     # N % 128
+    assert gg(A16, A16, A16, A16, A16, 4, 64, 128, 200, A16, 0, 128, None) == SHAPE     # K % 128
+    assert gg(A16, A16, A16, A16, A16, 4, 64, 128, 1024 * 128 + 128, A16, 0, 128, None) == SHAPE  # K max
+    assert gg(A16, A16, A16, A16, A16, 4, 64, 128, 256, A16, 2, 128, None) == DTYPE
+    assert gg(A16, A16, A16, A16, None, 4, 64, 128, 256, A16, 0, 128, None) == NULL     # offsets
+    assert gg(A16 + 4, A16, A16, A16, A16, 4, 64, 128, 256, A16, 0, 128, None) == ALIGN  # codes 16-byte
+    assert gg(A16, A16 + 2, A16, A16, A16, 4, 64, 128, 256, A16, 0, 128, None) == ALIGN  # scales 4-byte
+    assert gg(None, None, None, None, None, 4, 0, 128, 256, None, 0, 128, None) == OK    # M_total = 0
 
 
 def test_binding_refuses_cpu_tensors():
