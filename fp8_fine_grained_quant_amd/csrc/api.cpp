@@ -208,7 +208,8 @@ static fp8q_status fp8q_grouped_gemm_impl(int exact, const uint8_t* xq, const fl
   if (c != FP8Q_OK) return c;
   if (!aligned16(xq) || !aligned16(wq) || !aligned4(xs) || !aligned4(ws) || !aligned4(offsets))
     return FP8Q_ERR_ALIGN;
-  if ((M_total / 256 + E) * (N / 128) > kMaxGroups) return FP8Q_ERR_SHAPE;
+  // the launch grid: a partial m-tile per expert on top of ceil(M_total / 256)
+  if (((M_total + 255) / 256 + E) * (N / 128) > kMaxGroups) return FP8Q_ERR_SHAPE;
   GemmArgs a{};
   a.A = xq; a.B = wq; a.sa = xs; a.sb = ws; a.C = y;
   a.lda = K; a.ldb = K; a.ld_sa = K / 128; a.sb_rs = K / 128; a.sb_cs = 1; a.ldc = ld_y;
@@ -235,7 +236,7 @@ fp8q_status fp8q_grouped_gemm_dgrad(const uint8_t* dyq, const float* dys, const 
   if (c != FP8Q_OK) return c;
   if (!aligned16(dyq) || !aligned16(wq_t) || !aligned4(dys) || !aligned4(ws) || !aligned4(offsets))
     return FP8Q_ERR_ALIGN;
-  if ((M_total / 256 + E) * (K / 128) > kMaxGroups) return FP8Q_ERR_SHAPE;
+  if (((M_total + 255) / 256 + E) * (K / 128) > kMaxGroups) return FP8Q_ERR_SHAPE;
   // Per expert: the Dgrad NT form (A = dY rows of the expert, contraction N)
   // with B = W_e^T = columns [eN, (e+1)N) of the stacked transposed codes
   // [K, E*N], and the block scale of (output column k, chunk kb) at

@@ -115,6 +115,11 @@ def test_grouped_backward_argument_errors(lib):
     assert gd(A16, A16, A16, A16, A16, 4, 64, 200, 256, A16, 0, 256, None) == SHAPE  # N % 128
     assert gd(A16, A16, A16, A16, None, 4, 64, 256, 256, A16, 0, 256, None) == NULL
     assert gd(A16, A16, A16, A16, A16, 0, 64, 256, 256, A16, 0, 256, None) == SHAPE  # E = 0
+    # launch grid (ceil(M_total / 256) + E) * (N / 128) one past 2^31 - 1: rejected before any launch
+    m_edge = 256 * 8388606 + 1
+    assert gd(A16, A16, A16, A16, A16, 1, m_edge, 128, 32768, A16, 0, 32768, None) == SHAPE
+    assert lib.fp8q_grouped_gemm(A16, A16, A16, A16, A16, 1, m_edge, 32768, 128, A16, 0, 32768, None) == SHAPE
+    assert lib.fp8q_grouped_gemm_mx(A16, A16, A16, A16, A16, 1, m_edge, 32768, 128, A16, 0, 32768, None) == SHAPE
     gw = lib.fp8q_grouped_gemm_wgrad
     assert gw(A16, A16, A16, A16, A16, 4, 300, 128, 256, 640, A16, 0, None) == STRIDE  # ld_t < 768
     assert gw(A16, A16, A16, A16, A16, 4, 300, 128, 256, 800, A16, 0, None) == ALIGN   # ld_t % 128
