@@ -142,6 +142,7 @@ static fp8q_status fp8q_gemm_fprop_impl(int exact, const uint8_t* xq, const floa
   const fp8q_status c = check_gemm_out(y, yt, ld_y, N);
   if (c != FP8Q_OK) return c;
   if (!aligned16(xq) || !aligned16(wq) || !aligned4(xs) || !aligned4(ws)) return FP8Q_ERR_ALIGN;
+  if (cdiv(M, 256) * (N / 128) > kMaxGroups) return FP8Q_ERR_SHAPE;  // the launch grid
   GemmArgs a{};
   a.A = xq; a.B = wq; a.sa = xs; a.sb = ws; a.C = y;
   a.lda = K; a.ldb = K; a.ld_sa = K / 128; a.sb_rs = K / 128; a.sb_cs = 1; a.ldc = ld_y;
@@ -162,6 +163,7 @@ static fp8q_status fp8q_gemm_dgrad_impl(int exact, const uint8_t* dyq, const flo
   const fp8q_status c = check_gemm_out(dx, dxt, ld_dx, K);
   if (c != FP8Q_OK) return c;
   if (!aligned16(dyq) || !aligned16(wq_t) || !aligned4(dys) || !aligned4(ws)) return FP8Q_ERR_ALIGN;
+  if (cdiv(M, 256) * (K / 128) > kMaxGroups) return FP8Q_ERR_SHAPE;  // the launch grid
   // NT form over the contraction axis N: A = dY [M, N], B = W^T codes [K, N];
   // the block scale of (output column k, chunk kb over N) is ws[kb, k/128].
   GemmArgs a{};
@@ -184,6 +186,7 @@ static fp8q_status fp8q_gemm_wgrad_impl(int exact, const uint8_t* dyq_t, const f
   const fp8q_status c = check_gemm_out(dw, FP8Q_F32, ld_dw, K);
   if (c != FP8Q_OK) return c;
   if (!aligned16(dyq_t) || !aligned16(xq_t) || !aligned4(dys_t) || !aligned4(xs_t)) return FP8Q_ERR_ALIGN;
+  if (cdiv(N, 256) * (K / 128) > kMaxGroups) return FP8Q_ERR_SHAPE;  // the launch grid
   // NT form over the tokens: A = dY^T codes [N, T], B = X^T codes [K, T], one
   // scale per row of each per 128 tokens.
   GemmArgs a{};
@@ -366,6 +369,7 @@ fp8q_status fp8q_gemm_mx(const uint8_t* aq, const uint8_t* as, int64_t lda, int6
   if (!aligned4(as) || !aligned4(bs) || ld_sa % 4 != 0 || ld_sb % 4 != 0) return FP8Q_ERR_ALIGN;
   // the kernel's buffer descriptors address one tile's rows with 32-bit offsets
   if (256 * lda > INT32_MAX || 128 * ldb > INT32_MAX) return FP8Q_ERR_SHAPE;
+  if (cdiv(M, 256) * (N / 128) > kMaxGroups) return FP8Q_ERR_SHAPE;  // the launch grid
   fp8q::MxArgs a{};
   a.g.A = aq; a.g.B = bq; a.g.C = c;
   a.g.lda = lda; a.g.ldb = ldb; a.g.ldc = ld_c;

@@ -86,6 +86,13 @@ def test_gemm_argument_errors(lib):
     assert fp(A16, A16, A16, A16, 64, 128, 256, A16, 0, 132, None) == ALIGN  # 264-byte rows
     assert fp(A16 + 8, A16, A16, A16, 64, 128, 256, A16, 0, 128, None) == ALIGN
     assert fp(A16, A16, A16, A16, 0, 128, 256, None, 0, 128, None) == OK     # M = 0
+    # outputs whose launch grid (ceil(rows / 256) x cols / 128 tiles) exceeds 2^31 - 1: rejected on the host
+    big_m, big_n = (1 << 31) - 1, (1 << 31) - 128
+    assert fp(A16, A16, A16, A16, big_m, big_n, 128, A16, 0, big_n, None) == SHAPE
+    assert lib.fp8q_gemm_dgrad(A16, A16, A16, A16, big_m, 128, big_n, A16, 0, big_n, None) == SHAPE
+    assert lib.fp8q_gemm_wgrad(A16, A16, A16, A16, 128, big_m, big_n, A16, big_n, 0, None) == SHAPE
+    assert lib.fp8q_gemm_mx(A16, A16, 128, 4, A16, A16, 128, 4, big_m, big_n, 128, A16, 0, big_n, 0,
+                            None) == SHAPE
     kmax = 1024 * 128  # every chunk's block scale is kept in LDS
     assert fp(A16, A16, A16, A16, 64, 128, kmax + 128, A16, 0, 128, None) == SHAPE
     assert fp(A16, A16, A16, A16, 64, 256, kmax + 128, A16, 0, 256, None) == SHAPE
