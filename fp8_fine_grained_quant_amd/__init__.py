@@ -19,13 +19,14 @@ tensors in place of pointer + leading dimension):
     fp8q_quant_mx_transpose(x, q_t, s_t, q=None, s=None)
     fp8q_gemm_mx(aq, as_, bq, bs, c, accumulate=False)
     fp8q_grouped_gemm_mx(xq, xs, wq, ws, offsets, y)
+    fp8q_grouped_gemm_mx_dgrad(dyq, dys, wq_t, ws_t, offsets, dx)
 
 Each GEMM also takes exact=True, which calls the *_exact entry point (BF16
 matrix instruction on exactly converted codes: the exact-accumulation variant).
 
 Convenience wrappers that allocate the outputs: quant_act_1x128,
 quant_weight_128x128, quant_transpose, gemm_fprop, gemm_dgrad, gemm_wgrad,
-grouped_gemm, quant_mx, quant_mx_transpose, gemm_mx, grouped_gemm_mx (and those of the MoE
+grouped_gemm, quant_mx, quant_mx_transpose, gemm_mx, grouped_gemm_mx, grouped_gemm_mx_dgrad (and those of the MoE
 backward and the dual-output quantizer).
 """
 
@@ -45,7 +46,8 @@ EXPORTS = ["fp8q_status_string", "fp8q_quant_act_1x128", "fp8q_quant_weight_128x
            "fp8q_grouped_gemm", "fp8q_gemm_fprop_exact", "fp8q_gemm_dgrad_exact", "fp8q_gemm_wgrad_exact",
            "fp8q_grouped_gemm_exact", "fp8q_quant_transpose_grouped", "fp8q_grouped_gemm_dgrad",
            "fp8q_grouped_gemm_wgrad", "fp8q_quant_act_transpose", "fp8q_quant_mx_1x32",
-           "fp8q_quant_mx_transpose", "fp8q_gemm_mx", "fp8q_grouped_gemm_mx"]
+           "fp8q_quant_mx_transpose", "fp8q_gemm_mx", "fp8q_grouped_gemm_mx",
+           "fp8q_grouped_gemm_mx_dgrad"]
 
 
 class Fp8qError(RuntimeError):
@@ -83,6 +85,7 @@ def load_library(path=LIB_PATH):
         "fp8q_quant_mx_transpose": ([P, I32, I64, I64, I64, P, I64, P, I64, P, I64, P, I64, P], I32),
         "fp8q_gemm_mx": ([P, P, I64, I64, P, P, I64, I64, I64, I64, I64, P, I32, I64, I32, P], I32),
         "fp8q_grouped_gemm_mx": ([P, P, P, P, P, I64, I64, I64, I64, P, I32, I64, P], I32),
+        "fp8q_grouped_gemm_mx_dgrad": ([P, P, P, P, P, I64, I64, I64, I64, P, I32, I64, P], I32),
     }
     for name in ["fp8q_gemm_fprop", "fp8q_gemm_dgrad", "fp8q_gemm_wgrad", "fp8q_grouped_gemm"]:
         sig[name + "_exact"] = sig[name]
@@ -320,6 +323,24 @@ def fp8q_grouped_gemm_mx(xq, xs, wq, ws, offsets, y, stream=None):
            "fp8q_grouped_gemm_mx")
 
 
+def fp8q_grouped_gemm_mx_dgrad(dyq, dys, wq_t, ws_t, offsets, dx, stream=None):
+    """dX [M_total, K] = per expert dY rows . W_e; dyq [M_total, N], dys [M_total, N/32],
+    wq_t [K, E*N], ws_t [K, E*N/32] (quant_mx_transpose of the stacked weights [E*N, K])."""
+    _on_gpu(dyq, dys, wq_t, ws_t, offsets, dx)
+    _contig(dyq, dys, wq_t, ws_t, offsets)
+    if offsets.dtype != torch.int32:
+        raise TypeError("offsets are int32")
+    m_total, n = dyq.shape
+    k, en = wq_t.shape
+    e = offsets.shape[0] - 1
+    if en != e * n or tuple(dys.shape) != (m_total, n // 32) or tuple(ws_t.shape) != (k, en // 32):
+        raise ValueError("grouped MX Dgrad operands: dyq [M, N], dys [M, N/32], wq_t [K, E*N], ws_t [K, E*N/32]")
+    _check(load_library().fp8q_grouped_gemm_mx_dgrad(_ptr(dyq), _ptr(dys), _ptr(wq_t), _ptr(ws_t), _ptr(offsets), e,
+                                                      m_total, n, k, _ptr(dx), _dtype_code(dx), _ld(dx),
+                                                      _stream(stream)),
+           "fp8q_grouped_gemm_mx_dgrad")
+
+
 # ---------------------------------------------------------------- convenience
 def _cdiv(a, b):
     return (a + b - 1) // b
@@ -454,3 +475,10 @@ def grouped_gemm_mx(xq, xs, wq, ws, offsets, out_dtype=torch.bfloat16, stream=No
     y = torch.empty((xq.shape[0], wq.shape[1]), dtype=out_dtype, device=xq.device)
     fp8q_grouped_gemm_mx(xq, xs, wq, ws, offsets, y, stream)
     return y
+
+
+def grouped_gemm_mx_dgrad(dyq, dys, wq_t, ws_t, offsets, out_dtype=torch.bfloat16, stream=None):
+    """Grouped (MoE) MX Dgrad: rows [o_e, o_{e+1}) of dX are dY[o_e:o_{e+1}] . W_e."""
+    dx = torch.empty((dyq.shape[0], wq_t.shape[0]), dtype=out_dtype, device=dyq.device)
+    fp8q_grouped_gemm_mx_dgrad(dyq, dys, wq_t, ws_t, offsets, dx, stream)
+    return dx

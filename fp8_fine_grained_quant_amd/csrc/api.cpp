@@ -405,4 +405,34 @@ fp8q_status fp8q_grouped_gemm_mx(const uint8_t* xq, const uint8_t* xs, const uin
   return launched(fp8q::launch_gemm_mx(a, stream));
 }
 
+fp8q_status fp8q_grouped_gemm_mx_dgrad(const uint8_t* dyq, const uint8_t* dys, const uint8_t* wq_t,
+                                       const uint8_t* ws_t, const int32_t* offsets, int64_t E, int64_t M_total,
+                                       int64_t N, int64_t K, void* dx, fp8q_dtype dxt, int64_t ld_dx,
+                                       hipStream_t stream) {
+  if (E < 1 || E > 65536) return FP8Q_ERR_SHAPE;
+  if (M_total < 0 || N < 0 || K < 0 || M_total > kMaxDim || N > kMaxDim || K > kMaxDim) return FP8Q_ERR_SHAPE;
+  if (N % 128 != 0 || K % 128 != 0 || N > kMaxContraction) return FP8Q_ERR_SHAPE;
+  // the kernel addresses 128 rows of the stacked transposed codes (E*N bytes each) with 32-bit offsets
+  if (E * N > INT32_MAX / 128) return FP8Q_ERR_SHAPE;
+  if (!valid_dtype(dxt)) return FP8Q_ERR_DTYPE;
+  if (M_total == 0 || K == 0) return FP8Q_OK;
+  if (N == 0) return FP8Q_ERR_SHAPE;
+  if (!dyq || !dys || !wq_t || !ws_t || !offsets) return FP8Q_ERR_NULL;
+  const fp8q_status c = check_gemm_out(dx, dxt, ld_dx, K);
+  if (c != FP8Q_OK) return c;
+  if (!aligned16(dyq) || !aligned16(wq_t) || !aligned4(dys) || !aligned4(ws_t) || !aligned4(offsets))
+    return FP8Q_ERR_ALIGN;
+  if (((M_total + 255) / 256 + E) * (K / 128) > kMaxGroups) return FP8Q_ERR_SHAPE;
+  // Per expert: C = dY rows . B^T with B = W_e^T = columns [eN, (e+1)N) of
+  // the stacked transposed codes (row stride E*N) and of their scales (E*N/32)
+  fp8q::MxArgs a{};
+  a.g.A = dyq; a.g.B = wq_t; a.g.C = dx;
+  a.g.lda = N; a.g.ldb = E * N; a.g.ldc = ld_dx;
+  a.g.M = M_total; a.g.N = K; a.g.K = N;
+  a.g.out_f32 = dxt == FP8Q_F32; a.g.accumulate = 0;
+  a.g.offsets = offsets; a.g.E = E; a.g.b_estride = N;
+  a.sa = dys; a.sb = ws_t; a.ld_sa = N / 32; a.ld_sb = E * N / 32; a.sb_estride = N / 32;
+  return launched(fp8q::launch_gemm_mx(a, stream));
+}
+
 }  // extern "C"

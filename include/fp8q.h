@@ -364,6 +364,30 @@ fp8q_status fp8q_grouped_gemm_mx(const uint8_t* xq, const uint8_t* xs, const uin
                                  const int32_t* offsets, int64_t E, int64_t M_total, int64_t N, int64_t K, void* y,
                                  fp8q_dtype yt, int64_t ld_y, hipStream_t stream);
 
+/*
+ * Grouped (MoE) MX Dgrad: for every expert e, rows [o_e, o_{e+1}) of dX are
+ * dY[o_e:o_{e+1}, :] . W_e, as fp8q_grouped_gemm_dgrad with E8M0 block
+ * scales (the MoE backward's input gradient, "DeepSeek FP8 Training",
+ * input-gradient list; the expert layout is this library's own).
+ *   dyq  : [M_total, N] codes, dys : [M_total, N/32] E8M0 bytes
+ *          (fp8q_quant_mx_1x32 of dY; contiguous)
+ *   wq_t : [K, E*N] codes, ws_t : [K, E*N/32] E8M0 bytes: the q_t / s_t of
+ *          fp8q_quant_mx_transpose on the stacked weights [E*N, K]
+ *          (contiguous); W_e^T is columns [eN, (e+1)N) of both (N % 32 == 0,
+ *          so no scale block mixes two experts)
+ *   offsets : DEVICE int32 [E+1], as for fp8q_grouped_gemm
+ *   dx   : [M_total, K] of type dxt, row stride ld_dx
+ * Each output element takes the same instructions in the same order as
+ * fp8q_gemm_mx on that expert's rows with B = the expert's columns of wq_t.
+ * Rules: N % 128 == 0, K % 128 == 0, N <= 131072, 1 <= E <= 65536,
+ * E*N <= 2^31 / 128, any M_total >= 0; dyq, wq_t 16-byte aligned, dys, ws_t
+ * 4-byte aligned.  Experts with no rows are skipped.
+ */
+fp8q_status fp8q_grouped_gemm_mx_dgrad(const uint8_t* dyq, const uint8_t* dys, const uint8_t* wq_t,
+                                       const uint8_t* ws_t, const int32_t* offsets, int64_t E, int64_t M_total,
+                                       int64_t N, int64_t K, void* dx, fp8q_dtype dxt, int64_t ld_dx,
+                                       hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -169,6 +169,16 @@ def test_mx_argument_errors(lib):
     assert gg(A16 + 4, A16, A16, A16, A16, 4, 64, 128, 256, A16, 0, 128, None) == ALIGN  # codes 16-byte
     assert gg(A16, A16 + 2, A16, A16, A16, 4, 64, 128, 256, A16, 0, 128, None) == ALIGN  # scales 4-byte
     assert gg(None, None, None, None, None, 4, 0, 128, 256, None, 0, 128, None) == OK    # M_total = 0
+    gd = lib.fp8q_grouped_gemm_mx_dgrad
+    #         dyq  dys  wq_t ws_t off  E  M   N    K    dx   t  ldx
+    assert gd(A16, A16, A16, A16, A16, 0, 64, 128, 256, A16, 0, 256, None) == SHAPE     # E = 0
+    assert gd(A16, A16, A16, A16, A16, 4, 64, 200, 256, A16, 0, 256, None) == SHAPE     # N % 128
+    assert gd(A16, A16, A16, A16, A16, 4, 64, 128, 200, A16, 0, 256, None) == SHAPE     # K % 128
+    assert gd(A16, A16, A16, A16, A16, 65536, 64, 1 << 15, 256, A16, 0, 256, None) == SHAPE  # E*N too large
+    assert gd(A16, A16, A16, A16, A16, 4, 64, 128, 256, A16, 0, 128, None) == STRIDE    # ld_dx < K
+    assert gd(A16, A16, None, A16, A16, 4, 64, 128, 256, A16, 0, 256, None) == NULL
+    assert gd(A16, A16, A16, A16 + 1, A16, 4, 64, 128, 256, A16, 0, 256, None) == ALIGN
+    assert gd(None, None, None, None, None, 4, 0, 128, 256, None, 0, 256, None) == OK    # M_total = 0
 
 
 def test_binding_refuses_cpu_tensors():
