@@ -123,7 +123,7 @@ __global__ __launch_bounds__(kNT) void k_gemm_mx(MxArgs p) {
   // A scales: lane (w, l) fetches row 64w + l (clamped to a valid row).
   // B scales: lane L = 64w + l (mod 128) fetches tile row 16*(L%8) + L/8 into
   // word L, so the words land as [l16][j] and a lane reads its 8 columns'
-  // words with two 16-byte LDS reads (waves 2, 3 fill spare words).
+  // words with two 16-byte LDS reads (waves 2, 3 load nothing into spare words).
   const uint32_t voffSa = (uint32_t)(min(w * 64 + lane, rows - 1) * p.ld_sa);
   const int Lb = (w * 64 + lane) & (kBN - 1);
   const uint32_t voffSb = (uint32_t)((16 * (Lb & 7) + (Lb >> 3)) * p.ld_sb);
@@ -151,7 +151,10 @@ __global__ __launch_bounds__(kNT) void k_gemm_mx(MxArgs p) {
                                                  0, 0);
       }
     } else {
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rSb, (lds_ptr)(st + S::sb + w * 256), 4, voffSb, (uint32_t)kb * 4, 0,
+      // waves 2, 3: an out-of-range load (no memory access) into the spare
+      // words, which keeps every wave's load count per chunk
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rSb, (lds_ptr)(st + S::sb + w * 256), 4, voffSb,
+                                               w < 2 ? (uint32_t)kb * 4 : 0x40000000u, 0,
                                                0);
     }
   };
@@ -348,7 +351,7 @@ __global__ __launch_bounds__(kWNT) void k_gemm_mx_wide(MxArgs p) {
   // A scales: lane (w, l), w < 4, fetches row 64w + l (clamped to a valid
   // row).  B scales: lane L = 64w + l (L < 256, w < 4) fetches the word of
   // column 128 (L / 128) + 16 ((L % 128) % 8) + (L % 128) / 8 into word L, so
-  // each half's words land as [l16][j]; waves 4-7 write a spare copy.
+  // each half's words land as [l16][j]; waves 4-7 load nothing into a spare copy.
   const uint32_t voffSa = (uint32_t)(min(wr * 64 + lane, rows - 1) * p.ld_sa);
   const int Lb = (w * 64 + lane) & (kWBN - 1), Lh = Lb & 127;
   const uint32_t voffSb = (uint32_t)((128 * (Lb >> 7) + 16 * (Lh & 7) + (Lh >> 3)) * p.ld_sb);
@@ -369,7 +372,10 @@ __global__ __launch_bounds__(kWNT) void k_gemm_mx_wide(MxArgs p) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, (lds_ptr)(br + (w * kWIB + qq) * 1024), 16, voffB + qq * stepB,
                                                (uint32_t)kb * kBK, 0, 0);
     else
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rSb, (lds_ptr)(br + RB + w * 256), 4, voffSb, (uint32_t)kb * 4, 0, 0);
+      // waves 4-7: an out-of-range load (no memory access) into the spare
+      // copy, which keeps every wave's load count per chunk
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rSb, (lds_ptr)(br + RB + w * 256), 4, voffSb,
+                                               w < 4 ? (uint32_t)kb * 4 : 0x40000000u, 0, 0);
   };
   constexpr int kWaitA = 0x0F70 | kWDmaA;
 
