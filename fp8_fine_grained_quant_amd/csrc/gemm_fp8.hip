@@ -166,7 +166,7 @@ __global__ __launch_bounds__(kNT) void k_gemm_fp8(GemmArgs p) {
   const uint32_t voffB = (uint32_t)((w * kIB * 8 + r8) * p.ldb + 16 * lc);
   const uint32_t stepA = (uint32_t)(8 * p.lda), stepB = (uint32_t)(8 * p.ldb);
   // scales: lane (w, l) fetches row 64w + l (clamped to a valid row) and, in
-  // row mode, column (64w + l) % 128 (waves 2, 3 fill spare slots)
+  // row mode, column 64w + l for w < 2 (waves 2, 3 load nothing into spare slots)
   const uint32_t voffSa = (uint32_t)(min(w * 64 + lane, rows - 1) * p.ld_sa * 4);
   const uint32_t voffSb = (uint32_t)(((w * 64 + lane) & (kBN - 1)) * p.sb_rs * 4);
 
@@ -197,8 +197,10 @@ __global__ __launch_bounds__(kNT) void k_gemm_fp8(GemmArgs p) {
                                                  0, 0);
       }
     } else {
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rSb, (lds_ptr)(st + S::sb + w * 256), 4, voffSb, (uint32_t)kb * 4, 0,
-                                               0);
+      // waves 2, 3 keep the load count with an out-of-range load (no memory
+      // access) into the spare slots
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rSb, (lds_ptr)(st + S::sb + w * 256), 4, voffSb,
+                                               w < 2 ? (uint32_t)kb * 4 : 0x40000000u, 0, 0);
     }
   };
   auto issue = [&](int kb, uint8_t* st) {
@@ -705,8 +707,8 @@ __global__ __launch_bounds__(kWNT) void k_gemm_fp8_wide_row(GemmArgs p) {
   const uint32_t voffA = (uint32_t)((w * kWIA * 8 + r8) * p.lda + 16 * lc);
   const uint32_t voffB = (uint32_t)((w * kWIB * 8 + r8) * p.ldb + 16 * lc);
   const uint32_t stepA = (uint32_t)(8 * p.lda), stepB = (uint32_t)(8 * p.ldb);
-  // lane (w, l): row scale of row 64 (w % 4) + l (clamped to a valid row),
-  // column scale of column 64 w + l (mod 256)
+  // lane (w, l), w < 4: row scale of row 64 w + l (clamped to a valid row),
+  // column scale of column 64 w + l (waves 4-7 load nothing)
   const uint32_t voffSa = (uint32_t)(min(wr * 64 + lane, rows - 1) * p.ld_sa * 4);
   const uint32_t voffSb = (uint32_t)(((w * 64 + lane) & (kWBN - 1)) * p.sb_rs * 4);
 
@@ -716,7 +718,10 @@ __global__ __launch_bounds__(kWNT) void k_gemm_fp8_wide_row(GemmArgs p) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, (lds_ptr)(ar + (w * kWIA + d) * 1024), 16, voffA + d * stepA,
                                                (uint32_t)kb * kBK, 0, 0);
     else
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rSa, (lds_ptr)(ar + RA + w * 256), 4, voffSa, (uint32_t)kb * 4, 0, 0);
+      // waves 4-7 keep the load count with an out-of-range load (no memory
+      // access) into the second KB, which nothing reads
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rSa, (lds_ptr)(ar + RA + w * 256), 4, voffSa,
+                                               w < 4 ? (uint32_t)kb * 4 : 0x40000000u, 0, 0);
   };
   auto issue_b = [&](int kb, uint8_t* br, int q) {
     kb += cb;
@@ -724,7 +729,8 @@ __global__ __launch_bounds__(kWNT) void k_gemm_fp8_wide_row(GemmArgs p) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, (lds_ptr)(br + (w * kWIB + q) * 1024), 16, voffB + q * stepB,
                                                (uint32_t)kb * kBK, 0, 0);
     else
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rSb, (lds_ptr)(br + RB + w * 256), 4, voffSb, (uint32_t)kb * 4, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rSb, (lds_ptr)(br + RB + w * 256), 4, voffSb,
+                                               w < 4 ? (uint32_t)kb * 4 : 0x40000000u, 0, 0);
   };
   constexpr int kDmaB = kWIB + 1;
   constexpr int kWaitA = 0x0F70 | kWDmaA;
