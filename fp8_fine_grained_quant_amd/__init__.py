@@ -41,7 +41,7 @@ LIB_PATH = os.path.join(_HERE, "libfp8q.so")
 FP8Q_BF16, FP8Q_F32 = 0, 1
 _STATUS = ["FP8Q_OK", "FP8Q_ERR_NULL", "FP8Q_ERR_SHAPE", "FP8Q_ERR_STRIDE",
            "FP8Q_ERR_ALIGN", "FP8Q_ERR_DTYPE", "FP8Q_ERR_LAUNCH"]
-EXPORTS = ["fp8q_status_string", "fp8q_quant_act_1x128", "fp8q_quant_weight_128x128",
+EXPORTS = ["fp8q_status_string", "fp8q_set_gemm_tile", "fp8q_quant_act_1x128", "fp8q_quant_weight_128x128",
            "fp8q_quant_transpose", "fp8q_gemm_fprop", "fp8q_gemm_dgrad", "fp8q_gemm_wgrad",
            "fp8q_grouped_gemm", "fp8q_gemm_fprop_exact", "fp8q_gemm_dgrad_exact", "fp8q_gemm_wgrad_exact",
            "fp8q_grouped_gemm_exact", "fp8q_quant_transpose_grouped", "fp8q_grouped_gemm_dgrad",
@@ -70,6 +70,7 @@ def load_library(path=LIB_PATH):
     P, I64, I32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
     sig = {
         "fp8q_status_string": ([I32], ctypes.c_char_p),
+        "fp8q_set_gemm_tile": ([I32], I32),
         "fp8q_quant_act_1x128": ([P, I32, I64, I64, I64, P, I64, P, I64, P], I32),
         "fp8q_quant_weight_128x128": ([P, I32, I64, I64, I64, P, I64, P, I64, P, I64, P], I32),
         "fp8q_quant_transpose": ([P, I32, I64, I64, I64, P, I64, P, I64, P], I32),
@@ -101,6 +102,15 @@ def status_string(status):
     return load_library().fp8q_status_string(int(status)).decode()
 
 
+_TILES = {"auto": 0, "256x128": 1, "256x256": 2}
+
+
+def set_gemm_tile(tile):
+    """Force the GEMMs' workgroup tile ("256x128", "256x256") or give the
+    choice back to the library ("auto"); results are bit-identical."""
+    _check(load_library().fp8q_set_gemm_tile(_TILES[tile]), "fp8q_set_gemm_tile")
+
+
 # ----------------------------------------------------------------- marshalling
 def _stream(stream):
     if stream is None:
@@ -127,6 +137,26 @@ def _dtype_code(t):
     raise TypeError(f"unsupported dtype {t.dtype}")
 
 
+def _expect(t, shape, dtype, what):
+    """Shape and dtype of an operand the library will read or write through a
+    raw pointer: a mismatch would make a kernel run past the allocation, so it
+    is refused here (shape entries: an int, None for any, or ("min", n) for at
+    least n)."""
+    if t is None:
+        raise ValueError(f"{what} is required")
+    if t.dtype != dtype:
+        raise TypeError(f"{what}: dtype {t.dtype}, expected {dtype}")
+    if t.dim() != len(shape):
+        raise ValueError(f"{what}: {t.dim()}-D, expected {len(shape)}-D {shape}")
+    for got, want in zip(t.shape, shape):
+        ok = want is None or (got >= want[1] if isinstance(want, tuple) else got == want)
+        if not ok:
+            raise ValueError(f"{what}: shape {tuple(t.shape)}, expected {shape}")
+
+
+_U8, _F32 = torch.uint8, torch.float32
+
+
 def _check(status, name):
     if status != 0:
         raise Fp8qError(status, name)
@@ -139,16 +169,22 @@ def _on_gpu(*ts):
 
 
 def fp8q_quant_act_1x128(x, q, scale, stream=None):
-    _on_gpu(x, q, scale)
     rows, cols = x.shape
+    _expect(q, (rows, cols), _U8, "q")
+    _expect(scale, (rows, _cdiv(cols, 128)), _F32, "scale")
+    _on_gpu(x, q, scale)
     _check(load_library().fp8q_quant_act_1x128(_ptr(x), _dtype_code(x), rows, cols, _ld(x), _ptr(q), _ld(q),
                                                 _ptr(scale), _ld(scale), _stream(stream)),
            "fp8q_quant_act_1x128")
 
 
 def fp8q_quant_weight_128x128(w, q, q_t, scale, stream=None):
-    _on_gpu(w, q, q_t, scale)
     rows, cols = w.shape
+    _expect(q, (rows, cols), _U8, "q")
+    if q_t is not None:
+        _expect(q_t, (cols, rows), _U8, "q_t")
+    _expect(scale, (_cdiv(rows, 128), _cdiv(cols, 128)), _F32, "scale")
+    _on_gpu(w, q, q_t, scale)
     ld_qt = _ld(q_t) if q_t is not None else 0
     _check(load_library().fp8q_quant_weight_128x128(_ptr(w), _dtype_code(w), rows, cols, _ld(w), _ptr(q),
                                                      _ld(q), _ptr(q_t), ld_qt, _ptr(scale), _ld(scale),
@@ -157,8 +193,10 @@ def fp8q_quant_weight_128x128(w, q, q_t, scale, stream=None):
 
 
 def fp8q_quant_transpose(x, q_t, scale_t, stream=None):
-    _on_gpu(x, q_t, scale_t)
     rows, cols = x.shape
+    _expect(q_t, (cols, rows), _U8, "q_t")
+    _expect(scale_t, (cols, _cdiv(rows, 128)), _F32, "scale_t")
+    _on_gpu(x, q_t, scale_t)
     _check(load_library().fp8q_quant_transpose(_ptr(x), _dtype_code(x), rows, cols, _ld(x), _ptr(q_t),
                                                 _ld(q_t), _ptr(scale_t), _ld(scale_t), _stream(stream)),
            "fp8q_quant_transpose")
@@ -175,52 +213,73 @@ def _contig(*ts):
 
 
 def fp8q_gemm_fprop(xq, xs, wq, ws, y, stream=None, exact=False):
-    _on_gpu(xq, xs, wq, ws, y)
-    _contig(xq, xs, wq, ws)
     m, k = xq.shape
     n = wq.shape[0]
+    _expect(xq, (m, k), _U8, "xq")
+    _expect(xs, (m, _cdiv(k, 128)), _F32, "xs")
+    _expect(wq, (n, k), _U8, "wq")
+    _expect(ws, (_cdiv(n, 128), _cdiv(k, 128)), _F32, "ws")
+    _expect(y, (m, n), y.dtype, "y")
+    _on_gpu(xq, xs, wq, ws, y)
+    _contig(xq, xs, wq, ws)
     _check(_fn("fp8q_gemm_fprop", exact)(_ptr(xq), _ptr(xs), _ptr(wq), _ptr(ws), m, n, k, _ptr(y),
                                            _dtype_code(y), _ld(y), _stream(stream)),
            "fp8q_gemm_fprop")
 
 
 def fp8q_gemm_dgrad(dyq, dys, wq_t, ws, dx, stream=None, exact=False):
-    _on_gpu(dyq, dys, wq_t, ws, dx)
-    _contig(dyq, dys, wq_t, ws)
     m, n = dyq.shape
     k = wq_t.shape[0]
+    _expect(dyq, (m, n), _U8, "dyq")
+    _expect(dys, (m, _cdiv(n, 128)), _F32, "dys")
+    _expect(wq_t, (k, n), _U8, "wq_t")
+    _expect(ws, (_cdiv(n, 128), _cdiv(k, 128)), _F32, "ws")
+    _expect(dx, (m, k), dx.dtype, "dx")
+    _on_gpu(dyq, dys, wq_t, ws, dx)
+    _contig(dyq, dys, wq_t, ws)
     _check(_fn("fp8q_gemm_dgrad", exact)(_ptr(dyq), _ptr(dys), _ptr(wq_t), _ptr(ws), m, n, k, _ptr(dx),
                                            _dtype_code(dx), _ld(dx), _stream(stream)),
            "fp8q_gemm_dgrad")
 
 
 def fp8q_gemm_wgrad(dyq_t, dys_t, xq_t, xs_t, dw, accumulate=False, stream=None, exact=False):
-    _on_gpu(dyq_t, dys_t, xq_t, xs_t, dw)
-    _contig(dyq_t, dys_t, xq_t, xs_t)
     n, t = dyq_t.shape
     k = xq_t.shape[0]
-    if dw.dtype != torch.float32:
-        raise TypeError("dW is FP32")
+    _expect(dyq_t, (n, t), _U8, "dyq_t")
+    _expect(dys_t, (n, _cdiv(t, 128)), _F32, "dys_t")
+    _expect(xq_t, (k, t), _U8, "xq_t")
+    _expect(xs_t, (k, _cdiv(t, 128)), _F32, "xs_t")
+    _expect(dw, (n, k), _F32, "dw")
+    _on_gpu(dyq_t, dys_t, xq_t, xs_t, dw)
+    _contig(dyq_t, dys_t, xq_t, xs_t)
     _check(_fn("fp8q_gemm_wgrad", exact)(_ptr(dyq_t), _ptr(dys_t), _ptr(xq_t), _ptr(xs_t), t, n, k, _ptr(dw),
                                            _ld(dw), int(bool(accumulate)), _stream(stream)),
            "fp8q_gemm_wgrad")
 
 
 def fp8q_grouped_gemm(xq, xs, wq, ws, offsets, y, stream=None, exact=False):
-    _on_gpu(xq, xs, wq, ws, offsets, y)
-    _contig(xq, xs, wq, ws, offsets)
-    if offsets.dtype != torch.int32:
-        raise TypeError("offsets are int32")
     m_total, k = xq.shape
     e, n, _ = wq.shape
+    _expect(xq, (m_total, k), _U8, "xq")
+    _expect(xs, (m_total, _cdiv(k, 128)), _F32, "xs")
+    _expect(wq, (e, n, k), _U8, "wq")
+    _expect(ws, (e, _cdiv(n, 128), _cdiv(k, 128)), _F32, "ws")
+    _expect(offsets, (e + 1,), torch.int32, "offsets")
+    _expect(y, (m_total, n), y.dtype, "y")
+    _on_gpu(xq, xs, wq, ws, offsets, y)
+    _contig(xq, xs, wq, ws, offsets)
     _check(_fn("fp8q_grouped_gemm", exact)(_ptr(xq), _ptr(xs), _ptr(wq), _ptr(ws), _ptr(offsets), e, m_total,
                                              n, k, _ptr(y), _dtype_code(y), _ld(y), _stream(stream)),
            "fp8q_grouped_gemm")
 
 
 def fp8q_quant_act_transpose(x, q, scale, q_t, scale_t, stream=None):
-    _on_gpu(x, q, scale, q_t, scale_t)
     rows, cols = x.shape
+    _expect(q, (rows, cols), _U8, "q")
+    _expect(scale, (rows, _cdiv(cols, 128)), _F32, "scale")
+    _expect(q_t, (cols, rows), _U8, "q_t")
+    _expect(scale_t, (cols, _cdiv(rows, 128)), _F32, "scale_t")
+    _on_gpu(x, q, scale, q_t, scale_t)
     _check(load_library().fp8q_quant_act_transpose(_ptr(x), _dtype_code(x), rows, cols, _ld(x), _ptr(q), _ld(q),
                                                     _ptr(scale), _ld(scale), _ptr(q_t), _ld(q_t), _ptr(scale_t),
                                                     _ld(scale_t), _stream(stream)),
@@ -228,12 +287,14 @@ def fp8q_quant_act_transpose(x, q, scale, q_t, scale_t, stream=None):
 
 
 def fp8q_quant_transpose_grouped(x, offsets, q_t, scale_t, stream=None):
-    _on_gpu(x, offsets, q_t, scale_t)
-    _contig(offsets)
-    if offsets.dtype != torch.int32:
-        raise TypeError("offsets are int32")
     rows, cols = x.shape
     e = offsets.shape[0] - 1
+    cap = token_capacity(rows, e)
+    _expect(offsets, (e + 1,), torch.int32, "offsets")
+    _expect(q_t, (cols, ("min", cap)), _U8, "q_t")
+    _expect(scale_t, (cols, ("min", cap // 128)), _F32, "scale_t")
+    _on_gpu(x, offsets, q_t, scale_t)
+    _contig(offsets)
     _check(load_library().fp8q_quant_transpose_grouped(_ptr(x), _dtype_code(x), rows, cols, _ld(x),
                                                         _ptr(offsets), e, _ptr(q_t), _ld(q_t), _ptr(scale_t),
                                                         _ld(scale_t), _stream(stream)),
@@ -243,13 +304,17 @@ def fp8q_quant_transpose_grouped(x, offsets, q_t, scale_t, stream=None):
 def fp8q_grouped_gemm_dgrad(dyq, dys, wq_t, ws, offsets, dx, stream=None):
     """wq_t [K, E*N], ws [E*N/128, K/128] (quant_weight_128x128 of the stacked
     weights [E*N, K])."""
-    _on_gpu(dyq, dys, wq_t, ws, offsets, dx)
-    _contig(dyq, dys, wq_t, ws, offsets)
-    if offsets.dtype != torch.int32:
-        raise TypeError("offsets are int32")
     m_total, n = dyq.shape
     k = wq_t.shape[0]
     e = offsets.shape[0] - 1
+    _expect(offsets, (e + 1,), torch.int32, "offsets")
+    _expect(dyq, (m_total, n), _U8, "dyq")
+    _expect(dys, (m_total, _cdiv(n, 128)), _F32, "dys")
+    _expect(wq_t, (k, e * n), _U8, "wq_t")
+    _expect(ws, (_cdiv(e * n, 128), _cdiv(k, 128)), _F32, "ws")
+    _expect(dx, (m_total, k), dx.dtype, "dx")
+    _on_gpu(dyq, dys, wq_t, ws, offsets, dx)
+    _contig(dyq, dys, wq_t, ws, offsets)
     _check(load_library().fp8q_grouped_gemm_dgrad(_ptr(dyq), _ptr(dys), _ptr(wq_t), _ptr(ws), _ptr(offsets), e,
                                                    m_total, n, k, _ptr(dx), _dtype_code(dx), _ld(dx),
                                                    _stream(stream)),
@@ -259,15 +324,19 @@ def fp8q_grouped_gemm_dgrad(dyq, dys, wq_t, ws, offsets, dx, stream=None):
 def fp8q_grouped_gemm_wgrad(dyq_t, dys_t, xq_t, xs_t, offsets, m_total, dw, accumulate=False, stream=None):
     """Token-padded operands [N, ld_t] / [K, ld_t] (quant_transpose_grouped);
     dw [E, N, K] FP32 contiguous."""
-    _on_gpu(dyq_t, dys_t, xq_t, xs_t, offsets, dw)
-    _contig(dyq_t, dys_t, xq_t, xs_t, offsets, dw)
-    if offsets.dtype != torch.int32 or dw.dtype != torch.float32:
-        raise TypeError("offsets are int32 and dW is FP32")
     n, ld_t = dyq_t.shape
     k = xq_t.shape[0]
     e = offsets.shape[0] - 1
-    if xq_t.shape[1] != ld_t or dys_t.shape[1] * 128 != ld_t or xs_t.shape[1] * 128 != ld_t:
-        raise ValueError("the four operands share one padded token stride")
+    _expect(offsets, (e + 1,), torch.int32, "offsets")
+    _expect(dyq_t, (n, ld_t), _U8, "dyq_t")
+    _expect(dys_t, (n, ld_t // 128), _F32, "dys_t")
+    _expect(xq_t, (k, ld_t), _U8, "xq_t")
+    _expect(xs_t, (k, ld_t // 128), _F32, "xs_t")
+    _expect(dw, (e, n, k), _F32, "dw")
+    if ld_t % 128 != 0:
+        raise ValueError("the padded token stride is a multiple of 128")
+    _on_gpu(dyq_t, dys_t, xq_t, xs_t, offsets, dw)
+    _contig(dyq_t, dys_t, xq_t, xs_t, offsets, dw)
     _check(load_library().fp8q_grouped_gemm_wgrad(_ptr(dyq_t), _ptr(dys_t), _ptr(xq_t), _ptr(xs_t), _ptr(offsets),
                                                    e, m_total, n, k, ld_t, _ptr(dw), int(bool(accumulate)),
                                                    _stream(stream)),
@@ -275,16 +344,23 @@ def fp8q_grouped_gemm_wgrad(dyq_t, dys_t, xq_t, xs_t, offsets, m_total, dw, accu
 
 
 def fp8q_quant_mx_1x32(x, q, s, stream=None):
-    _on_gpu(x, q, s)
     rows, cols = x.shape
+    _expect(q, (rows, cols), _U8, "q")
+    _expect(s, (rows, _cdiv(cols, 32)), _U8, "s")
+    _on_gpu(x, q, s)
     _check(load_library().fp8q_quant_mx_1x32(_ptr(x), _dtype_code(x), rows, cols, _ld(x), _ptr(q), _ld(q),
                                               _ptr(s), _ld(s), _stream(stream)),
            "fp8q_quant_mx_1x32")
 
 
 def fp8q_quant_mx_transpose(x, q_t, s_t, q=None, s=None, stream=None):
-    _on_gpu(x, q_t, s_t, q, s)
     rows, cols = x.shape
+    _expect(q_t, (cols, rows), _U8, "q_t")
+    _expect(s_t, (cols, _cdiv(rows, 32)), _U8, "s_t")
+    if q is not None or s is not None:
+        _expect(q, (rows, cols), _U8, "q")
+        _expect(s, (rows, _cdiv(cols, 32)), _U8, "s")
+    _on_gpu(x, q_t, s_t, q, s)
     ldq = _ld(q) if q is not None else 0
     lds = _ld(s) if s is not None else 0
     _check(load_library().fp8q_quant_mx_transpose(_ptr(x), _dtype_code(x), rows, cols, _ld(x), _ptr(q_t),
@@ -296,11 +372,14 @@ def fp8q_quant_mx_transpose(x, q_t, s_t, q=None, s=None, stream=None):
 def fp8q_gemm_mx(aq, as_, bq, bs, c, accumulate=False, stream=None):
     """C [M, N] (= or +=) A . B^T; aq [M, K], as_ [M, >= K/32], bq [N, K],
     bs [N, >= K/32] (uint8 codes and E8M0 bytes, rows may be padded)."""
-    _on_gpu(aq, as_, bq, bs, c)
     m, k = aq.shape
     n = bq.shape[0]
-    if bq.shape[1] != k:
-        raise ValueError("A and B share the contraction length")
+    _expect(aq, (m, k), _U8, "aq")
+    _expect(as_, (m, ("min", _cdiv(k, 32))), _U8, "as_")
+    _expect(bq, (n, k), _U8, "bq")
+    _expect(bs, (n, ("min", _cdiv(k, 32))), _U8, "bs")
+    _expect(c, (m, n), c.dtype, "c")
+    _on_gpu(aq, as_, bq, bs, c)
     _check(load_library().fp8q_gemm_mx(_ptr(aq), _ptr(as_), _ld(aq), _ld(as_), _ptr(bq), _ptr(bs), _ld(bq),
                                         _ld(bs), m, n, k, _ptr(c), _dtype_code(c), _ld(c), int(bool(accumulate)),
                                         _stream(stream)),
@@ -310,14 +389,16 @@ def fp8q_gemm_mx(aq, as_, bq, bs, c, accumulate=False, stream=None):
 def fp8q_grouped_gemm_mx(xq, xs, wq, ws, offsets, y, stream=None):
     """Y [M_total, N] = per expert X rows . W_e^T; xq [M_total, K], xs [M_total, K/32],
     wq [E, N, K], ws [E, N, K/32] (uint8 codes and E8M0 bytes, contiguous)."""
-    _on_gpu(xq, xs, wq, ws, offsets, y)
-    _contig(xq, xs, wq, ws, offsets)
-    if offsets.dtype != torch.int32:
-        raise TypeError("offsets are int32")
     m_total, k = xq.shape
     e, n, _ = wq.shape
-    if wq.shape[2] != k or tuple(xs.shape) != (m_total, k // 32) or tuple(ws.shape) != (e, n, k // 32):
-        raise ValueError("grouped MX operands: xq [M, K], xs [M, K/32], wq [E, N, K], ws [E, N, K/32]")
+    _expect(xq, (m_total, k), _U8, "xq")
+    _expect(xs, (m_total, _cdiv(k, 32)), _U8, "xs")
+    _expect(wq, (e, n, k), _U8, "wq")
+    _expect(ws, (e, n, _cdiv(k, 32)), _U8, "ws")
+    _expect(offsets, (e + 1,), torch.int32, "offsets")
+    _expect(y, (m_total, n), y.dtype, "y")
+    _on_gpu(xq, xs, wq, ws, offsets, y)
+    _contig(xq, xs, wq, ws, offsets)
     _check(load_library().fp8q_grouped_gemm_mx(_ptr(xq), _ptr(xs), _ptr(wq), _ptr(ws), _ptr(offsets), e, m_total,
                                                 n, k, _ptr(y), _dtype_code(y), _ld(y), _stream(stream)),
            "fp8q_grouped_gemm_mx")
@@ -326,15 +407,17 @@ def fp8q_grouped_gemm_mx(xq, xs, wq, ws, offsets, y, stream=None):
 def fp8q_grouped_gemm_mx_dgrad(dyq, dys, wq_t, ws_t, offsets, dx, stream=None):
     """dX [M_total, K] = per expert dY rows . W_e; dyq [M_total, N], dys [M_total, N/32],
     wq_t [K, E*N], ws_t [K, E*N/32] (quant_mx_transpose of the stacked weights [E*N, K])."""
+    m_total, n = dyq.shape
+    k = wq_t.shape[0]
+    e = offsets.shape[0] - 1
+    _expect(offsets, (e + 1,), torch.int32, "offsets")
+    _expect(dyq, (m_total, n), _U8, "dyq")
+    _expect(dys, (m_total, _cdiv(n, 32)), _U8, "dys")
+    _expect(wq_t, (k, e * n), _U8, "wq_t")
+    _expect(ws_t, (k, _cdiv(e * n, 32)), _U8, "ws_t")
+    _expect(dx, (m_total, k), dx.dtype, "dx")
     _on_gpu(dyq, dys, wq_t, ws_t, offsets, dx)
     _contig(dyq, dys, wq_t, ws_t, offsets)
-    if offsets.dtype != torch.int32:
-        raise TypeError("offsets are int32")
-    m_total, n = dyq.shape
-    k, en = wq_t.shape
-    e = offsets.shape[0] - 1
-    if en != e * n or tuple(dys.shape) != (m_total, n // 32) or tuple(ws_t.shape) != (k, en // 32):
-        raise ValueError("grouped MX Dgrad operands: dyq [M, N], dys [M, N/32], wq_t [K, E*N], ws_t [K, E*N/32]")
     _check(load_library().fp8q_grouped_gemm_mx_dgrad(_ptr(dyq), _ptr(dys), _ptr(wq_t), _ptr(ws_t), _ptr(offsets), e,
                                                       m_total, n, k, _ptr(dx), _dtype_code(dx), _ld(dx),
                                                       _stream(stream)),

@@ -6,7 +6,30 @@
 #include "../../include/fp8q.h"
 #include "launch.h"
 
+#include <atomic>
 #include <stdint.h>
+
+namespace fp8q {
+
+namespace {
+std::atomic<int> g_gemm_tile{0};  // fp8q_set_gemm_tile
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cus[kMaxDevices];  // compute units per device, 0 = not yet queried
+}  // namespace
+
+int gemm_tile_setting() { return g_gemm_tile.load(std::memory_order_relaxed); }
+
+int device_cu_count() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+  cus = g_cus[dev].load(std::memory_order_relaxed);
+  if (cus > 0) return cus;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+  g_cus[dev].store(cus, std::memory_order_relaxed);
+  return cus;
+}
+
+}  // namespace fp8q
 
 namespace {
 
@@ -50,6 +73,12 @@ fp8q_status check_gemm_out(const void* y, fp8q_dtype yt, int64_t ld_y, int64_t n
 }  // namespace
 
 extern "C" {
+
+fp8q_status fp8q_set_gemm_tile(int tile) {
+  if (tile < 0 || tile > 2) return FP8Q_ERR_SHAPE;
+  fp8q::g_gemm_tile.store(tile, std::memory_order_relaxed);
+  return FP8Q_OK;
+}
 
 const char* fp8q_status_string(fp8q_status s) {
   switch (s) {
@@ -230,7 +259,10 @@ fp8q_status fp8q_grouped_gemm_dgrad(const uint8_t* dyq, const float* dys, const 
                                     void* dx, fp8q_dtype dxt, int64_t ld_dx, hipStream_t stream) {
   if (E < 1 || E > 65536) return FP8Q_ERR_SHAPE;
   if (M_total < 0 || N < 0 || K < 0 || M_total > kMaxDim || N > kMaxDim || K > kMaxDim) return FP8Q_ERR_SHAPE;
-  if (N % 128 != 0 || K % 128 != 0 || N > kMaxContraction || E * N > kMaxDim) return FP8Q_ERR_SHAPE;
+  if (N % 128 != 0 || K % 128 != 0 || N > kMaxContraction) return FP8Q_ERR_SHAPE;
+  // the kernels address 256 rows of the stacked transposed codes (E*N bytes
+  // each) with 32-bit buffer offsets
+  if (E * N > INT32_MAX / 256) return FP8Q_ERR_SHAPE;
   if (!valid_dtype(dxt)) return FP8Q_ERR_DTYPE;
   if (M_total == 0 || K == 0) return FP8Q_OK;
   if (N == 0) return FP8Q_ERR_SHAPE;
@@ -266,6 +298,8 @@ fp8q_status fp8q_grouped_gemm_wgrad(const uint8_t* dyq_t, const float* dys_t, co
   const int64_t cap = 128 * (M_total / 128 + E);
   if (ld_t < cap) return FP8Q_ERR_STRIDE;
   if (ld_t % 128 != 0) return FP8Q_ERR_ALIGN;
+  // the kernels address 256 operand rows (ld_t bytes each) with 32-bit buffer offsets
+  if (ld_t > INT32_MAX / 256) return FP8Q_ERR_SHAPE;
   if (!aligned16(dyq_t) || !aligned16(xq_t) || !aligned16(dw) || !aligned4(dys_t) || !aligned4(xs_t) ||
       !aligned4(offsets))
     return FP8Q_ERR_ALIGN;

@@ -11,6 +11,14 @@ namespace fp8q {
 constexpr float kFp8Max = 448.0f;
 constexpr float kAmaxFloor = 7.8886090522101181e-31f;  // 2^-100, exact in FP32
 
+// A buffer-load vector offset at or above the range of every buffer
+// descriptor built here (all ranges are below 2^31 bytes).  The range check
+// of a raw buffer access covers the vector offset plus the instruction
+// offset, so such a load performs no memory access and returns zeros; the
+// GEMMs use it for loads that only keep every wave's load count per chunk
+// equal.
+constexpr uint32_t kNoAccess = 0x80000000u;
+
 __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
 
 // FP32 -> BF16 bits, round to nearest even (finite inputs).

@@ -43,9 +43,6 @@
 // the 16-row slice, bytes [16g, 16g+16) and [64+16g, 64+16g+16) of the chunk,
 // g = l/16.  Result: lane l holds C[4g + r][l%16], r = 0..3.
 
-#include <stdlib.h>
-#include <string.h>
-
 #include "device_common.h"
 #include "gemm_tile.h"
 #include "launch.h"
@@ -190,8 +187,8 @@ __global__ __launch_bounds__(kNT) void k_gemm_fp8(GemmArgs p) {
         // load (no memory access) that keeps the count per chunk
         const bool real = (kb & 3) == 0 || kb == cb;
         uint8_t* dst = real ? reinterpret_cast<uint8_t*>(scA) + ((kb >> 2) & 1) * 4096 + w * 1024 : dmy;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rSa, (lds_ptr)dst, 16, voffSa,
-                                                 real ? (uint32_t)(kb & ~3) * 4 : 0x40000000u, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rSa, (lds_ptr)dst, 16, real ? voffSa : kNoAccess,
+                                                 real ? (uint32_t)(kb & ~3) * 4 : 0u, 0, 0);
       } else {
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rSa, (lds_ptr)(st + S::sa + w * 256), 4, voffSa, (uint32_t)kb * 4,
                                                  0, 0);
@@ -199,8 +196,8 @@ __global__ __launch_bounds__(kNT) void k_gemm_fp8(GemmArgs p) {
     } else {
       // waves 2, 3 keep the load count with an out-of-range load (no memory
       // access) into the spare slots
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rSb, (lds_ptr)(st + S::sb + w * 256), 4, voffSb,
-                                               w < 2 ? (uint32_t)kb * 4 : 0x40000000u, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rSb, (lds_ptr)(st + S::sb + w * 256), 4, w < 2 ? voffSb : kNoAccess,
+                                               w < 2 ? (uint32_t)kb * 4 : 0u, 0, 0);
     }
   };
   auto issue = [&](int kb, uint8_t* st) {
@@ -489,7 +486,7 @@ __global__ __launch_bounds__(kWNT) void k_gemm_fp8_wide(GemmArgs p) {
     } else {
       const bool real = w < 4 && (kb & 3) == 0;
       uint8_t* dst = real ? reinterpret_cast<uint8_t*>(scA) + ((kb >> 2) & 1) * 4096 + w * 1024 : dmy;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rSa, (lds_ptr)dst, 16, voffSa, real ? (uint32_t)kb * 4 : 0x40000000u,
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rSa, (lds_ptr)dst, 16, real ? voffSa : kNoAccess, real ? (uint32_t)kb * 4 : 0u,
                                                0, 0);
     }
   };
@@ -720,8 +717,8 @@ __global__ __launch_bounds__(kWNT) void k_gemm_fp8_wide_row(GemmArgs p) {
     else
       // waves 4-7 keep the load count with an out-of-range load (no memory
       // access) into the second KB, which nothing reads
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rSa, (lds_ptr)(ar + RA + w * 256), 4, voffSa,
-                                               w < 4 ? (uint32_t)kb * 4 : 0x40000000u, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rSa, (lds_ptr)(ar + RA + w * 256), 4, w < 4 ? voffSa : kNoAccess,
+                                               w < 4 ? (uint32_t)kb * 4 : 0u, 0, 0);
   };
   auto issue_b = [&](int kb, uint8_t* br, int q) {
     kb += cb;
@@ -729,8 +726,8 @@ __global__ __launch_bounds__(kWNT) void k_gemm_fp8_wide_row(GemmArgs p) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, (lds_ptr)(br + (w * kWIB + q) * 1024), 16, voffB + q * stepB,
                                                (uint32_t)kb * kBK, 0, 0);
     else
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rSb, (lds_ptr)(br + RB + w * 256), 4, voffSb,
-                                               w < 4 ? (uint32_t)kb * 4 : 0x40000000u, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rSb, (lds_ptr)(br + RB + w * 256), 4, w < 4 ? voffSb : kNoAccess,
+                                               w < 4 ? (uint32_t)kb * 4 : 0u, 0, 0);
   };
   constexpr int kDmaB = kWIB + 1;
   constexpr int kWaitA = 0x0F70 | kWDmaA;
@@ -897,21 +894,15 @@ hipError_t launch_one(const GemmArgs& a, hipStream_t st) {
 // the time of a 256 x 128 one (measured) for twice the work, so it wins
 // whenever it makes more than one tile per two compute units: below that the
 // 256 x 128 grid also finishes in one round and keeps every unit busy.
-// Grouped launches estimate the tile count from the total rows.  The
-// environment variable FP8Q_GEMM_TILE = "256x128" or "256x256" overrides the
-// choice (both tiles give bit-identical results), for tests and measurement.
+// Grouped launches estimate the tile count from the total rows.
+// fp8q_set_gemm_tile forces either tile (both give bit-identical results),
+// for tests and measurement.
 static bool use_wide_tile(const GemmArgs& a) {
   if (a.N % kWBN != 0) return false;
-  if (const char* f = getenv("FP8Q_GEMM_TILE")) {
-    if (!strcmp(f, "256x128")) return false;
-    if (!strcmp(f, "256x256")) return true;
-  }
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-    cus = 256;
+  const int forced = gemm_tile_setting();
+  if (forced != 0) return forced == 2;
   const int64_t tiles = ((a.M + kBM - 1) / kBM) * (a.N / kWBN);
-  return 2 * tiles > cus;
+  return 2 * tiles > device_cu_count();
 }
 
 hipError_t launch_gemm_fp8(const GemmArgs& a, hipStream_t st) {

@@ -30,9 +30,6 @@
 // therefore passes byte g of the row's 4-byte scale word of the chunk,
 // shifted down to bits [7:0] (operand select 0).
 
-#include <stdlib.h>
-#include <string.h>
-
 #include "device_common.h"
 #include "gemm_tile.h"
 #include "launch.h"
@@ -144,8 +141,8 @@ __global__ __launch_bounds__(kNT) void k_gemm_mx(MxArgs p) {
         // load (no memory access) that keeps the per-chunk load count
         const bool real = (kb & 3) == 0;
         uint8_t* dst = real ? reinterpret_cast<uint8_t*>(scA) + ((kb >> 2) & 1) * 4096 + w * 1024 : dmy;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rSa, (lds_ptr)dst, 16, voffSa,
-                                                 real ? (uint32_t)kb * 4 : 0x40000000u, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rSa, (lds_ptr)dst, 16, real ? voffSa : kNoAccess,
+                                                 real ? (uint32_t)kb * 4 : 0u, 0, 0);
       } else {
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rSa, (lds_ptr)(st + S::sa + w * 256), 4, voffSa, (uint32_t)kb * 4,
                                                  0, 0);
@@ -153,8 +150,8 @@ __global__ __launch_bounds__(kNT) void k_gemm_mx(MxArgs p) {
     } else {
       // waves 2, 3: an out-of-range load (no memory access) into the spare
       // words, which keeps every wave's load count per chunk
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rSb, (lds_ptr)(st + S::sb + w * 256), 4, voffSb,
-                                               w < 2 ? (uint32_t)kb * 4 : 0x40000000u, 0,
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rSb, (lds_ptr)(st + S::sb + w * 256), 4, w < 2 ? voffSb : kNoAccess,
+                                               w < 2 ? (uint32_t)kb * 4 : 0u, 0,
                                                0);
     }
   };
@@ -363,7 +360,7 @@ __global__ __launch_bounds__(kWNT) void k_gemm_mx_wide(MxArgs p) {
     } else {
       const bool real = w < 4 && (kb & 3) == 0;
       uint8_t* dst = real ? reinterpret_cast<uint8_t*>(scA) + ((kb >> 2) & 1) * 4096 + w * 1024 : dmy;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rSa, (lds_ptr)dst, 16, voffSa, real ? (uint32_t)kb * 4 : 0x40000000u,
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rSa, (lds_ptr)dst, 16, real ? voffSa : kNoAccess, real ? (uint32_t)kb * 4 : 0u,
                                                0, 0);
     }
   };
@@ -374,8 +371,8 @@ __global__ __launch_bounds__(kWNT) void k_gemm_mx_wide(MxArgs p) {
     else
       // waves 4-7: an out-of-range load (no memory access) into the spare
       // copy, which keeps every wave's load count per chunk
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rSb, (lds_ptr)(br + RB + w * 256), 4, voffSb,
-                                               w < 4 ? (uint32_t)kb * 4 : 0x40000000u, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rSb, (lds_ptr)(br + RB + w * 256), 4, w < 4 ? voffSb : kNoAccess,
+                                               w < 4 ? (uint32_t)kb * 4 : 0u, 0, 0);
   };
   constexpr int kWaitA = 0x0F70 | kWDmaA;
 
@@ -523,18 +520,12 @@ hipError_t launch_mx(const MxArgs& a, hipStream_t st) {
 }  // namespace
 
 // The 256 x 256 tile when its grid has more tiles than half the compute
-// units (the rule and the FP8Q_GEMM_TILE override of the FP8 GEMM).
+// units (the rule and the fp8q_set_gemm_tile setting of the FP8 GEMM).
 static bool use_wide_mx(const MxArgs& a) {
   if (a.g.N % kWBN != 0) return false;
-  if (const char* f = getenv("FP8Q_GEMM_TILE")) {
-    if (!strcmp(f, "256x128")) return false;
-    if (!strcmp(f, "256x256")) return true;
-  }
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-    cus = 256;
-  return 2 * ((a.g.M + kBM - 1) / kBM) * (a.g.N / kWBN) > cus;
+  const int forced = gemm_tile_setting();
+  if (forced != 0) return forced == 2;
+  return 2 * ((a.g.M + kBM - 1) / kBM) * (a.g.N / kWBN) > device_cu_count();
 }
 
 hipError_t launch_gemm_mx(const MxArgs& a, hipStream_t st) {

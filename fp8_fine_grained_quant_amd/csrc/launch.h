@@ -61,6 +61,13 @@ struct GemmArgs {
 };
 
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t st);
+
+// Workgroup tile of the block-scaled GEMMs: 0 = chosen by problem size,
+// 1 = 256 x 128, 2 = 256 x 256 (fp8q_set_gemm_tile; both tiles give the same
+// result bits).
+int gemm_tile_setting();
+// Compute units of the current device, queried once per device.
+int device_cu_count();
 // the FP8 matrix-instruction kernel (a.exact == 0)
 hipError_t launch_gemm_fp8(const GemmArgs& a, hipStream_t st);
 

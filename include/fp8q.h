@@ -35,7 +35,8 @@
  * Conventions of every entry point:
  *   - All pointers are DEVICE pointers owned by the caller.  The library
  *     allocates nothing, keeps no pointer after returning and has no global
- *     state: calls are re-entrant and thread-safe.  Buffers must stay valid
+ *     state beyond the tile setting of fp8q_set_gemm_tile: calls are
+ *     re-entrant and thread-safe.  Buffers must stay valid
  *     until the work enqueued on `stream` has completed.
  *   - Work is enqueued asynchronously on `stream` (NULL = the default
  *     stream).  Results are deterministic (no atomics, no split-K).
@@ -43,9 +44,8 @@
  *     problem size (the wide one when its grid has more tiles than half the
  *     device's compute units and the output width is a multiple of 256).
  *     Both run the same arithmetic in the same order, so the choice never
- *     changes a result bit.  The environment variable FP8Q_GEMM_TILE =
- *     "256x128" or "256x256" overrides the choice (read at each call), for
- *     tests and measurement.
+ *     changes a result bit.  fp8q_set_gemm_tile (below) forces either tile
+ *     for tests and measurement.
  *   - Arguments are validated on the host before anything is enqueued; a bad
  *     argument returns its status and enqueues nothing.  A zero-size call is
  *     a no-op returning FP8Q_OK.  A launch failure reported by the HIP runtime
@@ -84,6 +84,14 @@ typedef enum { FP8Q_BF16 = 0, FP8Q_F32 = 1 } fp8q_dtype;
 
 /* Human-readable name of a status code (static storage, never NULL). */
 const char* fp8q_status_string(fp8q_status s);
+
+/* Process-wide choice of the GEMMs' workgroup tile, for tests and
+ * measurement: 0 = by problem size (the default), 1 = 256x128, 2 = 256x256
+ * where the output width allows it.  The tiles give bit-identical results, so
+ * this changes timing only.  It is the library's one piece of state: calls on
+ * other threads see the new value from their next launch.  Returns
+ * FP8Q_ERR_SHAPE (and changes nothing) for any other value. */
+fp8q_status fp8q_set_gemm_tile(int tile);
 
 /*
  * 1x128 activation quantization ("unified E4M3" page, "Fine-Grained
@@ -233,7 +241,9 @@ fp8q_status fp8q_quant_transpose_grouped(const void* x, fp8q_dtype xt, int64_t r
  *          stacked weights [E*N, K]; W_e^T is columns [eN, (e+1)N)
  *   ws   : the SAME [E*N/128, K/128] scale array of that call
  *   dx   : [M_total, K] of type dxt, row stride ld_dx (rules as fp8q_gemm_dgrad)
- * Rules: N % 128 == 0, K % 128 == 0, 1 <= E <= 65536, E*N < 2^31.
+ * Rules: N % 128 == 0, K % 128 == 0, 1 <= E <= 65536, E*N <= (2^31-1)/256
+ * (the kernels address 256 rows of wq_t with 32-bit offsets), else
+ * FP8Q_ERR_SHAPE.
  */
 fp8q_status fp8q_grouped_gemm_dgrad(const uint8_t* dyq, const float* dys, const uint8_t* wq_t, const float* ws,
                                     const int32_t* offsets, int64_t E, int64_t M_total, int64_t N, int64_t K,
@@ -249,7 +259,9 @@ fp8q_status fp8q_grouped_gemm_dgrad(const uint8_t* dyq, const float* dys, const 
  *   ld_t : the padded token stride of all four, ld_t >= cap, ld_t % 128 == 0
  *   dw   : [E, N, K] FP32, contiguous; an expert with no tokens gets 0
  *          (accumulate = 0) or is left unchanged (accumulate = 1)
- * Rules: K % 128 == 0, any N >= 0, M_total <= 131072, 1 <= E <= 65536.
+ * Rules: K % 128 == 0, any N >= 0, M_total <= 131072, 1 <= E <= 65536,
+ * ld_t <= (2^31-1)/256 (the kernels address 256 operand rows with 32-bit
+ * offsets), else FP8Q_ERR_SHAPE.
  */
 fp8q_status fp8q_grouped_gemm_wgrad(const uint8_t* dyq_t, const float* dys_t, const uint8_t* xq_t,
                                     const float* xs_t, const int32_t* offsets, int64_t E, int64_t M_total,

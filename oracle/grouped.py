@@ -25,7 +25,7 @@ belong to no expert are not defined.
 
 import numpy as np
 
-from .gemm import _deq_rows, dgrad_ref, wgrad_ref
+from .gemm import dgrad_ref, wgrad_ref
 from .quant import quant_transpose
 
 GROUP = 128
@@ -112,17 +112,3 @@ def grouped_wgrad_ref(dyq_t, dys_t, xq_t, xs_t, offsets):
         c0 = p // GROUP
         dw[e], s[e] = wgrad_ref(dyq_t[:, p:p + m], dys_t[:, c0:c0 + nc], xq_t[:, p:p + m], xs_t[:, c0:c0 + nc])
     return dw, s
-
-
-def grouped_wgrad_deq(dyq_t, dys_t, xq_t, xs_t, offsets):
-    """The dequantized operands of expert e's Wgrad, for exact-rational checks:
-    a list of (dY_e^T [N, m_e], X_e^T [K, m_e]) float64 pairs."""
-    out = []
-    offsets = np.asarray(offsets, dtype=np.int64)
-    for e, p in enumerate(padded_starts(offsets)):
-        m = int(offsets[e + 1] - offsets[e])
-        nc = (m + GROUP - 1) // GROUP
-        c0 = p // GROUP
-        out.append((_deq_rows(dyq_t[:, p:p + m], dys_t[:, c0:c0 + nc]),
-                    _deq_rows(xq_t[:, p:p + m], xs_t[:, c0:c0 + nc])))
-    return out

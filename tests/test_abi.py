@@ -51,6 +51,13 @@ def test_every_kernel_launch_stub_is_defined(lib):
     assert sum(1 for l in out.splitlines() if "__device_stub__" in l) >= 25
 
 
+def test_gemm_tile_setting(lib):
+    assert lib.fp8q_set_gemm_tile(3) == SHAPE
+    assert lib.fp8q_set_gemm_tile(-1) == SHAPE
+    for t in (1, 2, 0):
+        assert lib.fp8q_set_gemm_tile(t) == OK
+
+
 def test_status_strings(lib):
     for code, name in enumerate(fq._STATUS):
         assert fq.status_string(code).startswith(name)
@@ -127,8 +134,15 @@ def test_grouped_backward_argument_errors(lib):
     assert gd(A16, A16, A16, A16, A16, 1, m_edge, 128, 32768, A16, 0, 32768, None) == SHAPE
     assert lib.fp8q_grouped_gemm(A16, A16, A16, A16, A16, 1, m_edge, 32768, 128, A16, 0, 32768, None) == SHAPE
     assert lib.fp8q_grouped_gemm_mx(A16, A16, A16, A16, A16, 1, m_edge, 32768, 128, A16, 0, 32768, None) == SHAPE
+    # stacked transposed weights wider than 32-bit buffer offsets cover for 256 rows: one step past the bound
+    # (E*N = 2^23, against the bound (2^31 - 1) / 256 = 2^23 - 1)
+    assert gd(A16, A16, A16, A16, A16, 64, 64, 1 << 17, 256, A16, 0, 256, None) == SHAPE
+    assert gd(A16, A16, A16, A16, A16, 65536, 64, 128, 256, A16, 0, 256, None) == SHAPE
     gw = lib.fp8q_grouped_gemm_wgrad
     assert gw(A16, A16, A16, A16, A16, 4, 300, 128, 256, 640, A16, 0, None) == STRIDE  # ld_t < 768
+    # a padded token stride past what 32-bit buffer offsets cover for 256 rows (the next multiple of 128)
+    ld_big = (((1 << 31) - 1) // 256 // 128 + 1) * 128
+    assert gw(A16, A16, A16, A16, A16, 4, 300, 128, 256, ld_big, A16, 0, None) == SHAPE
     assert gw(A16, A16, A16, A16, A16, 4, 300, 128, 256, 800, A16, 0, None) == ALIGN   # ld_t % 128
     assert gw(A16, A16, A16, A16, A16, 4, 300, 128, 200, 768, A16, 0, None) == SHAPE   # K % 128
     assert gw(A16, A16, A16, A16, A16, 4, 300, 128, 256, 768, A16, 2, None) == SHAPE   # accumulate flag

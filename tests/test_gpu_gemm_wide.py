@@ -1,12 +1,10 @@
 """The two workgroup tiles of the FP8 GEMM (256 x 128 with four waves, 256 x
 256 with eight) run the same per-wave arithmetic in the same order, so their
 outputs must agree bit for bit.  The library picks a tile by problem size;
-FP8Q_GEMM_TILE forces one.  Each case runs both tiles on the same operands
+fp8q_set_gemm_tile forces one.  Each case runs both tiles on the same operands
 (the GPU quantizers' codes of seeded inputs) and compares the raw output bits;
 one forced-wide case with a ragged tail is also checked against the oracle.
 The 256 x 128 kernel is checked against the oracle in test_gpu_gemm.py."""
-
-import os
 
 import numpy as np
 import pytest
@@ -21,17 +19,13 @@ pytestmark = pytest.mark.gpu
 
 
 def _with_tile(tile, fn):
-    old = os.environ.get("FP8Q_GEMM_TILE")
-    os.environ["FP8Q_GEMM_TILE"] = tile
+    fq.set_gemm_tile(tile)
     try:
         out = fn()
         torch.cuda.synchronize()
         return out
     finally:
-        if old is None:
-            del os.environ["FP8Q_GEMM_TILE"]
-        else:
-            os.environ["FP8Q_GEMM_TILE"] = old
+        fq.set_gemm_tile("auto")
 
 
 def _same_bits(fn, what):
