@@ -33,9 +33,10 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_FP8_TFLOPS = 5000.0      # MI355X dense FP8 MFMA
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense BF16 MFMA (the exact-accumulation GEMMs)
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-KERNEL_SOURCES = ["quant_kernels.hip", "gemm_fp8.hip", "gemm_kernels.hip", "gemm_tile.h", "device_common.h",
+KERNEL_SOURCES = ["quant_kernels.hip", "gemm_fp8.hip", "gemm_tile.h", "device_common.h",
                   "quant_mx.hip", "gemm_mx.hip"]
 
 
@@ -199,6 +200,194 @@ def make_mx_ops(L, dev):
     return ops
 
 
+def make_exact_ops(L, O):
+    """The exact-accumulation GEMMs (BF16 matrix instruction on exactly
+    converted codes, FP32 promotion per 128-K chunk) on the step's own
+    quantized operands: the linear layer's three products and the grouped
+    Fprop, as make_ops."""
+    import torch
+    import fp8_fine_grained_quant_amd as fq
+
+    E = 32
+    M, K, N = L["x"].shape[0], L["x"].shape[1], L["w"].shape[0]
+    Mm, Nm = L["xm"].shape[0], L["wm"].shape[0] // E
+    dev = L["x"].device
+    y = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+    dx = torch.empty(M, K, dtype=torch.bfloat16, device=dev)
+    dw = torch.empty(N, K, dtype=torch.float32, device=dev)
+    ym = torch.empty(Mm, Nm, dtype=torch.bfloat16, device=dev)
+    ops = [
+        ("gemm_fprop_exact", lambda: fq.fp8q_gemm_fprop(O["xq"], O["xs"], O["wq"], O["ws"], y, exact=True),
+         "mfma_bf16", 2.0 * M * N * K),
+        ("gemm_dgrad_exact", lambda: fq.fp8q_gemm_dgrad(O["dyq"], O["dys"], O["wq_t"], O["ws"], dx, exact=True),
+         "mfma_bf16", 2.0 * M * N * K),
+        ("gemm_wgrad_exact", lambda: fq.fp8q_gemm_wgrad(O["dyq_t"], O["dys_t"], O["xq_t"], O["xs_t"], dw,
+                                                        exact=True), "mfma_bf16", 2.0 * M * N * K),
+        ("grouped_gemm_exact", lambda: fq.fp8q_grouped_gemm(O["xmq"], O["xms"], O["wmq"].view(E, Nm, K),
+                                                            O["wms"].view(E, Nm // 128, K // 128), L["off"], ym,
+                                                            exact=True), "mfma_bf16", 2.0 * Mm * Nm * K),
+    ]
+    return ops, dict(y=y, dx=dx, dw=dw, ym=ym)
+
+
+def tiny_gemm_latency(dev, reps=200):
+    """The tiny Fprop (X bf16 [128,256], W fp32 [128,256], bf16 Y [128,128]):
+    one launch, so its figure is latency.  Returns the median of single
+    launches bracketed by HIP events, and the per-launch time of `reps`
+    launches back to back."""
+    import torch
+    import fp8_fine_grained_quant_amd as fq
+    import synth
+
+    x, w = synth.tiny_fprop()
+    xq, xs = fq.quant_act_1x128(x.to(dev))
+    wq, ws, _ = fq.quant_weight_128x128(w.to(dev), transpose=False)
+    y = torch.empty(128, 128, dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream()
+    for _ in range(20):
+        fq.fp8q_gemm_fprop(xq, xs, wq, ws, y)
+    torch.cuda.synchronize()
+    single = []
+    for _ in range(50):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        fq.fp8q_gemm_fprop(xq, xs, wq, ws, y)
+        b.record(stream)
+        b.synchronize()
+        single.append(a.elapsed_time(b) * 1e3)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(reps):
+        fq.fp8q_gemm_fprop(xq, xs, wq, ws, y)
+    b.record(stream)
+    torch.cuda.synchronize()
+    single.sort()
+    return {"workload": "tiny Fprop X [128,256] . W [128,256]^T, bf16 out (8.39 MFLOP)",
+            "single_launch_us_median": round(single[len(single) // 2], 2),
+            "back_to_back_us_per_launch": round(a.elapsed_time(b) * 1e3 / reps, 2),
+            "launches": reps}
+
+
+def telemetry(ops, seconds=1.5):
+    """GPU clock and power while the step runs back to back for `seconds`
+    (amdsmi, sampled every 20 ms from a thread); also the step time of that
+    sustained loop.  None with the reason if telemetry is unavailable."""
+    import threading
+    import torch
+    try:
+        import amdsmi
+        amdsmi.amdsmi_init()
+    except Exception as ex:  # pragma: no cover - depends on the host
+        return {"unavailable": f"amdsmi: {ex}"}
+    try:
+        handles = amdsmi.amdsmi_get_processor_handles()
+        h = handles[0]
+        try:
+            want = torch.cuda.get_device_properties(0).pci_bus_id
+            for c in handles:
+                if int(amdsmi.amdsmi_get_gpu_device_bdf(c).split(":")[1], 16) == want:
+                    h = c
+        except Exception:
+            pass
+        clk, pwr = [], []
+        stop = threading.Event()
+
+        def sample():
+            while not stop.is_set():
+                try:
+                    c = amdsmi.amdsmi_get_clock_info(h, amdsmi.AmdSmiClkType.GFX)
+                    clk.append(float(c.get("clk", c.get("cur_clk"))))
+                except Exception:
+                    pass
+                try:
+                    p = amdsmi.amdsmi_get_power_info(h)
+                    v = p.get("current_socket_power", "N/A")
+                    if v in ("N/A", None):
+                        v = p.get("average_socket_power", "N/A")
+                    if v not in ("N/A", None):
+                        pwr.append(float(v))
+                except Exception:
+                    pass
+                time.sleep(0.02)
+
+        th = threading.Thread(target=sample, daemon=True)
+        th.start()
+        torch.cuda.synchronize()
+        t0, n = time.perf_counter(), 0
+        while time.perf_counter() - t0 < seconds:
+            for _ in range(10):
+                for _, fn, _, _ in ops:
+                    fn()
+            n += 10
+            torch.cuda.synchronize()
+        dt = time.perf_counter() - t0
+        stop.set()
+        th.join()
+        med = lambda v: sorted(v)[len(v) // 2] if v else None
+        return {"sclk_mhz": {"median": med(clk), "min": min(clk) if clk else None, "max": max(clk) if clk else None,
+                             "samples": len(clk)},
+                "power_w": {"median": med(pwr), "max": max(pwr) if pwr else None, "samples": len(pwr)},
+                "sustained_ms_per_step": round(dt * 1e3 / n, 4), "steps": n,
+                "note": "sampled while the step ran back to back for ~1.5 s right after the timed region"}
+    finally:
+        try:
+            amdsmi.amdsmi_shut_down()
+        except Exception:
+            pass
+
+
+def context_error(H, outs, samples=64, seed=7):
+    """Error of the GPU outputs against the unquantized product in FP64 (the
+    inputs before quantization: X and dY in BF16, W in FP32), on sampled
+    output rows: relative Frobenius norm and max |y - Y_true| / S_true with
+    S_true = sum_k |a_k b_k|.  Plain NumPy on the host inputs."""
+    import numpy as np
+
+    rng = np.random.Generator(np.random.PCG64(seed))
+    x = H["x"].float().numpy().astype(np.float64)
+    dy = H["dy"].float().numpy().astype(np.float64)
+    w = H["w"].numpy().astype(np.float64)
+    M, K = x.shape
+    N = w.shape[0]
+    rows = np.sort(rng.choice(M, samples, replace=False))
+    chans = np.sort(rng.choice(N, samples, replace=False))
+    cases = {
+        "fprop": (x[rows], w, lambda o: o["y"][rows]),
+        "dgrad": (dy[rows], w.T, lambda o: o["dx"][rows]),
+        "wgrad": (dy[:, chans].T, x.T, lambda o: o["dw"][chans]),
+    }
+    out = {}
+    for name, (a, b, pick) in cases.items():
+        y_true = a @ b.T
+        s_true = np.abs(a) @ np.abs(b).T
+        d = {}
+        for path, o in outs.items():
+            y = pick(o).float().cpu().numpy().astype(np.float64)
+            err = y - y_true
+            d[path] = {"rel_frobenius": float(np.linalg.norm(err) / np.linalg.norm(y_true)),
+                       "max_err_over_S_true": float((np.abs(err) / s_true).max())}
+        out[name] = d
+    out["sample"] = f"{samples} seeded output rows of each product (dW: {samples} rows = output channels)"
+    return out
+
+
+def trace_summary(csv_path):
+    """Per-kernel launch count, mean, median and minimum duration (us) from a
+    rocprofv3 --kernel-trace CSV, as a markdown table on stdout (the median
+    is robust to the warm-up launches that the mean includes)."""
+    import csv
+    from collections import defaultdict
+    d = defaultdict(list)
+    with open(csv_path) as f:
+        for r in csv.DictReader(f):
+            d[r["Kernel_Name"]].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    print("| kernel | launches | mean us | median us | min us |")
+    print("|---|---|---|---|---|")
+    for k, v in sorted(d.items(), key=lambda kv: -sum(kv[1])):
+        v.sort()
+        print(f"| `{k[:90]}` | {len(v)} | {sum(v) / len(v):.2f} | {v[len(v) // 2]:.2f} | {v[0]:.2f} |")
+
+
 def time_ops(ops, steps, warmup, stream, flush=None):
     """Run `warmup` untimed passes, then time `steps` passes back to back
     (HIP events on `stream` before the first and after the last launch only),
@@ -249,9 +438,10 @@ def time_ops(ops, steps, warmup, stream, flush=None):
         times = sorted(ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(steps))
         avg_ms = sum(times) / len(times)
         d = {"avg_us": round(avg_ms * 1e3, 2), "median_us": round(times[len(times) // 2] * 1e3, 2)}
-        if kind == "mfma":
+        if kind in ("mfma", "mfma_bf16"):
             a = work / (avg_ms * 1e-3) / 1e12
-            d.update(gflop=round(work / 1e9, 3), tflops=round(a, 1), frac_peak=round(a / PEAK_FP8_TFLOPS, 4))
+            peak = PEAK_FP8_TFLOPS if kind == "mfma" else PEAK_BF16_TFLOPS
+            d.update(gflop=round(work / 1e9, 3), tflops=round(a, 1), frac_peak=round(a / peak, 4))
         else:
             a = work / (avg_ms * 1e-3) / 1e9
             d.update(mbytes=round(work / 1e6, 3), gbs=round(a, 1), frac_peak=round(a / PEAK_HBM_GBS, 4))
@@ -284,30 +474,54 @@ def cpu_baseline(H, frac):
     xm_s = xm[:ts].float().numpy()
     offs = np.minimum(off.numpy().astype(np.int64), ts)
     experts = [e for e in range(len(offs) - 1) if offs[e + 1] > offs[e]]
+    per_op = {}
+
+    def timed(name, fn, kind, work):
+        t = time.perf_counter()
+        r = fn()
+        dt = time.perf_counter() - t
+        d = {"s": round(dt, 3)}
+        if kind == "gemm":
+            d["gflops"] = round(work / dt / 1e9, 2)
+        else:
+            d["gbs"] = round(work / dt / 1e9, 4)
+        per_op[name] = d
+        return r
+
+    act_bytes = lambda r, c: r * c * 3 + r * cdiv(c, 128) * 4
     flops = 0.0
     t0 = time.perf_counter()
-    xq, xsc = oracle.quant_act_1x128(x_s)
-    wq, wsc, _ = oracle.quant_weight_128x128(w.numpy())
-    oracle.fprop_ref(xq, xsc, wq, wsc)
-    dyq, dysc = oracle.quant_act_1x128(dy_s)
-    oracle.dgrad_ref(dyq, dysc, wq, wsc)
-    xq_t, xs_t = oracle.quant_transpose(x_s)
-    dq_t, ds_t = oracle.quant_transpose(dy_s)
-    oracle.wgrad_ref(dq_t, ds_t, xq_t, xs_t)
+    xq, xsc = timed("quant_act X", lambda: oracle.quant_act_1x128(x_s), "quant", act_bytes(rs, K))
+    wq, wsc, _ = timed("quant_weight W (+q_t)", lambda: oracle.quant_weight_128x128(w.numpy()), "quant",
+                       N * K * 6 + cdiv(N, 128) * cdiv(K, 128) * 4)
+    timed("gemm_fprop", lambda: oracle.fprop_ref(xq, xsc, wq, wsc), "gemm", 2.0 * rs * N * K)
+    dyq, dysc = timed("quant_act dY", lambda: oracle.quant_act_1x128(dy_s), "quant", act_bytes(rs, N))
+    timed("gemm_dgrad", lambda: oracle.dgrad_ref(dyq, dysc, wq, wsc), "gemm", 2.0 * rs * N * K)
+    xq_t, xs_t = timed("quant_transpose X", lambda: oracle.quant_transpose(x_s), "quant", act_bytes(rs, K))
+    dq_t, ds_t = timed("quant_transpose dY", lambda: oracle.quant_transpose(dy_s), "quant", act_bytes(rs, N))
+    timed("gemm_wgrad", lambda: oracle.wgrad_ref(dq_t, ds_t, xq_t, xs_t), "gemm", 2.0 * rs * N * K)
     flops += 3 * 2.0 * rs * N * K
-    xmq, xmsc = oracle.quant_act_1x128(xm_s)
+    xmq, xmsc = timed("quant_act X_moe", lambda: oracle.quant_act_1x128(xm_s), "quant", act_bytes(ts, K))
     wmq = np.zeros(wm.shape, dtype=np.uint8)
     wms = np.zeros((wm.shape[0], N // 128, K // 128), dtype=np.float32)
-    for e in experts:
-        wmq[e], wms[e], _ = oracle.quant_weight_128x128(wm[e].numpy())
-    oracle.grouped_ref(xmq, xmsc, wmq, wms, offs)
+
+    def quant_experts():
+        for e in experts:
+            wmq[e], wms[e], _ = oracle.quant_weight_128x128(wm[e].numpy())
+
+    timed("quant_weight W_moe", quant_experts, "quant", len(experts) * (N * K * 5 + (N // 128) * (K // 128) * 4))
+    timed("grouped_gemm", lambda: oracle.grouped_ref(xmq, xmsc, wmq, wms, offs), "gemm", 2.0 * ts * N * K)
     flops += 2.0 * ts * N * K
     dt = time.perf_counter() - t0
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(blas_threads), "kind": "oracle",
             "sample": f"one step on a token sample: linear layer on the first {rs} of {M} tokens (all three "
                       f"GEMMs, all quantizers, full W), MoE layer on the first {ts} of {xm.shape[0]} tokens "
                       f"({len(experts)} experts reached, their weights quantized); {dt:.1f}s wall; FP64 BLAS "
-                      f"GEMMs on {blas_threads} threads, NumPy quantizers on one"}
+                      f"GEMMs on {blas_threads} threads, NumPy quantizers on one",
+            "per_op": per_op,
+            "per_op_note": "quantizers: NumPy on one core, GB/s of the same algorithmic bytes as the GPU's; "
+                           "GEMMs: the FP64 product of the dequantized operands plus the sum|a*b| normaliser "
+                           f"(two BLAS GEMMs) on {blas_threads} threads, GFLOP/s of the useful 2MNK"}
 
 
 def kernel_source_hash():
@@ -355,7 +569,12 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=float, default=0.0, metavar="MB",
                     help="only run a plain device copy of MB megabytes (counter calibration) and exit")
+    ap.add_argument("--trace-summary", metavar="CSV",
+                    help="only summarize a rocprofv3 kernel-trace CSV (per-kernel mean/median/min) and exit")
     args = ap.parse_args()
+    if args.trace_summary:
+        trace_summary(args.trace_summary)
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU: the path is built and timed on a single MI355X; "
               "multi-GPU runs are not part of this library", file=sys.stderr)
@@ -372,14 +591,15 @@ def main():
     dev = "cuda:0"
     H = host_inputs()
     L = build_workload(H, dev)
-    if args.no_cpu_baseline:
-        del H
     ops, O = make_ops(L, dev)
     names = [o[0] for o in ops]
 
     stream = torch.cuda.current_stream()
     log(f"warmup {args.warmup} steps, timing {args.steps} steps")
     ms_step, kernels = time_ops(ops, args.steps, args.warmup, stream)
+    log("telemetry: the step back to back for ~1.5 s")
+    tele = telemetry(ops)
+    log(f"telemetry {tele}")
 
     # the MoE backward, beside the step
     bops, _ = make_moe_bwd_ops(L, dev)
@@ -404,6 +624,23 @@ def main():
     ms_mx, mkernels = time_ops(mops, args.steps, args.warmup, stream, flush)
     del flush_buf
     mx_flops = sum(w for _, _, k, w in mops if k == "mfma")
+
+    # the exact-accumulation GEMMs on the step's quantized operands, beside the step
+    flush_buf = torch.zeros(1 << 28, dtype=torch.float32, device=dev)
+    flush = flush_buf.sum
+    xops, X = make_exact_ops(L, O)
+    log(f"exact-accumulation GEMMs: warmup {args.warmup}, timing {args.steps} passes")
+    _, xkernels = time_ops(xops, args.steps, args.warmup, stream, flush)
+    del flush_buf
+
+    log("tiny GEMM latency")
+    tiny = tiny_gemm_latency(dev)
+    log(f"tiny {tiny}")
+
+    log("context error against the unquantized FP64 products")
+    ctx = context_error(H, {"fp8": {"y": O["y"], "dx": O["dx"], "dw": O["dw"]},
+                            "exact": {"y": X["y"], "dx": X["dx"], "dw": X["dw"]}})
+    log(f"context {ctx}")
     lin = ["quant_act X", "quant_weight W (+q_t)", "gemm_fprop", "quant_act dY", "gemm_dgrad", "quant_transpose X",
            "quant_transpose dY", "gemm_wgrad"]
     lin_us = sum(kernels[n]["avg_us"] for n in lin)
@@ -477,6 +714,17 @@ def main():
             "method_linear_layer_us": {"as_step": round(lin_us, 2), "with_dual_quantizers": round(lin_dual_us, 2)},
             "kernels": mkernels,
         },
+        "exact_variant": {
+            "workload": "the step's GEMMs (linear Fprop, Dgrad, Wgrad; MoE grouped Fprop) on the same quantized "
+                        "operands through the *_exact entry points: codes converted exactly to BF16, BF16 matrix "
+                        "instruction (exact products, FP32 sums), FP32 promotion per 128-K chunk; the path that "
+                        "stays within 1e-5 * sum|a*b| of the exact contraction",
+            "peak_tflops": PEAK_BF16_TFLOPS,
+            "kernels": xkernels,
+        },
+        "tiny_gemm": tiny,
+        "telemetry": tele,
+        "context_error": ctx,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

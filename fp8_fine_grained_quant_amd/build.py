@@ -13,7 +13,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libfp8q.so")
-SOURCES = ["quant_kernels.hip", "quant_mx.hip", "gemm_kernels.hip", "gemm_fp8.hip", "gemm_mx.hip", "api.cpp"]
+SOURCES = ["quant_kernels.hip", "quant_mx.hip", "gemm_fp8.hip", "gemm_mx.hip", "api.cpp"]
 ARCH = os.environ.get("FP8Q_ARCH", "gfx950")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

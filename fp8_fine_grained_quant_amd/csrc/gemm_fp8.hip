@@ -42,6 +42,18 @@
 // B, which leaves every dot product unchanged): lane l supplies row l%16 of
 // the 16-row slice, bytes [16g, 16g+16) and [64+16g, 64+16g+16) of the chunk,
 // g = l/16.  Result: lane l holds C[4g + r][l%16], r = 0..3.
+//
+// Exact mode (the _exact entry points, template flag EX of the 256 x 128
+// kernel).  gfx950's FP8 matrix instruction aligns the 8 products of each
+// group of 8 consecutive K to the largest one and truncates the others 13
+// bits below its exponent (measured), the analogue of the limited
+// accumulation the innerforce.co.kr excerpt reports for H800 tensor cores
+// (paragraph after Figure 7 (a)).  Exact mode keeps the same data movement,
+// slot schedule and promotion, but converts each lane's 32 code bytes exactly
+// to BF16 (every E4M3 value is a BF16 value) and forms the chunk's partial
+// with four v_mfma_f32_16x16x32_bf16 over quarters of 8 K per lane, whose
+// products are exact and whose sums are FP32.  A fragments are converted once
+// per chunk, B fragments once per column.
 
 #include "device_common.h"
 #include "gemm_tile.h"
@@ -52,6 +64,8 @@ namespace {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void* lds_ptr;
 
 constexpr int kBM = 256, kBN = 128, kBK = 128;
@@ -94,6 +108,20 @@ __device__ __forceinline__ v8i make_frag(uint4 lo, uint4 hi) {
   return f;
 }
 
+// Exact mode: a lane's 32 code bytes of a fragment -> four groups of 8 BF16
+// values (bytes [8q, 8q+8) -> out[q]).  Every E4M3 value is a BF16 value, so
+// the conversion (scale 1.0) is exact.
+__device__ __forceinline__ void to_bf16_quarters(const v8i& f, v8bf (&out)[4]) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const v2bf c0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(f[2 * q], 1.0f, false);
+    const v2bf c1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(f[2 * q], 1.0f, true);
+    const v2bf c2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(f[2 * q + 1], 1.0f, false);
+    const v2bf c3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(f[2 * q + 1], 1.0f, true);
+    out[q] = v8bf{c0[0], c0[1], c1[0], c1[1], c2[0], c2[1], c3[0], c3[1]};
+  }
+}
+
 template <int V>
 struct IC {
   static constexpr int value = V;
@@ -116,7 +144,7 @@ __device__ __forceinline__ void row_scales(float v, float k, float (&out)[4]) {
 
 }  // namespace
 
-template <int SB_MODE, int OUT_F32, bool GROUPED, bool KG, bool SC4>
+template <int SB_MODE, int OUT_F32, bool GROUPED, bool KG, bool SC4, bool EX>
 __global__ __launch_bounds__(kNT) void k_gemm_fp8(GemmArgs p) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
   typedef Stage<SB_MODE, SC4> S;
@@ -283,6 +311,16 @@ __global__ __launch_bounds__(kNT) void k_gemm_fp8(GemmArgs p) {
   auto mfma = [&](const v8i& x, const v8i& y) -> v4f {
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(x, y, v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
   };
+  // exact mode: the chunk's partial as four BF16 instructions over quarters
+  // of 8 K per lane (exact products, FP32 sums); lane group g covers the same
+  // K positions of A and B in each, so together they cover the chunk once
+  v8bf abf[kTM][4];  // A fragments of the current chunk in BF16 (exact mode)
+  auto mfma_ex = [&](const v8bf (&x)[4], const v8bf (&y)[4]) -> v4f {
+    v4f c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x[0], y[0], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x[1], y[1], c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x[2], y[2], c, 0, 0, 0);
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(x[3], y[3], c, 0, 0, 0);
+  };
   auto fence = [] { asm volatile("" ::: "memory"); };
 
   // ---- prologue: block B scales of every chunk to LDS, chunks 0 and 1 in
@@ -330,6 +368,8 @@ __global__ __launch_bounds__(kNT) void k_gemm_fp8(GemmArgs p) {
       // next chunk's columns 0 and 1 at column 7, after the barrier that
       // publishes it (column 6 reads none)
       const v8i bcur = bring[(2 * u + j) % 3];
+      v8bf bbf[4];
+      if (EX) to_bf16_quarters(bcur, bbf);
       if (j + 2 < kTN) {
         bring[(2 * u + j + 2) % 3] = rdB(cur, j + 2);
       } else if (j == kTN - 1) {
@@ -345,7 +385,12 @@ __global__ __launch_bounds__(kNT) void k_gemm_fp8(GemmArgs p) {
 #pragma unroll
       for (int i = 0; i < kTM; ++i) {
         const int t = kTM * j + i;
-        pp[i] = mfma(a[i], bcur);
+        if (EX) {
+          if (j == 0) to_bf16_quarters(a[i], abf[i]);
+          pp[i] = mfma_ex(abf[i], bbf);
+        } else {
+          pp[i] = mfma(a[i], bcur);
+        }
         if (t >= kSkew) {
           const int tp = t - kSkew;
           promote(tp % kTM, tp / kTM, sbc[tp / kTM]);
@@ -877,14 +922,14 @@ __global__ __launch_bounds__(kWNT) void k_gemm_fp8_wide_row(GemmArgs p) {
 
 namespace {
 
-template <int SB_MODE, int OUT_F32, bool GROUPED, bool KG = false, bool SC4 = false>
+template <int SB_MODE, int OUT_F32, bool GROUPED, bool KG = false, bool SC4 = false, bool EX = false>
 hipError_t launch_one(const GemmArgs& a, hipStream_t st) {
   const int64_t tiles_n = a.N / kBN, tiles_m = (a.M + kBM - 1) / kBM;
   const int64_t tiles = KG ? a.E * 8 * ((tiles_m * tiles_n + 7) / 8)  // every expert: 8 XCD shares
                         : GROUPED ? (tiles_m + a.E) * tiles_n             // upper bound: a partial tile per expert
                                   : tiles_m * tiles_n;
   if (tiles <= 0) return hipSuccess;
-  hipLaunchKernelGGL((k_gemm_fp8<SB_MODE, OUT_F32, GROUPED, KG, SC4>), dim3((uint32_t)tiles), dim3(kNT), 0, st, a);
+  hipLaunchKernelGGL((k_gemm_fp8<SB_MODE, OUT_F32, GROUPED, KG, SC4, EX>), dim3((uint32_t)tiles), dim3(kNT), 0, st, a);
   return hipGetLastError();
 }
 
@@ -903,6 +948,27 @@ static bool use_wide_tile(const GemmArgs& a) {
   if (forced != 0) return forced == 2;
   const int64_t tiles = ((a.M + kBM - 1) / kBM) * (a.N / kWBN);
   return 2 * tiles > device_cu_count();
+}
+
+// The exact-accumulation entry points: the 256 x 128 kernel in exact mode.
+static hipError_t launch_exact(const GemmArgs& a, hipStream_t st) {
+  const bool sc4 = a.ld_sa % 4 == 0 && (reinterpret_cast<uintptr_t>(a.sa) & 15) == 0;
+  const bool g = a.offsets != nullptr;
+  if (a.sb_mode == kSbRow) return launch_one<kSbRow, 1, false, false, false, true>(a, st);
+  if (sc4) {
+    if (g) return a.out_f32 ? launch_one<kSbBlock, 1, true, false, true, true>(a, st)
+                            : launch_one<kSbBlock, 0, true, false, true, true>(a, st);
+    return a.out_f32 ? launch_one<kSbBlock, 1, false, false, true, true>(a, st)
+                     : launch_one<kSbBlock, 0, false, false, true, true>(a, st);
+  }
+  if (g) return a.out_f32 ? launch_one<kSbBlock, 1, true, false, false, true>(a, st)
+                          : launch_one<kSbBlock, 0, true, false, false, true>(a, st);
+  return a.out_f32 ? launch_one<kSbBlock, 1, false, false, false, true>(a, st)
+                   : launch_one<kSbBlock, 0, false, false, false, true>(a, st);
+}
+
+hipError_t launch_gemm(const GemmArgs& a, hipStream_t st) {
+  return a.exact ? launch_exact(a, st) : launch_gemm_fp8(a, st);
 }
 
 hipError_t launch_gemm_fp8(const GemmArgs& a, hipStream_t st) {

@@ -1,13 +1,16 @@
 """Shared helpers of the GPU parity tests: move seeded inputs to the GPU, run the
 oracle on the same inputs, and compare element by element."""
 
+import json
 import math
+import os
 
 import numpy as np
 import torch
 
 DEV = "cuda:0"
 REL_TOL = 1e-5          # |y - Y_ref| <= 1e-5 * sum_k |a_k b_k|
+ERR_LOG = os.environ.get("FP8Q_ERR_LOG")  # if set: every GEMM check appends its error statistics (JSON lines)
 
 
 def gpu(t):
@@ -78,6 +81,9 @@ def check_gemm(y, y_ref, s_ref, out_bf16, what, exact=True, nk=None):
         rne = torch.from_numpy(y_ref.astype(np.float32)).to(torch.bfloat16).double().numpy()
         stats["n_not_rne_of_ref"] = int((y != rne).sum())
     print("GEMM", stats, flush=True)
+    if ERR_LOG:
+        with open(ERR_LOG, "a") as f:
+            f.write(json.dumps(stats) + "\n")
     if over.any():
         idx = np.argwhere(over)[:5]
         detail = [(tuple(int(v) for v in i), float(y[tuple(i)]), float(y_ref[tuple(i)]), float(s_ref[tuple(i)]))
