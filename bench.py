@@ -230,6 +230,32 @@ def make_exact_ops(L, O):
     return ops, dict(y=y, dx=dx, dw=dw, ym=ym)
 
 
+def make_fused_ops(L, O):
+    """Fprop and Dgrad of the linear layer with the next layer's 1x128
+    quantization of their BF16 output fused into the GEMM epilogue, beside
+    the same GEMMs followed by the separate quantizer, as make_ops."""
+    import torch
+    import fp8_fine_grained_quant_amd as fq
+
+    M, K, N = L["x"].shape[0], L["x"].shape[1], L["w"].shape[0]
+    dev = L["x"].device
+    e = lambda *s, dt=torch.uint8: torch.empty(*s, dtype=dt, device=dev)
+    F = dict(y=e(M, N, dt=torch.bfloat16), yq=e(M, N), ys=e(M, N // 128, dt=torch.float32),
+             dx=e(M, K, dt=torch.bfloat16), dxq=e(M, K), dxs=e(M, K // 128, dt=torch.float32))
+    flop = 2.0 * M * N * K
+    ops = [
+        ("gemm_fprop + quant_act Y", lambda: (fq.fp8q_gemm_fprop(O["xq"], O["xs"], O["wq"], O["ws"], F["y"]),
+                                              fq.fp8q_quant_act_1x128(F["y"], F["yq"], F["ys"])), "mfma", flop),
+        ("gemm_fprop_quant", lambda: fq.fp8q_gemm_fprop_quant(O["xq"], O["xs"], O["wq"], O["ws"], F["y"], F["yq"],
+                                                               F["ys"]), "mfma", flop),
+        ("gemm_dgrad + quant_act dX", lambda: (fq.fp8q_gemm_dgrad(O["dyq"], O["dys"], O["wq_t"], O["ws"], F["dx"]),
+                                               fq.fp8q_quant_act_1x128(F["dx"], F["dxq"], F["dxs"])), "mfma", flop),
+        ("gemm_dgrad_quant", lambda: fq.fp8q_gemm_dgrad_quant(O["dyq"], O["dys"], O["wq_t"], O["ws"], F["dx"],
+                                                               F["dxq"], F["dxs"]), "mfma", flop),
+    ]
+    return ops
+
+
 def tiny_gemm_latency(dev, reps=200):
     """The tiny Fprop (X bf16 [128,256], W fp32 [128,256], bf16 Y [128,128]):
     one launch, so its figure is latency.  Returns the median of single
@@ -631,6 +657,9 @@ def main():
     xops, X = make_exact_ops(L, O)
     log(f"exact-accumulation GEMMs: warmup {args.warmup}, timing {args.steps} passes")
     _, xkernels = time_ops(xops, args.steps, args.warmup, stream, flush)
+    fops = make_fused_ops(L, O)
+    log(f"fused output quantization: warmup {args.warmup}, timing {args.steps} passes")
+    _, fkernels = time_ops(fops, args.steps, args.warmup, stream, flush)
     del flush_buf
 
     log("tiny GEMM latency")
@@ -721,6 +750,17 @@ def main():
                         "stays within 1e-5 * sum|a*b| of the exact contraction",
             "peak_tflops": PEAK_BF16_TFLOPS,
             "kernels": xkernels,
+        },
+        "fused_output_quant": {
+            "workload": "the linear layer's Fprop (Y [4096,2048]) and Dgrad (dX [4096,7168]) writing BF16 output "
+                        "and, fused into the epilogue, its 1x128 E4M3 codes and scales (the next layer's FP8 "
+                        "input), against the same GEMM followed by quant_act_1x128 of its output; each entry is "
+                        "one launch pair or one launch between HIP events",
+            "kernels": fkernels,
+            "saved_us": {
+                "fprop": round(fkernels["gemm_fprop + quant_act Y"]["avg_us"] - fkernels["gemm_fprop_quant"]["avg_us"], 2),
+                "dgrad": round(fkernels["gemm_dgrad + quant_act dX"]["avg_us"] - fkernels["gemm_dgrad_quant"]["avg_us"],
+                               2)},
         },
         "tiny_gemm": tiny,
         "telemetry": tele,

@@ -47,7 +47,7 @@ EXPORTS = ["fp8q_status_string", "fp8q_set_gemm_tile", "fp8q_quant_act_1x128", "
            "fp8q_grouped_gemm_exact", "fp8q_quant_transpose_grouped", "fp8q_grouped_gemm_dgrad",
            "fp8q_grouped_gemm_wgrad", "fp8q_quant_act_transpose", "fp8q_quant_mx_1x32",
            "fp8q_quant_mx_transpose", "fp8q_gemm_mx", "fp8q_grouped_gemm_mx",
-           "fp8q_grouped_gemm_mx_dgrad"]
+           "fp8q_grouped_gemm_mx_dgrad", "fp8q_gemm_fprop_quant", "fp8q_gemm_dgrad_quant"]
 
 
 class Fp8qError(RuntimeError):
@@ -87,6 +87,8 @@ def load_library(path=LIB_PATH):
         "fp8q_gemm_mx": ([P, P, I64, I64, P, P, I64, I64, I64, I64, I64, P, I32, I64, I32, P], I32),
         "fp8q_grouped_gemm_mx": ([P, P, P, P, P, I64, I64, I64, I64, P, I32, I64, P], I32),
         "fp8q_grouped_gemm_mx_dgrad": ([P, P, P, P, P, I64, I64, I64, I64, P, I32, I64, P], I32),
+        "fp8q_gemm_fprop_quant": ([P, P, P, P, I64, I64, I64, P, I64, P, I64, P, I64, I32, P], I32),
+        "fp8q_gemm_dgrad_quant": ([P, P, P, P, I64, I64, I64, P, I64, P, I64, P, I64, I32, P], I32),
     }
     for name in ["fp8q_gemm_fprop", "fp8q_gemm_dgrad", "fp8q_gemm_wgrad", "fp8q_grouped_gemm"]:
         sig[name + "_exact"] = sig[name]
@@ -255,6 +257,48 @@ def fp8q_gemm_wgrad(dyq_t, dys_t, xq_t, xs_t, dw, accumulate=False, stream=None,
     _check(_fn("fp8q_gemm_wgrad", exact)(_ptr(dyq_t), _ptr(dys_t), _ptr(xq_t), _ptr(xs_t), t, n, k, _ptr(dw),
                                            _ld(dw), int(bool(accumulate)), _stream(stream)),
            "fp8q_gemm_wgrad")
+
+
+def fp8q_gemm_fprop_quant(xq, xs, wq, ws, y, yq, ys, stream=None, exact=False):
+    """Fprop with the output's 1x128 quantization in the epilogue: y [M, N]
+    BF16 (or None: codes only), yq [M, N] uint8, ys [M, N/128] FP32."""
+    m, k = xq.shape
+    n = wq.shape[0]
+    _expect(xq, (m, k), _U8, "xq")
+    _expect(xs, (m, _cdiv(k, 128)), _F32, "xs")
+    _expect(wq, (n, k), _U8, "wq")
+    _expect(ws, (_cdiv(n, 128), _cdiv(k, 128)), _F32, "ws")
+    if y is not None:
+        _expect(y, (m, n), torch.bfloat16, "y")
+    _expect(yq, (m, n), _U8, "yq")
+    _expect(ys, (m, _cdiv(n, 128)), _F32, "ys")
+    _on_gpu(xq, xs, wq, ws, y, yq, ys)
+    _contig(xq, xs, wq, ws)
+    _check(load_library().fp8q_gemm_fprop_quant(_ptr(xq), _ptr(xs), _ptr(wq), _ptr(ws), m, n, k, _ptr(y),
+                                                 _ld(y) if y is not None else 0, _ptr(yq), _ld(yq), _ptr(ys),
+                                                 _ld(ys), int(bool(exact)), _stream(stream)),
+           "fp8q_gemm_fprop_quant")
+
+
+def fp8q_gemm_dgrad_quant(dyq, dys, wq_t, ws, dx, dxq, dxs, stream=None, exact=False):
+    """Dgrad with the output's 1x128 quantization in the epilogue: dx [M, K]
+    BF16 (or None: codes only), dxq [M, K] uint8, dxs [M, K/128] FP32."""
+    m, n = dyq.shape
+    k = wq_t.shape[0]
+    _expect(dyq, (m, n), _U8, "dyq")
+    _expect(dys, (m, _cdiv(n, 128)), _F32, "dys")
+    _expect(wq_t, (k, n), _U8, "wq_t")
+    _expect(ws, (_cdiv(n, 128), _cdiv(k, 128)), _F32, "ws")
+    if dx is not None:
+        _expect(dx, (m, k), torch.bfloat16, "dx")
+    _expect(dxq, (m, k), _U8, "dxq")
+    _expect(dxs, (m, _cdiv(k, 128)), _F32, "dxs")
+    _on_gpu(dyq, dys, wq_t, ws, dx, dxq, dxs)
+    _contig(dyq, dys, wq_t, ws)
+    _check(load_library().fp8q_gemm_dgrad_quant(_ptr(dyq), _ptr(dys), _ptr(wq_t), _ptr(ws), m, n, k, _ptr(dx),
+                                                 _ld(dx) if dx is not None else 0, _ptr(dxq), _ld(dxq), _ptr(dxs),
+                                                 _ld(dxs), int(bool(exact)), _stream(stream)),
+           "fp8q_gemm_dgrad_quant")
 
 
 def fp8q_grouped_gemm(xq, xs, wq, ws, offsets, y, stream=None, exact=False):
@@ -458,6 +502,26 @@ def gemm_fprop(xq, xs, wq, ws, out_dtype=torch.bfloat16, stream=None, exact=Fals
     y = torch.empty((xq.shape[0], wq.shape[0]), dtype=out_dtype, device=xq.device)
     fp8q_gemm_fprop(xq, xs, wq, ws, y, stream, exact)
     return y
+
+
+def gemm_fprop_quant(xq, xs, wq, ws, with_output=True, stream=None, exact=False):
+    """Fprop with fused output quantization: (y BF16 or None, yq, ys)."""
+    m, n = xq.shape[0], wq.shape[0]
+    y = torch.empty((m, n), dtype=torch.bfloat16, device=xq.device) if with_output else None
+    yq = torch.empty((m, n), dtype=torch.uint8, device=xq.device)
+    ys = torch.empty((m, _cdiv(n, 128)), dtype=torch.float32, device=xq.device)
+    fp8q_gemm_fprop_quant(xq, xs, wq, ws, y, yq, ys, stream, exact)
+    return y, yq, ys
+
+
+def gemm_dgrad_quant(dyq, dys, wq_t, ws, with_output=True, stream=None, exact=False):
+    """Dgrad with fused output quantization: (dx BF16 or None, dxq, dxs)."""
+    m, k = dyq.shape[0], wq_t.shape[0]
+    dx = torch.empty((m, k), dtype=torch.bfloat16, device=dyq.device) if with_output else None
+    dxq = torch.empty((m, k), dtype=torch.uint8, device=dyq.device)
+    dxs = torch.empty((m, _cdiv(k, 128)), dtype=torch.float32, device=dyq.device)
+    fp8q_gemm_dgrad_quant(dyq, dys, wq_t, ws, dx, dxq, dxs, stream, exact)
+    return dx, dxq, dxs
 
 
 def gemm_dgrad(dyq, dys, wq_t, ws, out_dtype=torch.bfloat16, stream=None, exact=False):

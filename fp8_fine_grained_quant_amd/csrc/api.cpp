@@ -159,17 +159,33 @@ fp8q_status fp8q_quant_transpose_grouped(const void* x, fp8q_dtype xt, int64_t r
 
 }  // extern "C"
 
+// The fused output quantization's arguments: codes [rows, ncols] (row stride
+// ld_q bytes) and scales [rows, ncols/128] (row stride ld_s).
+static fp8q_status check_quant_out(const uint8_t* q, int64_t ld_q, const float* s, int64_t ld_s, int64_t ncols) {
+  if (!q || !s) return FP8Q_ERR_NULL;
+  if (ld_q < ncols || ld_s < ncols / 128) return FP8Q_ERR_STRIDE;
+  if (!aligned16(q) || ld_q % 16 != 0 || !aligned4(s)) return FP8Q_ERR_ALIGN;
+  return FP8Q_OK;
+}
+
 static fp8q_status fp8q_gemm_fprop_impl(int exact, const uint8_t* xq, const float* xs, const uint8_t* wq, const float* ws,
                             int64_t M, int64_t N, int64_t K, void* y, fp8q_dtype yt, int64_t ld_y,
-                            hipStream_t stream) {
+                            hipStream_t stream, uint8_t* qo = nullptr, int64_t ld_qo = 0, float* so = nullptr,
+                            int64_t ld_so = 0, bool quant_out = false) {
   if (M < 0 || N < 0 || K < 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim) return FP8Q_ERR_SHAPE;
   if (N % 128 != 0 || K % 128 != 0 || K > kMaxContraction) return FP8Q_ERR_SHAPE;
   if (!valid_dtype(yt)) return FP8Q_ERR_DTYPE;
   if (M == 0 || N == 0) return FP8Q_OK;
   if (K == 0) return FP8Q_ERR_SHAPE;  // an empty contraction would leave Y undefined
   if (!xq || !xs || !wq || !ws) return FP8Q_ERR_NULL;
-  const fp8q_status c = check_gemm_out(y, yt, ld_y, N);
-  if (c != FP8Q_OK) return c;
+  if (quant_out) {
+    const fp8q_status c = check_quant_out(qo, ld_qo, so, ld_so, N);
+    if (c != FP8Q_OK) return c;
+  }
+  if (!quant_out || y != nullptr) {
+    const fp8q_status c = check_gemm_out(y, yt, ld_y, N);
+    if (c != FP8Q_OK) return c;
+  }
   if (!aligned16(xq) || !aligned16(wq) || !aligned4(xs) || !aligned4(ws)) return FP8Q_ERR_ALIGN;
   if (cdiv(M, 256) * (N / 128) > kMaxGroups) return FP8Q_ERR_SHAPE;  // the launch grid
   GemmArgs a{};
@@ -177,20 +193,28 @@ static fp8q_status fp8q_gemm_fprop_impl(int exact, const uint8_t* xq, const floa
   a.lda = K; a.ldb = K; a.ld_sa = K / 128; a.sb_rs = K / 128; a.sb_cs = 1; a.ldc = ld_y;
   a.M = M; a.N = N; a.K = K;
   a.sb_mode = fp8q::kSbBlock; a.out_f32 = yt == FP8Q_F32; a.accumulate = 0; a.exact = exact;
+  a.qo = qo; a.ld_qo = ld_qo; a.so = so; a.ld_so = ld_so;
   return launched(fp8q::launch_gemm(a, stream));
 }
 
 static fp8q_status fp8q_gemm_dgrad_impl(int exact, const uint8_t* dyq, const float* dys, const uint8_t* wq_t, const float* ws,
                             int64_t M, int64_t N, int64_t K, void* dx, fp8q_dtype dxt, int64_t ld_dx,
-                            hipStream_t stream) {
+                            hipStream_t stream, uint8_t* qo = nullptr, int64_t ld_qo = 0, float* so = nullptr,
+                            int64_t ld_so = 0, bool quant_out = false) {
   if (M < 0 || N < 0 || K < 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim) return FP8Q_ERR_SHAPE;
   if (N % 128 != 0 || K % 128 != 0 || N > kMaxContraction) return FP8Q_ERR_SHAPE;
   if (!valid_dtype(dxt)) return FP8Q_ERR_DTYPE;
   if (M == 0 || K == 0) return FP8Q_OK;
   if (N == 0) return FP8Q_ERR_SHAPE;
   if (!dyq || !dys || !wq_t || !ws) return FP8Q_ERR_NULL;
-  const fp8q_status c = check_gemm_out(dx, dxt, ld_dx, K);
-  if (c != FP8Q_OK) return c;
+  if (quant_out) {
+    const fp8q_status c = check_quant_out(qo, ld_qo, so, ld_so, K);
+    if (c != FP8Q_OK) return c;
+  }
+  if (!quant_out || dx != nullptr) {
+    const fp8q_status c = check_gemm_out(dx, dxt, ld_dx, K);
+    if (c != FP8Q_OK) return c;
+  }
   if (!aligned16(dyq) || !aligned16(wq_t) || !aligned4(dys) || !aligned4(ws)) return FP8Q_ERR_ALIGN;
   if (cdiv(M, 256) * (K / 128) > kMaxGroups) return FP8Q_ERR_SHAPE;  // the launch grid
   // NT form over the contraction axis N: A = dY [M, N], B = W^T codes [K, N];
@@ -200,6 +224,7 @@ static fp8q_status fp8q_gemm_dgrad_impl(int exact, const uint8_t* dyq, const flo
   a.lda = N; a.ldb = N; a.ld_sa = N / 128; a.sb_rs = 1; a.sb_cs = K / 128; a.ldc = ld_dx;
   a.M = M; a.N = K; a.K = N;
   a.sb_mode = fp8q::kSbBlock; a.out_f32 = dxt == FP8Q_F32; a.accumulate = 0; a.exact = exact;
+  a.qo = qo; a.ld_qo = ld_qo; a.so = so; a.ld_so = ld_so;
   return launched(fp8q::launch_gemm(a, stream));
 }
 
@@ -317,6 +342,19 @@ fp8q_status fp8q_grouped_gemm_wgrad(const uint8_t* dyq_t, const float* dys_t, co
   return launched(fp8q::launch_gemm(a, stream));
 }
 
+fp8q_status fp8q_gemm_fprop_quant(const uint8_t* xq, const float* xs, const uint8_t* wq, const float* ws, int64_t M,
+                                  int64_t N, int64_t K, void* y, int64_t ld_y, uint8_t* yq, int64_t ld_yq, float* ys,
+                                  int64_t ld_ys, int exact, hipStream_t stream) {
+  if (exact != 0 && exact != 1) return FP8Q_ERR_SHAPE;
+  return fp8q_gemm_fprop_impl(exact, xq, xs, wq, ws, M, N, K, y, FP8Q_BF16, ld_y, stream, yq, ld_yq, ys, ld_ys, true);
+}
+fp8q_status fp8q_gemm_dgrad_quant(const uint8_t* dyq, const float* dys, const uint8_t* wq_t, const float* ws,
+                                  int64_t M, int64_t N, int64_t K, void* dx, int64_t ld_dx, uint8_t* dxq,
+                                  int64_t ld_dxq, float* dxs, int64_t ld_dxs, int exact, hipStream_t stream) {
+  if (exact != 0 && exact != 1) return FP8Q_ERR_SHAPE;
+  return fp8q_gemm_dgrad_impl(exact, dyq, dys, wq_t, ws, M, N, K, dx, FP8Q_BF16, ld_dx, stream, dxq, ld_dxq, dxs,
+                              ld_dxs, true);
+}
 fp8q_status fp8q_gemm_fprop(const uint8_t* xq, const float* xs, const uint8_t* wq, const float* ws, int64_t M,
                             int64_t N, int64_t K, void* y, fp8q_dtype yt, int64_t ld_y, hipStream_t stream) {
   return fp8q_gemm_fprop_impl(0, xq, xs, wq, ws, M, N, K, y, yt, ld_y, stream);

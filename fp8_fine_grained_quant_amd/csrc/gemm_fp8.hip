@@ -144,7 +144,7 @@ __device__ __forceinline__ void row_scales(float v, float k, float (&out)[4]) {
 
 }  // namespace
 
-template <int SB_MODE, int OUT_F32, bool GROUPED, bool KG, bool SC4, bool EX>
+template <int SB_MODE, int OUT_F32, bool GROUPED, bool KG, bool SC4, bool EX, bool QO>
 __global__ __launch_bounds__(kNT) void k_gemm_fp8(GemmArgs p) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
   typedef Stage<SB_MODE, SC4> S;
@@ -454,7 +454,13 @@ __global__ __launch_bounds__(kNT) void k_gemm_fp8(GemmArgs p) {
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   __builtin_amdgcn_s_barrier();
   fence();
-  store_tile<kTM, kTN, OUT_F32, OUT_F32 ? 16 : 32>(acc, st0 + w * 12288, po, tc.m0 + w * 64, tc.mend, tc.n0, lane);
+  if constexpr (QO) {
+    static_assert(!OUT_F32 && !KG && SB_MODE == kSbBlock, "fused output quantization: BF16 Fprop/Dgrad only");
+    store_tile_q<kTM, kTN, 32>(acc, st0 + w * 12288, po, tc.m0 + w * 64, tc.mend, tc.n0, lane);
+  } else {
+    store_tile<kTM, kTN, OUT_F32, OUT_F32 ? 16 : 32>(acc, st0 + w * 12288, po, tc.m0 + w * 64, tc.mend, tc.n0,
+                                                   lane);
+  }
 #endif  // __HIP_DEVICE_COMPILE__
 }
 
@@ -489,7 +495,7 @@ static_assert(kWIB == kTM, "one B load per slot of the last column");
 static_assert(kWDmaA <= kWDmaSlots && kWFirstSlot + kWDmaSlots <= kTM * (kTN - 1), "A loads between the barriers");
 static_assert(4 * kBM * kBK + 4 * 2 * kMaxChunks + 4 * 2 * 256 * 4 + 1024 <= 160 * 1024, "LDS of one CU");
 
-template <int OUT_F32, bool GROUPED>
+template <int OUT_F32, bool GROUPED, bool QO>
 __global__ __launch_bounds__(kWNT) void k_gemm_fp8_wide(GemmArgs p) {
 #if defined(__HIP_DEVICE_COMPILE__)
   __shared__ __attribute__((aligned(16))) uint8_t sa0[kBM * kBK];
@@ -687,8 +693,13 @@ __global__ __launch_bounds__(kWNT) void k_gemm_fp8_wide(GemmArgs p) {
   __builtin_amdgcn_s_barrier();
   fence();
   uint8_t* const ep = (w >> 1) == 0 ? sa0 : (w >> 1) == 1 ? sa1 : (w >> 1) == 2 ? sb0 : sb1;
-  store_tile<kTM, kTN, OUT_F32, OUT_F32 ? 16 : 32>(acc, ep + (w & 1) * 12288, p, tc.m0 + wr * 64, tc.mend,
-                                                 tc.n0 + wc * 128, lane);
+  if constexpr (QO) {
+    static_assert(!OUT_F32 && !GROUPED, "fused output quantization: BF16 Fprop/Dgrad only");
+    store_tile_q<kTM, kTN, 32>(acc, ep + (w & 1) * 12288, p, tc.m0 + wr * 64, tc.mend, tc.n0 + wc * 128, lane);
+  } else {
+    store_tile<kTM, kTN, OUT_F32, OUT_F32 ? 16 : 32>(acc, ep + (w & 1) * 12288, p, tc.m0 + wr * 64, tc.mend,
+                                                   tc.n0 + wc * 128, lane);
+  }
 #endif  // __HIP_DEVICE_COMPILE__
 }
 
@@ -922,14 +933,16 @@ __global__ __launch_bounds__(kWNT) void k_gemm_fp8_wide_row(GemmArgs p) {
 
 namespace {
 
-template <int SB_MODE, int OUT_F32, bool GROUPED, bool KG = false, bool SC4 = false, bool EX = false>
+template <int SB_MODE, int OUT_F32, bool GROUPED, bool KG = false, bool SC4 = false, bool EX = false,
+          bool QO = false>
 hipError_t launch_one(const GemmArgs& a, hipStream_t st) {
   const int64_t tiles_n = a.N / kBN, tiles_m = (a.M + kBM - 1) / kBM;
   const int64_t tiles = KG ? a.E * 8 * ((tiles_m * tiles_n + 7) / 8)  // every expert: 8 XCD shares
                         : GROUPED ? (tiles_m + a.E) * tiles_n             // upper bound: a partial tile per expert
                                   : tiles_m * tiles_n;
   if (tiles <= 0) return hipSuccess;
-  hipLaunchKernelGGL((k_gemm_fp8<SB_MODE, OUT_F32, GROUPED, KG, SC4, EX>), dim3((uint32_t)tiles), dim3(kNT), 0, st, a);
+  hipLaunchKernelGGL((k_gemm_fp8<SB_MODE, OUT_F32, GROUPED, KG, SC4, EX, QO>), dim3((uint32_t)tiles), dim3(kNT), 0, st,
+                     a);
   return hipGetLastError();
 }
 
@@ -954,6 +967,9 @@ static bool use_wide_tile(const GemmArgs& a) {
 static hipError_t launch_exact(const GemmArgs& a, hipStream_t st) {
   const bool sc4 = a.ld_sa % 4 == 0 && (reinterpret_cast<uintptr_t>(a.sa) & 15) == 0;
   const bool g = a.offsets != nullptr;
+  if (a.qo != nullptr)  // fused output quantization (BF16 Fprop / Dgrad)
+    return sc4 ? launch_one<kSbBlock, 0, false, false, true, true, true>(a, st)
+               : launch_one<kSbBlock, 0, false, false, false, true, true>(a, st);
   if (a.sb_mode == kSbRow) return launch_one<kSbRow, 1, false, false, false, true>(a, st);
   if (sc4) {
     if (g) return a.out_f32 ? launch_one<kSbBlock, 1, true, false, true, true>(a, st)
@@ -986,16 +1002,25 @@ hipError_t launch_gemm_fp8(const GemmArgs& a, hipStream_t st) {
     if (a.k_grouped) return launch_one<kSbRow, 1, true, true>(a, st);
     return launch_one<kSbRow, 1, false>(a, st);
   }
+  if (a.qo != nullptr) {  // fused output quantization (BF16 Fprop / Dgrad)
+    if (sc4 && use_wide_tile(a)) {
+      hipLaunchKernelGGL((k_gemm_fp8_wide<0, false, true>), dim3((uint32_t)(((a.M + kBM - 1) / kBM) * (a.N / kWBN))),
+                         dim3(kWNT), 0, st, a);
+      return hipGetLastError();
+    }
+    return sc4 ? launch_one<kSbBlock, 0, false, false, true, false, true>(a, st)
+               : launch_one<kSbBlock, 0, false, false, false, false, true>(a, st);
+  }
   // the 256 x 256 tile when it leaves no more than half of the chip idle
   if (sc4 && !(a.out_f32 && a.offsets != nullptr) && use_wide_tile(a)) {  // no FP32-output grouped instantiation
     const int64_t tn = a.N / kWBN, tm = (a.M + kBM - 1) / kBM;
     const int64_t tiles = a.offsets != nullptr ? (tm + a.E) * tn : tm * tn;  // grouped: upper bound
     if (a.offsets != nullptr)
-      hipLaunchKernelGGL((k_gemm_fp8_wide<0, true>), dim3((uint32_t)tiles), dim3(kWNT), 0, st, a);
+      hipLaunchKernelGGL((k_gemm_fp8_wide<0, true, false>), dim3((uint32_t)tiles), dim3(kWNT), 0, st, a);
     else if (a.out_f32)
-      hipLaunchKernelGGL((k_gemm_fp8_wide<1, false>), dim3((uint32_t)tiles), dim3(kWNT), 0, st, a);
+      hipLaunchKernelGGL((k_gemm_fp8_wide<1, false, false>), dim3((uint32_t)tiles), dim3(kWNT), 0, st, a);
     else
-      hipLaunchKernelGGL((k_gemm_fp8_wide<0, false>), dim3((uint32_t)tiles), dim3(kWNT), 0, st, a);
+      hipLaunchKernelGGL((k_gemm_fp8_wide<0, false, false>), dim3((uint32_t)tiles), dim3(kWNT), 0, st, a);
     return hipGetLastError();
   }
   // row scales in 16-byte blocks of 4 chunks when every scale row is 16-byte aligned

@@ -163,4 +163,63 @@ __device__ __forceinline__ void store_tile(const float (&acc)[TM][TN][4], uint8_
   }
 }
 
+// The epilogue with the output's own quantization fused in (BF16 output):
+// every wave's strip is 128 columns wide and starts on a multiple of 128, so
+// each of its rows holds exactly one 1x128 group of the output.  Each value
+// is first rounded to BF16 (RNE); the group's max-abs, scale and codes are
+// then taken from those BF16 values with the quantizers' own arithmetic
+// (group_scale, pack4_e4m3), so the codes and scales equal what
+// quant_act_1x128 computes from the stored BF16 output.  The BF16 values
+// leave through store_tile (skipped when p.C is NULL); the scaled values are
+// staged through the wave's LDS region in passes of 16 rows so that every
+// code store is a full 16-byte row segment.  The accumulators are only read.
+template <int TM, int TN, int ER>
+__device__ __forceinline__ void store_tile_q(const float (&acc)[TM][TN][4], uint8_t* ep, const GemmArgs& p,
+                                             int64_t row0, int64_t mend, int col0, int lane) {
+  static_assert(TN == 8, "a wave's strip is one 128-column group wide");
+  constexpr int P = 128 * 4 + 16;  // padded LDS row pitch of the scaled values
+  const int g = lane >> 4, l16 = lane & 15;
+  auto rounded = [](float v) { return bf16_to_f32(f32_to_bf16_rne(v)); };
+  if (p.C != nullptr) {
+    store_tile<TM, TN, 0, ER>(acc, ep, p, row0, mend, col0, lane);
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the staging area is read out
+    __builtin_amdgcn_wave_barrier();
+  }
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {  // one 16-row sub-tile per pass
+    if (i) {
+      __builtin_amdgcn_s_waitcnt(0xC07F);
+      __builtin_amdgcn_wave_barrier();
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      uint32_t m = 0;
+#pragma unroll
+      for (int j = 0; j < TN; ++j) m = max(m, abs_bits(rounded(acc[i][j][r])));
+      m = row16_max_u32(m);  // the 16 lanes of lane group g hold the row's 128 columns
+      float sc, inv;
+      group_scale(__uint_as_float(m), sc, inv);
+      const int64_t row = row0 + 16 * i + 4 * g + r;
+      if (l16 == 0 && row < mend) p.so[row * p.ld_so + (col0 >> 7)] = sc;
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        *reinterpret_cast<float*>(ep + (4 * g + r) * P + 4 * (16 * j + l16)) = rounded(acc[i][j][r]) * inv;
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    __builtin_amdgcn_wave_barrier();
+    // lane (rl = lane / 8, ch = lane % 8): 16 consecutive values of row rl
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+      const int rl = it * 8 + (lane >> 3), ch = lane & 7;
+      const int64_t row = row0 + 16 * i + rl;
+      const float4* src = reinterpret_cast<const float4*>(ep + rl * P + 64 * ch);
+      const float4 v0 = src[0], v1 = src[1], v2 = src[2], v3 = src[3];
+      if (row >= mend) continue;
+      const uint32_t w0 = pack4_e4m3(v0.x, v0.y, v0.z, v0.w), w1 = pack4_e4m3(v1.x, v1.y, v1.z, v1.w);
+      const uint32_t w2 = pack4_e4m3(v2.x, v2.y, v2.z, v2.w), w3 = pack4_e4m3(v3.x, v3.y, v3.z, v3.w);
+      st_stream16<0>(p.qo + row * p.ld_qo + col0 + 16 * ch, w0, w1, w2, w3);
+    }
+  }
+}
+
 }  // namespace fp8q

@@ -58,6 +58,13 @@ struct GemmArgs {
   // operands), and writes its own output C + e*c_estride; M, N are per expert
   int k_grouped;
   int64_t c_estride;
+  // fused output quantization (BF16 output only; qo == NULL: none): the 1x128
+  // E4M3 codes qo [M, N] (row stride ld_qo bytes) and scales so [M, N/128]
+  // (row stride ld_so) of the BF16-rounded output, as quant_act_1x128 would
+  // produce them from C; C may then be NULL (codes only)
+  uint8_t* qo;
+  float* so;
+  int64_t ld_qo, ld_so;
 };
 
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t st);

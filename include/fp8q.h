@@ -269,6 +269,35 @@ fp8q_status fp8q_grouped_gemm_wgrad(const uint8_t* dyq_t, const float* dys_t, co
                                     hipStream_t stream);
 
 /*
+ * Fprop and Dgrad with the output's own quantization fused into the epilogue.
+ * The BF16 output of each product is the next layer's FP8 input ("DeepSeek
+ * FP8 Training", Fprop list: Y leaves the GEMM in BF16 and the following
+ * layer's input is quantized 1x128; input-gradient list: dX feeds the layer
+ * below), and activations are kept and passed on in FP8 (the innerforce.co.kr
+ * excerpt of the DeepSeek-V3 report, paragraph on the FP8 framework).  Each
+ * call writes, besides the BF16 output, its 1x128 E4M3 codes and FP32 scales,
+ * computed from the BF16-rounded values with the quantizers' arithmetic: the
+ * codes and scales are bit for bit those of fp8q_quant_act_1x128 applied to
+ * the BF16 output, which this saves reading back.
+ *   fprop: arguments as fp8q_gemm_fprop with yt = BF16; yq [M, N] codes (row
+ *          stride ld_yq bytes, a multiple of 16, 16-byte aligned), ys
+ *          [M, N/128] FP32 (row stride ld_ys >= N/128)
+ *   dgrad: arguments as fp8q_gemm_dgrad with dxt = BF16; dxq [M, K], dxs
+ *          [M, K/128] likewise
+ *   y / dx may be NULL: then only the codes and scales are written.
+ *   exact = 0: the FP8 matrix instruction; 1: the exact-accumulation form
+ *   (see the _exact variants below); any other value: FP8Q_ERR_SHAPE.
+ * Rules and errors otherwise as fp8q_gemm_fprop / fp8q_gemm_dgrad; NULL codes
+ * or scales give FP8Q_ERR_NULL.
+ */
+fp8q_status fp8q_gemm_fprop_quant(const uint8_t* xq, const float* xs, const uint8_t* wq, const float* ws,
+                                  int64_t M, int64_t N, int64_t K, void* y, int64_t ld_y, uint8_t* yq,
+                                  int64_t ld_yq, float* ys, int64_t ld_ys, int exact, hipStream_t stream);
+fp8q_status fp8q_gemm_dgrad_quant(const uint8_t* dyq, const float* dys, const uint8_t* wq_t, const float* ws,
+                                  int64_t M, int64_t N, int64_t K, void* dx, int64_t ld_dx, uint8_t* dxq,
+                                  int64_t ld_dxq, float* dxs, int64_t ld_dxs, int exact, hipStream_t stream);
+
+/*
  * Exact-accumulation variants.  Same arguments, rules, layouts and results
  * definition as the four GEMMs above; only the in-chunk arithmetic differs.
  * gfx950's FP8 matrix instruction adds the 8 products of each group of 8

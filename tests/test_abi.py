@@ -117,6 +117,27 @@ def test_gemm_argument_errors(lib):
     assert gg(A16, A16, A16, A16, A16 + 2, 4, 64, 128, 256, A16, 0, 128, None) == ALIGN
 
 
+def test_fused_quant_argument_errors(lib):
+    fq_ = lib.fp8q_gemm_fprop_quant
+    #          xq   xs   wq   ws   M   N    K    y    ldy  yq   ldyq ys  ldys ex
+    assert fq_(A16, A16, A16, A16, 64, 256, 256, A16, 256, None, 256, A16, 2, 0, None) == NULL
+    assert fq_(A16, A16, A16, A16, 64, 256, 256, A16, 256, A16, 256, None, 2, 0, None) == NULL
+    assert fq_(A16, A16, A16, A16, 64, 256, 256, A16, 256, A16, 248, A16, 2, 0, None) == STRIDE  # ld_yq < N
+    assert fq_(A16, A16, A16, A16, 64, 256, 256, A16, 256, A16, 256, A16, 1, 0, None) == STRIDE  # ld_ys < N/128
+    assert fq_(A16, A16, A16, A16, 64, 256, 256, A16, 256, A16, 264, A16, 2, 0, None) == ALIGN   # ld_yq % 16
+    assert fq_(A16, A16, A16, A16, 64, 256, 256, A16, 256, A16 + 8, 256, A16, 2, 0, None) == ALIGN
+    assert fq_(A16, A16, A16, A16, 64, 256, 256, A16, 250, A16, 256, A16, 2, 0, None) == STRIDE  # ld_y < N
+    assert fq_(A16, A16, A16, A16, 64, 256, 256, A16, 256, A16, 256, A16, 2, 2, None) == SHAPE   # exact flag
+    assert fq_(A16, A16, A16, A16, 64, 200, 256, A16, 256, A16, 256, A16, 2, 0, None) == SHAPE   # N % 128
+    assert fq_(A16, A16, A16, A16, 0, 256, 256, None, 256, None, 256, None, 2, 0, None) == OK    # M = 0
+    dq = lib.fp8q_gemm_dgrad_quant
+    #         dyq  dys  wq_t ws   M   N    K    dx   ldx  dxq  ldq  dxs lds ex
+    assert dq(A16, A16, A16, A16, 64, 256, 384, A16, 384, None, 384, A16, 3, 0, None) == NULL
+    assert dq(A16, A16, A16, A16, 64, 256, 384, A16, 384, A16, 256, A16, 3, 0, None) == STRIDE  # ld_dxq < K
+    assert dq(A16, A16, A16, A16, 64, 256, 384, A16, 384, A16, 384, A16, 2, 0, None) == STRIDE  # ld_dxs < K/128
+    assert dq(A16, A16, A16, A16, 64, 256, 384, A16, 384, A16, 384, A16, 3, -1, None) == SHAPE
+
+
 def test_grouped_backward_argument_errors(lib):
     tg = lib.fp8q_quant_transpose_grouped
     # rows 300, E 4: capacity 128 * (2 + 4) = 768 token columns, 6 scale columns
