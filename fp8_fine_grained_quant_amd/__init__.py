@@ -47,7 +47,8 @@ EXPORTS = ["fp8q_status_string", "fp8q_set_gemm_tile", "fp8q_quant_act_1x128", "
            "fp8q_grouped_gemm_exact", "fp8q_quant_transpose_grouped", "fp8q_grouped_gemm_dgrad",
            "fp8q_grouped_gemm_wgrad", "fp8q_quant_act_transpose", "fp8q_quant_mx_1x32",
            "fp8q_quant_mx_transpose", "fp8q_gemm_mx", "fp8q_grouped_gemm_mx",
-           "fp8q_grouped_gemm_mx_dgrad", "fp8q_gemm_fprop_quant", "fp8q_gemm_dgrad_quant"]
+           "fp8q_grouped_gemm_mx_dgrad", "fp8q_gemm_fprop_quant", "fp8q_gemm_dgrad_quant",
+           "fp8q_gemm_fprop_interval"]
 
 
 class Fp8qError(RuntimeError):
@@ -89,6 +90,7 @@ def load_library(path=LIB_PATH):
         "fp8q_grouped_gemm_mx_dgrad": ([P, P, P, P, P, I64, I64, I64, I64, P, I32, I64, P], I32),
         "fp8q_gemm_fprop_quant": ([P, P, P, P, I64, I64, I64, P, I64, P, I64, P, I64, I32, P], I32),
         "fp8q_gemm_dgrad_quant": ([P, P, P, P, I64, I64, I64, P, I64, P, I64, P, I64, I32, P], I32),
+        "fp8q_gemm_fprop_interval": ([P, P, P, P, I64, I64, I64, P, I64, I64, P], I32),
     }
     for name in ["fp8q_gemm_fprop", "fp8q_gemm_dgrad", "fp8q_gemm_wgrad", "fp8q_grouped_gemm"]:
         sig[name + "_exact"] = sig[name]
@@ -278,6 +280,24 @@ def fp8q_gemm_fprop_quant(xq, xs, wq, ws, y, yq, ys, stream=None, exact=False):
                                                  _ld(y) if y is not None else 0, _ptr(yq), _ld(yq), _ptr(ys),
                                                  _ld(ys), int(bool(exact)), _stream(stream)),
            "fp8q_gemm_fprop_quant")
+
+
+def fp8q_gemm_fprop_interval(xq, xs, wq, ws, y, interval, stream=None):
+    """The promotion-interval study: Fprop into FP32 y [M, N] with partials
+    chained through the matrix instruction over `interval` K (128, 256, 512,
+    1024; 0 = all of K); scales must be constant over each interval."""
+    m, k = xq.shape
+    n = wq.shape[0]
+    _expect(xq, (m, k), _U8, "xq")
+    _expect(xs, (m, _cdiv(k, 128)), _F32, "xs")
+    _expect(wq, (n, k), _U8, "wq")
+    _expect(ws, (_cdiv(n, 128), _cdiv(k, 128)), _F32, "ws")
+    _expect(y, (m, n), _F32, "y")
+    _on_gpu(xq, xs, wq, ws, y)
+    _contig(xq, xs, wq, ws)
+    _check(load_library().fp8q_gemm_fprop_interval(_ptr(xq), _ptr(xs), _ptr(wq), _ptr(ws), m, n, k, _ptr(y),
+                                                    _ld(y), int(interval), _stream(stream)),
+           "fp8q_gemm_fprop_interval")
 
 
 def fp8q_gemm_dgrad_quant(dyq, dys, wq_t, ws, dx, dxq, dxs, stream=None, exact=False):

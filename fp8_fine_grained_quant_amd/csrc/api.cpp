@@ -355,6 +355,30 @@ fp8q_status fp8q_gemm_dgrad_quant(const uint8_t* dyq, const float* dys, const ui
   return fp8q_gemm_dgrad_impl(exact, dyq, dys, wq_t, ws, M, N, K, dx, FP8Q_BF16, ld_dx, stream, dxq, ld_dxq, dxs,
                               ld_dxs, true);
 }
+fp8q_status fp8q_gemm_fprop_interval(const uint8_t* xq, const float* xs, const uint8_t* wq, const float* ws,
+                                     int64_t M, int64_t N, int64_t K, float* y, int64_t ld_y, int64_t interval,
+                                     hipStream_t stream) {
+  int chunks = -1;
+  if (interval == 0) chunks = 0;
+  else if (interval == 128 || interval == 256 || interval == 512 || interval == 1024) chunks = (int)(interval / 128);
+  if (chunks < 0) return FP8Q_ERR_SHAPE;
+  if (M < 0 || N < 0 || K < 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim) return FP8Q_ERR_SHAPE;
+  if (N % 128 != 0 || K % 512 != 0 || K > kMaxContraction) return FP8Q_ERR_SHAPE;
+  if (M == 0 || N == 0) return FP8Q_OK;
+  if (K == 0) return FP8Q_ERR_SHAPE;
+  if (!xq || !xs || !wq || !ws) return FP8Q_ERR_NULL;
+  const fp8q_status c = check_gemm_out(y, FP8Q_F32, ld_y, N);
+  if (c != FP8Q_OK) return c;
+  if (!aligned16(xq) || !aligned16(wq) || !aligned16(xs) || !aligned4(ws)) return FP8Q_ERR_ALIGN;
+  if (cdiv(M, 256) * (N / 128) > kMaxGroups) return FP8Q_ERR_SHAPE;
+  GemmArgs a{};
+  a.A = xq; a.B = wq; a.sa = xs; a.sb = ws; a.C = y;
+  a.lda = K; a.ldb = K; a.ld_sa = K / 128; a.sb_rs = K / 128; a.sb_cs = 1; a.ldc = ld_y;
+  a.M = M; a.N = N; a.K = K;
+  a.sb_mode = fp8q::kSbBlock; a.out_f32 = 1;
+  return launched(fp8q::launch_gemm_interval(a, chunks, stream));
+}
+
 fp8q_status fp8q_gemm_fprop(const uint8_t* xq, const float* xs, const uint8_t* wq, const float* ws, int64_t M,
                             int64_t N, int64_t K, void* y, fp8q_dtype yt, int64_t ld_y, hipStream_t stream) {
   return fp8q_gemm_fprop_impl(0, xq, xs, wq, ws, M, N, K, y, yt, ld_y, stream);

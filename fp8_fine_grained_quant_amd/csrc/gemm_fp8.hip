@@ -144,7 +144,7 @@ __device__ __forceinline__ void row_scales(float v, float k, float (&out)[4]) {
 
 }  // namespace
 
-template <int SB_MODE, int OUT_F32, bool GROUPED, bool KG, bool SC4, bool EX, bool QO>
+template <int SB_MODE, int OUT_F32, bool GROUPED, bool KG, bool SC4, bool EX, bool QO, int INTV>
 __global__ __launch_bounds__(kNT) void k_gemm_fp8(GemmArgs p) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
   typedef Stage<SB_MODE, SC4> S;
@@ -292,11 +292,27 @@ __global__ __launch_bounds__(kNT) void k_gemm_fp8(GemmArgs p) {
   float sbc_prev = 0.f; // row mode: scale of the previous chunk's last column
   float sbc_first = 0.f;  // row mode: scale of the current chunk's column 0
 
+  // Promotion interval study (INTV != 1): within an interval of INTV chunks
+  // (INTV == 0: the whole contraction) each sub-tile's partial is chained
+  // through the matrix instruction's accumulator operand, and only the
+  // interval's sum is promoted, with the scales of its last chunk (the
+  // caller makes the scales constant over each interval).  INTV == 1 is the
+  // method: a fresh partial per chunk, promoted at once.
+  v4f pch[kTM][kTN];
+  if (INTV != 1) {
+#pragma unroll
+    for (int i = 0; i < kTM; ++i)
+#pragma unroll
+      for (int j = 0; j < kTN; ++j) pch[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+  }
+  bool promote_now = true;  // INTV != 1: the chunk being promoted ends its interval
   auto promote = [&](int i, int j, float sbc) {
+    if (INTV != 1 && !promote_now) return;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const float s = ROW ? sc[i][r] * sbc : sc[i][r];
-      acc[i][j][r] = __builtin_fmaf(pp[i][r], s, acc[i][j][r]);
+      const float part = INTV == 1 ? pp[i][r] : pch[i][j][r];
+      acc[i][j][r] = __builtin_fmaf(part, s, acc[i][j][r]);
     }
   };
   auto load_sc = [&](int i) {
@@ -388,15 +404,22 @@ __global__ __launch_bounds__(kNT) void k_gemm_fp8(GemmArgs p) {
         if (EX) {
           if (j == 0) to_bf16_quarters(a[i], abf[i]);
           pp[i] = mfma_ex(abf[i], bbf);
-        } else {
+        } else if (INTV == 1) {
           pp[i] = mfma(a[i], bcur);
+        } else {
+          const bool first = INTV == 0 ? c == 0 : c % INTV == 0;
+          const v4f zero = {0.f, 0.f, 0.f, 0.f};
+          pch[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[i], bcur, first ? zero : pch[i][j], 0, 0, 0,
+                                                                       0, 0, 0);
         }
         if (t >= kSkew) {
           const int tp = t - kSkew;
+          if (INTV != 1) promote_now = INTV == 0 ? c == nk - 1 : ((c + 1) % INTV == 0 || c == nk - 1);
           promote(tp % kTM, tp / kTM, sbc[tp / kTM]);
         } else {
           // the previous chunk's last column, rows t+1; then this chunk's
           // scales for those rows (row 0's were set at the previous chunk end)
+          if (INTV != 1) promote_now = INTV != 0 && c > 0 && c % INTV == 0;
           promote(t + 1, kTN - 1, sbc_prev);
           load_sc(t + 1);
         }
@@ -446,6 +469,7 @@ __global__ __launch_bounds__(kNT) void k_gemm_fp8(GemmArgs p) {
   if (c < nk) step(c, IC<0>());
   if (c + 1 < nk) step(c + 1, IC<1>());
   // the last chunk's last column, rows 1-3 (load_sc(0) above only touched row 0)
+  promote_now = true;
 #pragma unroll
   for (int i = 1; i < kTM; ++i) promote(i, kTN - 1, sbc_prev);
 
@@ -934,15 +958,15 @@ __global__ __launch_bounds__(kWNT) void k_gemm_fp8_wide_row(GemmArgs p) {
 namespace {
 
 template <int SB_MODE, int OUT_F32, bool GROUPED, bool KG = false, bool SC4 = false, bool EX = false,
-          bool QO = false>
+          bool QO = false, int INTV = 1>
 hipError_t launch_one(const GemmArgs& a, hipStream_t st) {
   const int64_t tiles_n = a.N / kBN, tiles_m = (a.M + kBM - 1) / kBM;
   const int64_t tiles = KG ? a.E * 8 * ((tiles_m * tiles_n + 7) / 8)  // every expert: 8 XCD shares
                         : GROUPED ? (tiles_m + a.E) * tiles_n             // upper bound: a partial tile per expert
                                   : tiles_m * tiles_n;
   if (tiles <= 0) return hipSuccess;
-  hipLaunchKernelGGL((k_gemm_fp8<SB_MODE, OUT_F32, GROUPED, KG, SC4, EX, QO>), dim3((uint32_t)tiles), dim3(kNT), 0, st,
-                     a);
+  hipLaunchKernelGGL((k_gemm_fp8<SB_MODE, OUT_F32, GROUPED, KG, SC4, EX, QO, INTV>), dim3((uint32_t)tiles), dim3(kNT),
+                     0, st, a);
   return hipGetLastError();
 }
 
@@ -985,6 +1009,20 @@ static hipError_t launch_exact(const GemmArgs& a, hipStream_t st) {
 
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t st) {
   return a.exact ? launch_exact(a, st) : launch_gemm_fp8(a, st);
+}
+
+// The promotion-interval study: Fprop-form products (block B scales, FP32
+// output, 16-byte row-scale blocks) with the partials chained through the
+// matrix instruction over `chunks` chunks (0: the whole contraction).
+hipError_t launch_gemm_interval(const GemmArgs& a, int chunks, hipStream_t st) {
+  switch (chunks) {
+    case 1: return launch_one<kSbBlock, 1, false, false, true, false, false, 1>(a, st);
+    case 2: return launch_one<kSbBlock, 1, false, false, true, false, false, 2>(a, st);
+    case 4: return launch_one<kSbBlock, 1, false, false, true, false, false, 4>(a, st);
+    case 8: return launch_one<kSbBlock, 1, false, false, true, false, false, 8>(a, st);
+    case 0: return launch_one<kSbBlock, 1, false, false, true, false, false, 0>(a, st);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_gemm_fp8(const GemmArgs& a, hipStream_t st) {

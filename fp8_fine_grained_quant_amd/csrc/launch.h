@@ -77,6 +77,9 @@ int gemm_tile_setting();
 int device_cu_count();
 // the FP8 matrix-instruction kernel (a.exact == 0)
 hipError_t launch_gemm_fp8(const GemmArgs& a, hipStream_t st);
+// the promotion-interval study (block scales, FP32 output): partials chained
+// through the matrix instruction over `chunks` chunks (1, 2, 4, 8; 0 = all)
+hipError_t launch_gemm_interval(const GemmArgs& a, int chunks, hipStream_t st);
 
 // Microscaling (MXFP8 E4M3) quantizers: one E8M0 scale byte per 32
 // consecutive elements, along rows (quant_mx) or along columns with the

@@ -298,6 +298,29 @@ fp8q_status fp8q_gemm_dgrad_quant(const uint8_t* dyq, const float* dys, const ui
                                   int64_t ld_dxq, float* dxs, int64_t ld_dxs, int exact, hipStream_t stream);
 
 /*
+ * Promotion-interval study (numerics only; not a step of the method).  The
+ * method promotes the FP8 partial of every 128-long K chunk into FP32 ("How
+ * does the unified E4M3 format contribute to the efficiency of DeepSeek-V3",
+ * "Enhanced Numerical Stability": promotion at fixed intervals; the
+ * innerforce.co.kr excerpt of the DeepSeek-V3 report, paragraph after Figure
+ * 7 (a), where the interval is lost in the extracted text).  This entry point
+ * computes the Fprop product with the partial of each 16x16 output block
+ * chained through the matrix instruction's accumulator operand over
+ * `interval` elements of K (128, 256, 512 or 1024; 0 = the whole
+ * contraction) and promoted only at the end of each interval, with the
+ * scales of the interval's last chunk.  The result is the Fprop product only
+ * if xs and ws are constant over every interval (for instance all 1, which
+ * operands whose groups reach exactly 448 give); the library does not check.
+ * interval = 128 is fp8q_gemm_fprop with FP32 output.
+ *   Arguments as fp8q_gemm_fprop with yt = FP32 (y, ld_y).
+ * Rules: K % 512 == 0 (16-byte scale rows), N % 128 == 0, xs 16-byte
+ * aligned, interval as above, else FP8Q_ERR_SHAPE / FP8Q_ERR_ALIGN.
+ */
+fp8q_status fp8q_gemm_fprop_interval(const uint8_t* xq, const float* xs, const uint8_t* wq, const float* ws,
+                                     int64_t M, int64_t N, int64_t K, float* y, int64_t ld_y, int64_t interval,
+                                     hipStream_t stream);
+
+/*
  * Exact-accumulation variants.  Same arguments, rules, layouts and results
  * definition as the four GEMMs above; only the in-chunk arithmetic differs.
  * gfx950's FP8 matrix instruction adds the 8 products of each group of 8

@@ -48,7 +48,7 @@ def bf16_ulp(v):
     return np.exp2(e - 7)
 
 
-def check_gemm(y, y_ref, s_ref, out_bf16, what, exact=True, nk=None):
+def check_gemm(y, y_ref, s_ref, out_bf16, what, exact=True, nk=None, strict=False):
     """Elementwise bar, S = sum_k |a_k b_k| of the exact contraction.
 
     exact=True (the *_exact entry points): FP32 output |y - Y_ref| <= 1e-5 S;
@@ -58,7 +58,11 @@ def check_gemm(y, y_ref, s_ref, out_bf16, what, exact=True, nk=None):
     keeps 14 bits below the largest of each group of 8 products and truncates
     the rest, so each group may lose < 7 * 2^-13 of its largest product:
     |y - Y_ref| <= 2^-10 S + (nk + 17) 2^-24 S (+ ulp_bf16 for BF16 output),
-    and for FP32 output the mean of |y - Y_ref| / S must stay below 5e-5."""
+    and for FP32 output the mean of |y - Y_ref| / S must stay below 5e-5.
+
+    strict=True (FP8 entry points on the configurations' full-size BF16
+    products, where it holds): the exact bar as well, no element outside
+    ulp_bf16(Y_ref) + 1e-5 S."""
     y = np.asarray(y, np.float64)
     err = np.abs(y - y_ref)
     s = np.maximum(s_ref, 1e-300)
@@ -91,6 +95,8 @@ def check_gemm(y, y_ref, s_ref, out_bf16, what, exact=True, nk=None):
         raise AssertionError(f"{what}: {int(over.sum())} of {y.size} outside tolerance; first: {detail}")
     if not exact and not out_bf16 and y.size:
         assert stats["mean_err_over_S"] <= 5e-5, stats
+    if strict:
+        assert stats["n_over_1e-5_S"] == 0, stats
     return stats
 
 

@@ -138,6 +138,18 @@ def test_fused_quant_argument_errors(lib):
     assert dq(A16, A16, A16, A16, 64, 256, 384, A16, 384, A16, 384, A16, 3, -1, None) == SHAPE
 
 
+def test_interval_study_argument_errors(lib):
+    f = lib.fp8q_gemm_fprop_interval
+    #        xq   xs   wq   ws   M   N    K    y    ldy  interval
+    assert f(A16, A16, A16, A16, 64, 128, 512, A16, 128, 384, None) == SHAPE    # not a supported interval
+    assert f(A16, A16, A16, A16, 64, 128, 512, A16, 128, 2048, None) == SHAPE
+    assert f(A16, A16, A16, A16, 64, 128, 384, A16, 128, 128, None) == SHAPE    # K % 512
+    assert f(A16, A16 + 4, A16, A16, 64, 128, 512, A16, 128, 0, None) == ALIGN  # xs 16-byte
+    assert f(A16, A16, A16, A16, 64, 128, 512, A16, 120, 256, None) == STRIDE
+    assert f(A16, None, A16, A16, 64, 128, 512, A16, 128, 512, None) == NULL
+    assert f(A16, A16, A16, A16, 0, 128, 512, None, 128, 1024, None) == OK      # M = 0
+
+
 def test_grouped_backward_argument_errors(lib):
     tg = lib.fp8q_quant_transpose_grouped
     # rows 300, E 4: capacity 128 * (2 + 4) = 768 token columns, 6 scale columns

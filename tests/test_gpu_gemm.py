@@ -82,7 +82,7 @@ def test_fprop_linear_config_full_size_sampled_rows(exact):
     y = _run_fprop(x, w, torch.bfloat16, exact)
     rows = sample_rows(4096, 64, 11, must=(0, 255, 256, 4095))
     y_ref, s_ref = _ref_rows_fprop(x, w, rows)
-    check_gemm(f32(y)[rows], y_ref, s_ref, True, "C2 fprop", exact, nk=56)
+    check_gemm(f32(y)[rows], y_ref, s_ref, True, "C2 fprop", exact, nk=56, strict=True)
 
 
 @MODES
@@ -125,7 +125,7 @@ def test_dgrad_linear_config_full_size_sampled_rows(exact):
     log("C3 dgrad 4096x7168 (contraction 2048), 64 sampled rows")
     rows = sample_rows(4096, 64, 12, must=(0, 4095))
     y, y_ref, s_ref = _dgrad_case(dy, w, rows, exact)
-    check_gemm(y, y_ref, s_ref, True, "C3 dgrad", exact, nk=16)
+    check_gemm(y, y_ref, s_ref, True, "C3 dgrad", exact, nk=16, strict=True)
 
 
 # --------------------------------------------------------------------- Wgrad
@@ -243,4 +243,4 @@ def test_grouped_moe_config_sampled_rows(exact):
     rows = np.array(sorted(set(r for r in rows if 0 <= r < off[-1])), dtype=np.int64)
     log(f"checking experts {pick}, {len(rows)} rows")
     y, y_ref, s_ref, _, _ = _grouped_case(x, w, offsets, rows, exact)
-    check_gemm(y, y_ref, s_ref, True, "C5 grouped", exact, nk=56)
+    check_gemm(y, y_ref, s_ref, True, "C5 grouped", exact, nk=56, strict=True)

@@ -138,7 +138,7 @@ def test_grouped_dgrad_moe_config_sampled_rows():
         wo, wso, _ = oracle.quant_weight_128x128(f32(w[int(ex)]))
         sel = np.nonzero(experts == ex)[0]
         y_ref[sel], s_ref[sel] = oracle.dgrad_ref(dyo[sel], dyso[sel], wo, wso)
-    check_gemm(f32(dx)[rows], y_ref, s_ref, True, "C6 grouped dgrad", False, nk=n // 128)
+    check_gemm(f32(dx)[rows], y_ref, s_ref, True, "C6 grouped dgrad", False, nk=n // 128, strict=True)
 
 
 # ---------------------------------------------------------------- grouped Wgrad
