@@ -4,11 +4,13 @@ on one MI355X.
 
 One step = one pass of the whole hot path over one batch of synthetic inputs:
   linear layer X [4096,7168] bf16, W [2048,7168] fp32, dY [4096,2048] bf16
-    quant_act(X) -> quant_weight(W, +q_t) -> Fprop Y = X W^T (bf16)
-    quant_act(dY) -> Dgrad dX = dY W (bf16)
-    quant_transpose(X), quant_transpose(dY) -> Wgrad dW = dY^T X (fp32)
+    quant_batch[quant_weight(W, +q_t), quant_act_transpose(X)] -> Fprop Y = X W^T (bf16)
+    quant_act_transpose(dY) -> Dgrad dX = dY W (bf16)
+    Wgrad dW = dY^T X (fp32) on the transposed codes kept from both
   MoE layer X [16384,7168] bf16 routed to 32 experts W_e [2048,7168] fp32
     quant_act(X) -> quant_weight(W stacked) -> grouped Fprop (bf16)
+The same step with every quantizer as its own launch (quant_act X, quant_weight
+W, quant_act dY, quant_transpose X and dY) is timed and reported beside it.
 Inputs are generated and resident in HBM before the timed region.
 
 Reported beside the step (not part of its value): the microscaling (MXFP8)
@@ -67,8 +69,15 @@ def build_workload(H, dev):
                 wm=g(H["wm"]).reshape(-1, H["wm"].shape[2]), off=g(H["off"]), dym=g(H["dym"]))
 
 
-def make_ops(L, dev):
-    """The step's kernels as (name, launch, kind, algorithmic work per launch)."""
+def make_ops(L, dev, form="batched"):
+    """The step's kernels as (name, launch, kind, algorithmic work per launch).
+
+    form "batched" (the step): the layer input X is quantized once into its
+    row and transposed codes (the transposed ones are kept for the weight
+    gradient), in the same grid as the weight W; dY likewise once into both
+    layouts.  form "separate": every quantizer of the path is its own launch
+    (1x128 X, 128x128 W, 1x128 dY, then the two transposing quantizers for
+    the weight gradient), as the path's steps are listed."""
     import torch
     import fp8_fine_grained_quant_amd as fq
 
@@ -86,6 +95,33 @@ def make_ops(L, dev):
         ym=e(Mm, Nm, dt=torch.bfloat16),
     )
     act_bytes = lambda r, c, es: r * c * (es + 1) + r * cdiv(c, 128) * 4
+    w_bytes = N * K * 6 + cdiv(N, 128) * cdiv(K, 128) * 4
+    dual_bytes = lambda r, c: r * c * 4 + (r * cdiv(c, 128) + c * cdiv(r, 128)) * 4
+    moe = [
+        ("quant_act X_moe", lambda: fq.fp8q_quant_act_1x128(L["xm"], O["xmq"], O["xms"]), "hbm",
+         act_bytes(Mm, K, 2)),
+        ("quant_weight W_moe", lambda: fq.fp8q_quant_weight_128x128(L["wm"], O["wmq"], None, O["wms"]), "hbm",
+         E * Nm * K * 5 + cdiv(E * Nm, 128) * cdiv(K, 128) * 4),
+        ("grouped_gemm", lambda: fq.fp8q_grouped_gemm(O["xmq"], O["xms"], O["wmq"].view(E, Nm, K),
+                                                      O["wms"].view(E, Nm // 128, K // 128), L["off"], O["ym"]),
+         "mfma", 2.0 * Mm * Nm * K),
+    ]
+    if form == "batched":
+        ops = [
+            ("quant_batch W (+q_t) + X (rows + cols)",
+             lambda: fq.fp8q_quant_batch([("weight", L["w"], O["wq"], O["wq_t"], O["ws"]),
+                                          ("act_transpose", L["x"], O["xq"], O["xs"], O["xq_t"], O["xs_t"])]),
+             "hbm", w_bytes + dual_bytes(M, K)),
+            ("gemm_fprop", lambda: fq.fp8q_gemm_fprop(O["xq"], O["xs"], O["wq"], O["ws"], O["y"]), "mfma",
+             2.0 * M * N * K),
+            ("quant_act_transpose dY", lambda: fq.fp8q_quant_act_transpose(L["dy"], O["dyq"], O["dys"], O["dyq_t"],
+                                                                          O["dys_t"]), "hbm", dual_bytes(M, N)),
+            ("gemm_dgrad", lambda: fq.fp8q_gemm_dgrad(O["dyq"], O["dys"], O["wq_t"], O["ws"], O["dx"]), "mfma",
+             2.0 * M * N * K),
+            ("gemm_wgrad", lambda: fq.fp8q_gemm_wgrad(O["dyq_t"], O["dys_t"], O["xq_t"], O["xs_t"], O["dw"]),
+             "mfma", 2.0 * M * N * K),
+        ] + moe
+        return ops, O
     ops = [
         ("quant_act X", lambda: fq.fp8q_quant_act_1x128(L["x"], O["xq"], O["xs"]), "hbm", act_bytes(M, K, 2)),
         ("quant_weight W (+q_t)", lambda: fq.fp8q_quant_weight_128x128(L["w"], O["wq"], O["wq_t"], O["ws"]),
@@ -101,14 +137,7 @@ def make_ops(L, dev):
          act_bytes(M, N, 2)),
         ("gemm_wgrad", lambda: fq.fp8q_gemm_wgrad(O["dyq_t"], O["dys_t"], O["xq_t"], O["xs_t"], O["dw"]), "mfma",
          2.0 * M * N * K),
-        ("quant_act X_moe", lambda: fq.fp8q_quant_act_1x128(L["xm"], O["xmq"], O["xms"]), "hbm",
-         act_bytes(Mm, K, 2)),
-        ("quant_weight W_moe", lambda: fq.fp8q_quant_weight_128x128(L["wm"], O["wmq"], None, O["wms"]), "hbm",
-         E * Nm * K * 5 + cdiv(E * Nm, 128) * cdiv(K, 128) * 4),
-        ("grouped_gemm", lambda: fq.fp8q_grouped_gemm(O["xmq"], O["xms"], O["wmq"].view(E, Nm, K),
-                                                      O["wms"].view(E, Nm // 128, K // 128), L["off"], O["ym"]),
-         "mfma", 2.0 * Mm * Nm * K),
-    ]
+    ] + moe
     return ops, O
 
 
@@ -295,9 +324,11 @@ def tiny_gemm_latency(dev, reps=200):
 
 
 def telemetry(ops, seconds=1.5):
-    """GPU clock and power while the step runs back to back for `seconds`
-    (amdsmi, sampled every 20 ms from a thread); also the step time of that
-    sustained loop.  None with the reason if telemetry is unavailable."""
+    """GPU clock, power and activity while the step runs back to back for
+    `seconds` (amdsmi, sampled every 20 ms from a thread), and the step time
+    of that sustained loop.  Every device amdsmi lists is sampled; the one
+    reported is the one whose PCI bus matches cuda:0, else the busiest.
+    Returns the reason instead if telemetry is unavailable."""
     import threading
     import torch
     try:
@@ -307,33 +338,36 @@ def telemetry(ops, seconds=1.5):
         return {"unavailable": f"amdsmi: {ex}"}
     try:
         handles = amdsmi.amdsmi_get_processor_handles()
-        h = handles[0]
-        try:
-            want = torch.cuda.get_device_properties(0).pci_bus_id
-            for c in handles:
-                if int(amdsmi.amdsmi_get_gpu_device_bdf(c).split(":")[1], 16) == want:
-                    h = c
-        except Exception:
-            pass
-        clk, pwr = [], []
+        bus = []
+        for h in handles:
+            try:
+                bus.append(amdsmi.amdsmi_get_gpu_device_bdf(h))
+            except Exception:
+                bus.append("?")
+        samples = [{"clk": [], "pwr": [], "act": []} for _ in handles]
         stop = threading.Event()
 
         def sample():
             while not stop.is_set():
-                try:
-                    c = amdsmi.amdsmi_get_clock_info(h, amdsmi.AmdSmiClkType.GFX)
-                    clk.append(float(c.get("clk", c.get("cur_clk"))))
-                except Exception:
-                    pass
-                try:
-                    p = amdsmi.amdsmi_get_power_info(h)
-                    v = p.get("current_socket_power", "N/A")
-                    if v in ("N/A", None):
-                        v = p.get("average_socket_power", "N/A")
-                    if v not in ("N/A", None):
-                        pwr.append(float(v))
-                except Exception:
-                    pass
+                for h, smp in zip(handles, samples):
+                    try:
+                        c = amdsmi.amdsmi_get_clock_info(h, amdsmi.AmdSmiClkType.GFX)
+                        smp["clk"].append(float(c.get("clk", c.get("cur_clk"))))
+                    except Exception:
+                        pass
+                    try:
+                        p = amdsmi.amdsmi_get_power_info(h)
+                        v = p.get("current_socket_power", "N/A")
+                        if v in ("N/A", None):
+                            v = p.get("average_socket_power", "N/A")
+                        if v not in ("N/A", None):
+                            smp["pwr"].append(float(v))
+                    except Exception:
+                        pass
+                    try:
+                        smp["act"].append(float(amdsmi.amdsmi_get_gpu_activity(h)["gfx_activity"]))
+                    except Exception:
+                        pass
                 time.sleep(0.02)
 
         th = threading.Thread(target=sample, daemon=True)
@@ -350,11 +384,25 @@ def telemetry(ops, seconds=1.5):
         stop.set()
         th.join()
         med = lambda v: sorted(v)[len(v) // 2] if v else None
-        return {"sclk_mhz": {"median": med(clk), "min": min(clk) if clk else None, "max": max(clk) if clk else None,
-                             "samples": len(clk)},
-                "power_w": {"median": med(pwr), "max": max(pwr) if pwr else None, "samples": len(pwr)},
+        pick, how = None, "busiest"
+        try:
+            want = torch.cuda.get_device_properties(0).pci_bus_id
+            for k, b in enumerate(bus):
+                if b != "?" and int(b.split(":")[1], 16) == want:
+                    pick, how = k, "pci bus of cuda:0"
+        except Exception:
+            pass
+        if pick is None:
+            pick = max(range(len(handles)), key=lambda k: med(samples[k]["act"]) or 0.0)
+        smp = samples[pick]
+        return {"device": {"bdf": bus[pick], "chosen_by": how, "devices_listed": len(handles)},
+                "sclk_mhz": {"median": med(smp["clk"]), "min": min(smp["clk"]) if smp["clk"] else None,
+                             "max": max(smp["clk"]) if smp["clk"] else None, "samples": len(smp["clk"])},
+                "power_w": {"median": med(smp["pwr"]), "max": max(smp["pwr"]) if smp["pwr"] else None,
+                            "samples": len(smp["pwr"])},
+                "gfx_activity_pct": {"median": med(smp["act"]), "samples": len(smp["act"])},
                 "sustained_ms_per_step": round(dt * 1e3 / n, 4), "steps": n,
-                "note": "sampled while the step ran back to back for ~1.5 s right after the timed region"}
+                "note": "sampled while the step ran back to back for ~1.5 s, right before the timed region"}
     finally:
         try:
             amdsmi.amdsmi_shut_down()
@@ -621,11 +669,16 @@ def main():
     names = [o[0] for o in ops]
 
     stream = torch.cuda.current_stream()
-    log(f"warmup {args.warmup} steps, timing {args.steps} steps")
-    ms_step, kernels = time_ops(ops, args.steps, args.warmup, stream)
+    # the step under sustained load first: clock, power and activity, and the
+    # GPU at its working clocks before the timed region
     log("telemetry: the step back to back for ~1.5 s")
     tele = telemetry(ops)
     log(f"telemetry {tele}")
+    log(f"warmup {args.warmup} steps, timing {args.steps} steps")
+    ms_step, kernels = time_ops(ops, args.steps, args.warmup, stream)
+    sops, _ = make_ops(L, dev, form="separate")
+    log(f"the step with separate quantizer launches: warmup {args.warmup}, timing {args.steps} steps")
+    ms_sep, skernels = time_ops(sops, args.steps, args.warmup, stream)
 
     # the MoE backward, beside the step
     bops, _ = make_moe_bwd_ops(L, dev)
@@ -672,9 +725,12 @@ def main():
     log(f"context {ctx}")
     lin = ["quant_act X", "quant_weight W (+q_t)", "gemm_fprop", "quant_act dY", "gemm_dgrad", "quant_transpose X",
            "quant_transpose dY", "gemm_wgrad"]
-    lin_us = sum(kernels[n]["avg_us"] for n in lin)
-    lin_dual_us = lin_us - sum(kernels[f"quant_act {n}"]["avg_us"] + kernels[f"quant_transpose {n}"]["avg_us"]
-                               for n in ("X", "dY")) + sum(d["avg_us"] for d in dkernels.values())
+    lin_us = sum(skernels[n]["avg_us"] for n in lin)
+    lin_batched_us = sum(kernels[n]["avg_us"] for n in ("quant_batch W (+q_t) + X (rows + cols)", "gemm_fprop",
+                                                        "quant_act_transpose dY", "gemm_dgrad", "gemm_wgrad"))
+    quant_lin = {"batched": round(kernels["quant_batch W (+q_t) + X (rows + cols)"]["avg_us"]
+                                  + kernels["quant_act_transpose dY"]["avg_us"], 2),
+                 "separate": round(sum(skernels[n]["avg_us"] for n in lin if n.startswith("quant")), 2)}
 
     gemm_flops = sum(w for _, _, k, w in ops if k == "mfma")
     value = gemm_flops / (ms_step * 1e-3) / 1e12
@@ -718,6 +774,16 @@ def main():
         "roofline": roof,
         "kernel_source_sha": kernel_source_hash(),
         "kernels": kernels,
+        "linear_layer_quantization_us": quant_lin,
+        "linear_layer_quantization_note": "all quantization of the linear layer's step (X, W with its transposed "
+                                          "codes, dY, and the token-grouped transposed codes of X and dY): the step's "
+                                          "two batched/dual launches against the five separate quantizer launches; "
+                                          "316.9 MB of algorithmic bytes (70% of HBM peak = 56.6 us)",
+        "step_separate_quantizers": {
+            "ms_per_step": round(ms_sep, 4),
+            "value": round(sum(w for _, _, k, w in sops if k == "mfma") / (ms_sep * 1e-3) / 1e12, 2),
+            "kernels": skernels,
+        },
         "moe_backward": {
             "workload": "MoE layer backward: dY [16384,2048] bf16 (Student-t(3), 1% token rows x100), X and the "
                         "32 experts' W as the step's MoE layer; grouped Dgrad (bf16 dX) and grouped Wgrad "
@@ -731,8 +797,8 @@ def main():
             "workload": "quant_act_1x128 + quant_transpose of the linear layer's X [4096,7168] and dY [4096,2048] "
                         "(bf16) in one pass each",
             "kernels": dkernels,
-            "separate_us": {n: round(kernels[f"quant_act {n}"]["avg_us"] + kernels[f"quant_transpose {n}"]["avg_us"],
-                                     2) for n in ("X", "dY")},
+            "separate_us": {n: round(skernels[f"quant_act {n}"]["avg_us"]
+                                     + skernels[f"quant_transpose {n}"]["avg_us"], 2) for n in ("X", "dY")},
         },
         "microscaling_variant": {
             "workload": "the linear layer's Fprop+Dgrad+Wgrad (shapes as the step) in MXFP8 E4M3: 1x32 blocks "
@@ -740,7 +806,7 @@ def main():
                         "one dual quantizer per tensor",
             "ms_per_pass": round(ms_mx, 4),
             "gemm_tflops": round(mx_flops / (ms_mx * 1e-3) / 1e12, 2),
-            "method_linear_layer_us": {"as_step": round(lin_us, 2), "with_dual_quantizers": round(lin_dual_us, 2)},
+            "method_linear_layer_us": {"separate_quantizers": round(lin_us, 2), "as_step": round(lin_batched_us, 2)},
             "kernels": mkernels,
         },
         "exact_variant": {

@@ -48,7 +48,20 @@ EXPORTS = ["fp8q_status_string", "fp8q_set_gemm_tile", "fp8q_quant_act_1x128", "
            "fp8q_grouped_gemm_wgrad", "fp8q_quant_act_transpose", "fp8q_quant_mx_1x32",
            "fp8q_quant_mx_transpose", "fp8q_gemm_mx", "fp8q_grouped_gemm_mx",
            "fp8q_grouped_gemm_mx_dgrad", "fp8q_gemm_fprop_quant", "fp8q_gemm_dgrad_quant",
-           "fp8q_gemm_fprop_interval"]
+           "fp8q_gemm_fprop_interval", "fp8q_quant_batch"]
+
+
+MAX_QUANT_JOBS = 8
+QUANT_KINDS = {"act": 0, "weight": 1, "transpose": 2, "act_transpose": 3}
+
+
+class QuantJob(ctypes.Structure):
+    """fp8q_quant_job of include/fp8q.h."""
+    _fields_ = [("kind", ctypes.c_int32), ("xt", ctypes.c_int32), ("x", ctypes.c_void_p),
+                ("rows", ctypes.c_int64), ("cols", ctypes.c_int64), ("ld_x", ctypes.c_int64),
+                ("q", ctypes.c_void_p), ("ld_q", ctypes.c_int64), ("scale", ctypes.c_void_p),
+                ("ld_s", ctypes.c_int64), ("q_t", ctypes.c_void_p), ("ld_qt", ctypes.c_int64),
+                ("scale_t", ctypes.c_void_p), ("ld_st", ctypes.c_int64)]
 
 
 class Fp8qError(RuntimeError):
@@ -91,6 +104,7 @@ def load_library(path=LIB_PATH):
         "fp8q_gemm_fprop_quant": ([P, P, P, P, I64, I64, I64, P, I64, P, I64, P, I64, I32, P], I32),
         "fp8q_gemm_dgrad_quant": ([P, P, P, P, I64, I64, I64, P, I64, P, I64, P, I64, I32, P], I32),
         "fp8q_gemm_fprop_interval": ([P, P, P, P, I64, I64, I64, P, I64, I64, P], I32),
+        "fp8q_quant_batch": ([P, I32, P], I32),
     }
     for name in ["fp8q_gemm_fprop", "fp8q_gemm_dgrad", "fp8q_gemm_wgrad", "fp8q_grouped_gemm"]:
         sig[name + "_exact"] = sig[name]
@@ -280,6 +294,52 @@ def fp8q_gemm_fprop_quant(xq, xs, wq, ws, y, yq, ys, stream=None, exact=False):
                                                  _ld(y) if y is not None else 0, _ptr(yq), _ld(yq), _ptr(ys),
                                                  _ld(ys), int(bool(exact)), _stream(stream)),
            "fp8q_gemm_fprop_quant")
+
+
+def fp8q_quant_batch(jobs, stream=None):
+    """Several quantizations in one launch.  jobs: a list of
+        ("act", x, q, scale)
+        ("weight", w, q, q_t, scale)          # q_t may be None
+        ("transpose", x, q_t, scale_t)
+        ("act_transpose", x, q, scale, q_t, scale_t)
+    with the tensors of the single entry points (same shape rules)."""
+    if len(jobs) > MAX_QUANT_JOBS:
+        raise ValueError(f"at most {MAX_QUANT_JOBS} jobs per batch")
+    arr = (QuantJob * max(1, len(jobs)))()
+    for i, job in enumerate(jobs):
+        kind, x = job[0], job[1]
+        rows, cols = x.shape
+        q = scale = q_t = scale_t = None
+        if kind == "act":
+            q, scale = job[2:]
+        elif kind == "weight":
+            q, q_t, scale = job[2:]
+        elif kind == "transpose":
+            q_t, scale_t = job[2:]
+        elif kind == "act_transpose":
+            q, scale, q_t, scale_t = job[2:]
+        else:
+            raise ValueError(f"unknown quantization kind {kind!r}")
+        if q is not None:
+            _expect(q, (rows, cols), _U8, f"job {i} q")
+        if scale is not None:
+            gr = (_cdiv(rows, 128), _cdiv(cols, 128)) if kind == "weight" else (rows, _cdiv(cols, 128))
+            _expect(scale, gr, _F32, f"job {i} scale")
+        if q_t is not None:
+            _expect(q_t, (cols, rows), _U8, f"job {i} q_t")
+        if scale_t is not None:
+            _expect(scale_t, (cols, _cdiv(rows, 128)), _F32, f"job {i} scale_t")
+        _on_gpu(x, q, scale, q_t, scale_t)
+        j = arr[i]
+        j.kind, j.xt, j.x, j.rows, j.cols, j.ld_x = QUANT_KINDS[kind], _dtype_code(x), _ptr(x), rows, cols, _ld(x)
+        if q is not None:
+            j.q, j.ld_q, j.scale, j.ld_s = _ptr(q), _ld(q), _ptr(scale), _ld(scale)
+        if q_t is not None:
+            j.q_t, j.ld_qt = _ptr(q_t), _ld(q_t)
+        if scale_t is not None:
+            j.scale_t, j.ld_st = _ptr(scale_t), _ld(scale_t)
+    _check(load_library().fp8q_quant_batch(ctypes.cast(arr, ctypes.c_void_p), len(jobs), _stream(stream)),
+           "fp8q_quant_batch")
 
 
 def fp8q_gemm_fprop_interval(xq, xs, wq, ws, y, interval, stream=None):

@@ -157,6 +157,39 @@ fp8q_status fp8q_quant_transpose_grouped(const void* x, fp8q_dtype xt, int64_t r
                                                        scale_t, ld_st, stream));
 }
 
+fp8q_status fp8q_quant_batch(const fp8q_quant_job* jobs, int n_jobs, hipStream_t stream) {
+  if (n_jobs < 0 || n_jobs > FP8Q_MAX_QUANT_JOBS) return FP8Q_ERR_SHAPE;
+  if (n_jobs == 0) return FP8Q_OK;
+  if (!jobs) return FP8Q_ERR_NULL;
+  fp8q::QuantJob qj[FP8Q_MAX_QUANT_JOBS];
+  for (int i = 0; i < n_jobs; ++i) {
+    const fp8q_quant_job& J = jobs[i];
+    const fp8q_dtype xt = (fp8q_dtype)J.xt;
+    if (J.kind < FP8Q_QUANT_ACT_1X128 || J.kind > FP8Q_QUANT_ACT_TRANSPOSE) return FP8Q_ERR_SHAPE;
+    if (!valid_dtype(xt)) return FP8Q_ERR_DTYPE;
+    fp8q_status c = FP8Q_OK;
+    const int64_t rows = J.rows, cols = J.cols;
+    if (J.kind != FP8Q_QUANT_TRANSPOSE)
+      c = check_quant(J.x, esize(xt), rows, cols, J.ld_x, J.q, J.ld_q, cols, J.scale, J.ld_s, cdiv(cols, 128));
+    if (c == FP8Q_OK && (J.kind == FP8Q_QUANT_TRANSPOSE || J.kind == FP8Q_QUANT_ACT_TRANSPOSE))
+      c = check_quant(J.x, esize(xt), rows, cols, J.ld_x, J.q_t, J.ld_qt, rows, J.scale_t, J.ld_st, cdiv(rows, 128));
+    if (c == FP8Q_OK && J.kind == FP8Q_QUANT_WEIGHT_128X128 && rows > 0 && cols > 0 && J.q_t) {
+      if (J.ld_qt < rows) c = FP8Q_ERR_STRIDE;
+      else if (!aligned16(J.q_t) || J.ld_qt % 16 != 0) c = FP8Q_ERR_ALIGN;
+    }
+    if (c == FP8Q_OK && rows > 0 && cols > 0 && rows * cdiv(cols, 128) > kMaxGroups) c = FP8Q_ERR_SHAPE;
+    if (c != FP8Q_OK) return c;
+    fp8q::QuantJob& q = qj[i];
+    q.kind = J.kind; q.x_bf16 = xt == FP8Q_BF16; q.x = J.x; q.rows = rows; q.cols = cols; q.ld_x = J.ld_x;
+    const bool rows_out = J.kind != FP8Q_QUANT_TRANSPOSE, t_out = J.kind != FP8Q_QUANT_ACT_1X128;
+    q.q = rows_out ? J.q : nullptr; q.ld_q = J.ld_q; q.s = rows_out ? J.scale : nullptr; q.ld_s = J.ld_s;
+    q.q_t = t_out ? J.q_t : nullptr; q.ld_qt = J.ld_qt;
+    q.s_t = t_out ? J.scale_t : nullptr; q.ld_st = J.ld_st;
+  }
+  if (fp8q::quant_batch_blocks(qj, n_jobs) > kMaxGroups) return FP8Q_ERR_SHAPE;  // one grid dimension
+  return launched(fp8q::launch_quant_batch(qj, n_jobs, stream));
+}
+
 }  // extern "C"
 
 // The fused output quantization's arguments: codes [rows, ncols] (row stride

@@ -29,6 +29,29 @@ hipError_t launch_quant_transpose_grouped(const void* x, bool x_bf16, int64_t ro
                                           const int32_t* offsets, int64_t E, uint8_t* q_t, int64_t ld_qt,
                                           float* s_t, int64_t ld_st, hipStream_t st);
 
+// One quantization of a batched launch (kinds as fp8q_quant_kind: 0 act 1x128,
+// 1 weight 128x128 (q_t optional), 2 transpose, 3 act + transpose); arguments
+// as the single entry points, already validated.
+struct QuantJob {
+  int kind;
+  bool x_bf16;
+  const void* x;
+  int64_t rows, cols, ld_x;
+  uint8_t* q;
+  int64_t ld_q;
+  float* s;
+  int64_t ld_s;
+  uint8_t* q_t;
+  int64_t ld_qt;
+  float* s_t;
+  int64_t ld_st;
+};
+constexpr int kMaxQuantJobs = 8;
+// All jobs in one grid (each job's blocks form one contiguous range of it).
+hipError_t launch_quant_batch(const QuantJob* jobs, int n, hipStream_t st);
+// Workgroups that grid has (all must fit one grid dimension).
+int64_t quant_batch_blocks(const QuantJob* jobs, int n);
+
 // How the scale of the B operand (rows = output columns) is indexed.
 enum SbMode : int {
   kSbBlock = 0,  // one scale per 128 output columns per chunk: sb[(n/128)*sb_rs + kb*sb_cs]

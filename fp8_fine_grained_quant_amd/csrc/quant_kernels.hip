@@ -41,13 +41,14 @@ constexpr int64_t kNtCodeBytes = 64ll << 20;
 // scale is s[g]; no row/column split is needed.
 constexpr int kActU = 2;
 
+// One 256-thread block `vb` of the activation quantizer (the kernel below, and
+// activation jobs of the batched launch).
 template <class In, bool FLAT, int NTS>
-__global__ __launch_bounds__(256) void k_quant_act(const typename In::elem* __restrict__ x, int64_t ld_x,
-                                                   uint8_t* __restrict__ q, int64_t ld_q,
-                                                   float* __restrict__ s, int64_t ld_s,
-                                                   int cols, int ngr, int total) {
+__device__ __forceinline__ void quant_act_block(int vb, const typename In::elem* __restrict__ x, int64_t ld_x,
+                                                uint8_t* __restrict__ q, int64_t ld_q, float* __restrict__ s,
+                                                int64_t ld_s, int cols, int ngr, int total) {
   const int lane = threadIdx.x & 63;
-  const int wave = (int)((blockIdx.x * (uint32_t)blockDim.x + threadIdx.x) >> 6);
+  const int wave = (int)((vb * 256u + threadIdx.x) >> 6);
   const int team = lane >> 4, lig = lane & 15;
   float v[kActU][8];
   int grow[kActU], gcol[kActU];
@@ -106,6 +107,14 @@ __global__ __launch_bounds__(256) void k_quant_act(const typename In::elem* __re
   }
 }
 
+template <class In, bool FLAT, int NTS>
+__global__ __launch_bounds__(256) void k_quant_act(const typename In::elem* __restrict__ x, int64_t ld_x,
+                                                   uint8_t* __restrict__ q, int64_t ld_q,
+                                                   float* __restrict__ s, int64_t ld_s,
+                                                   int cols, int ngr, int total) {
+  quant_act_block<In, FLAT, NTS>((int)blockIdx.x, x, ld_x, q, ld_q, s, ld_s, cols, ngr, total);
+}
+
 hipError_t launch_quant_act(const void* x, bool x_bf16, int64_t rows, int64_t cols, int64_t ld_x,
                             uint8_t* q, int64_t ld_q, float* s, int64_t ld_s, hipStream_t st) {
   const int64_t ngr = (cols + 127) / 128;
@@ -148,17 +157,16 @@ __device__ __forceinline__ void load4<BF16In>(const uint16_t* p, float v[4]) {
   v[2] = bf16_to_f32(u.y & 0xFFFFu); v[3] = bf16_to_f32(u.y >> 16);
 }
 
+// One 128 x 128 block (bi, bj) of the weight quantizer; red (4 words) and tq
+// (16 KB, 16-byte aligned) are the block's LDS.
 template <class In, int NTS>
-__global__ __launch_bounds__(256) void k_quant_weight(const typename In::elem* __restrict__ w, int64_t ld_w,
-                                                      int rows, int cols,
-                                                      uint8_t* __restrict__ q, int64_t ld_q,
-                                                      uint8_t* __restrict__ qt, int64_t ld_qt,
-                                                      float* __restrict__ s, int64_t ld_s) {
-  __shared__ uint32_t red[4];
-  __shared__ __attribute__((aligned(16))) uint8_t tq[128 * 128];  // [column][row] codes of the block
+__device__ __forceinline__ void quant_weight_block(int bi, int bj, const typename In::elem* __restrict__ w,
+                                                   int64_t ld_w, int rows, int cols, uint8_t* __restrict__ q,
+                                                   int64_t ld_q, uint8_t* __restrict__ qt, int64_t ld_qt,
+                                                   float* __restrict__ s, int64_t ld_s, uint32_t* red,
+                                                   uint8_t* tq) {
   const int t = threadIdx.x;
   const int c4 = t & 31, rb = t >> 5;
-  const int bi = blockIdx.y, bj = blockIdx.x;
   const int r0 = bi * 128 + rb * 16;
   const int c0 = bj * 128 + c4 * 4;
   const bool full_c = c0 + 4 <= cols;
@@ -254,6 +262,18 @@ __global__ __launch_bounds__(256) void k_quant_weight(const typename In::elem* _
   }
 }
 
+template <class In, int NTS>
+__global__ __launch_bounds__(256) void k_quant_weight(const typename In::elem* __restrict__ w, int64_t ld_w,
+                                                      int rows, int cols,
+                                                      uint8_t* __restrict__ q, int64_t ld_q,
+                                                      uint8_t* __restrict__ qt, int64_t ld_qt,
+                                                      float* __restrict__ s, int64_t ld_s) {
+  __shared__ uint32_t red[4];
+  __shared__ __attribute__((aligned(16))) uint8_t tq[128 * 128];  // [column][row] codes of the block
+  quant_weight_block<In, NTS>((int)blockIdx.y, (int)blockIdx.x, w, ld_w, rows, cols, q, ld_q, qt, ld_qt, s, ld_s,
+                              red, tq);
+}
+
 hipError_t launch_quant_weight(const void* w, bool w_bf16, int64_t rows, int64_t cols, int64_t ld_w,
                                uint8_t* q, int64_t ld_q, uint8_t* q_t, int64_t ld_qt,
                                float* s, int64_t ld_s, hipStream_t st) {
@@ -300,19 +320,17 @@ hipError_t launch_quant_weight(const void* w, bool w_bf16, int64_t rows, int64_t
 // straight from registers, each segment would arrive as four 32-byte pieces
 // from four waves (measured 26.5 -> 22 us for X [4096,7168], 95 -> 80 us for
 // [16384,7168]).
+// One 128-token x 128-channel tile (bi, bj) of the transposing quantizer;
+// red (4 x 128 words) and tq (16 KB, 16-byte aligned) are the tile's LDS.
 template <class In, bool G, bool D, bool F>
-__global__ __launch_bounds__(256) void k_quant_transpose(const typename In::elem* __restrict__ x, int64_t ld_x,
-                                                         int rows, int cols,
-                                                         uint8_t* __restrict__ qt, int64_t ld_qt,
-                                                         float* __restrict__ st, int64_t ld_st,
-                                                         const int32_t* __restrict__ offsets, int E,
-                                                         uint8_t* __restrict__ q, int64_t ld_q,
-                                                         float* __restrict__ s, int64_t ld_s) {
-  __shared__ uint32_t red[4][128];
-  __shared__ __attribute__((aligned(16))) uint8_t tq[128 * 128];  // [channel][token] codes of the tile
+__device__ __forceinline__ void quant_transpose_block(int bi, int bj, const typename In::elem* __restrict__ x,
+                                                      int64_t ld_x, int rows, int cols, uint8_t* __restrict__ qt,
+                                                      int64_t ld_qt, float* __restrict__ st, int64_t ld_st,
+                                                      const int32_t* __restrict__ offsets, int E,
+                                                      uint8_t* __restrict__ q, int64_t ld_q, float* __restrict__ s,
+                                                      int64_t ld_s, uint32_t (*red)[128], uint8_t* tq) {
   const int t = threadIdx.x;
   const int c8 = t & 15, rblk = t >> 4;
-  const int bi = blockIdx.y, bj = blockIdx.x;
   // Output chunk bi (token columns [128 bi, 128 bi + 128) of q_t) comes from
   // input rows [rlo, rlo + 128), of which those below rhi exist.
   int rlo = bi * 128, rhi = rows;
@@ -445,6 +463,20 @@ __global__ __launch_bounds__(256) void k_quant_transpose(const typename In::elem
   }
 }
 
+template <class In, bool G, bool D, bool F>
+__global__ __launch_bounds__(256) void k_quant_transpose(const typename In::elem* __restrict__ x, int64_t ld_x,
+                                                         int rows, int cols,
+                                                         uint8_t* __restrict__ qt, int64_t ld_qt,
+                                                         float* __restrict__ st, int64_t ld_st,
+                                                         const int32_t* __restrict__ offsets, int E,
+                                                         uint8_t* __restrict__ q, int64_t ld_q,
+                                                         float* __restrict__ s, int64_t ld_s) {
+  __shared__ uint32_t red[4][128];
+  __shared__ __attribute__((aligned(16))) uint8_t tq[128 * 128];  // [channel][token] codes of the tile
+  quant_transpose_block<In, G, D, F>((int)blockIdx.y, (int)blockIdx.x, x, ld_x, rows, cols, qt, ld_qt, st, ld_st,
+                                     offsets, E, q, ld_q, s, ld_s, red, tq);
+}
+
 template <class In, bool D>
 static void launch_transpose_tiles(const void* x, int64_t rows, int64_t cols, int64_t ld_x, uint8_t* q_t,
                                    int64_t ld_qt, float* s_t, int64_t ld_st, uint8_t* q, int64_t ld_q, float* s,
@@ -490,6 +522,158 @@ hipError_t launch_quant_transpose_grouped(const void* x, bool x_bf16, int64_t ro
     hipLaunchKernelGGL((k_quant_transpose<F32In, true, false, false>), grid, dim3(256), 0, st, (const float*)x, ld_x,
                        (int)rows, (int)cols, q_t, ld_qt, s_t, ld_st, offsets, (int)E, nullptr, 0, nullptr, 0);
   return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Batched launch: several independent quantizations in one grid.  Each launch
+// of a 25-90 MB quantizer pays the ramp-up and drain of its own HBM stream
+// (a few us); in one grid the next job's blocks start while the previous
+// job's last blocks drain.  Every block runs exactly the code of the single
+// kernel it stands for (the block bodies above), so outputs are bit for bit
+// those of the separate calls.  Jobs go to one of two grids by resource
+// class: the activation quantizer needs ~30 VGPRs and no LDS and runs 8
+// waves per SIMD, the tile quantizers (weight, transpose, dual) up to ~147
+// VGPRs and 18 KB of LDS; one grid for both would hold the activation blocks
+// to the tile blocks' occupancy (measured: X and W in one grid 44.7 us
+// against 36.2 us for the two launches).
+struct QBody {
+  int variant;  // body and template arguments (see k_quant_batch)
+  int gx;       // weight / transpose: tiles along the columns
+  const void* x;
+  int64_t ld_x;
+  int rows, cols;
+  uint8_t* q;
+  int64_t ld_q;
+  float* s;
+  int64_t ld_s;
+  uint8_t* qt;
+  int64_t ld_qt;
+  float* st;
+  int64_t ld_st;
+  int ngr, total;  // activation jobs: groups per row, groups in all
+};
+struct QBatch {
+  QBody job[kMaxQuantJobs];
+  int start[kMaxQuantJobs + 1];  // first block of each job, start[n] = grid size
+  int n;
+};
+
+enum : int { kVAct = 0, kVWeight = 8, kVTrans = 12, kVDual = 16 };
+
+template <bool TILES>
+__global__ __launch_bounds__(256) void k_quant_batch(QBatch b) {
+  __shared__ uint32_t red[TILES ? 4 : 1][128];
+  __shared__ __attribute__((aligned(16))) uint8_t tq[TILES ? 128 * 128 : 16];
+  const int bid = (int)blockIdx.x;
+  int j = 0;
+  while (j + 1 < b.n && bid >= b.start[j + 1]) ++j;
+  const QBody& J = b.job[j];
+  const int vb = bid - b.start[j];
+  const int bi = vb / J.gx, bj = vb - (vb / J.gx) * J.gx;
+  const uint16_t* xb = (const uint16_t*)J.x;
+  const float* xf = (const float*)J.x;
+#define FP8Q_ACT_CASE(V, T, F, N, XP)                                                                     \
+  case V: quant_act_block<T, F, N>(vb, XP, J.ld_x, J.q, J.ld_q, J.s, J.ld_s, J.cols, J.ngr, J.total); break;
+#define FP8Q_W_CASE(V, T, N, XP)                                                                             \
+  case V: quant_weight_block<T, N>(bi, bj, XP, J.ld_x, J.rows, J.cols, J.q, J.ld_q, J.qt, J.ld_qt, J.s, J.ld_s, \
+                                   &red[0][0], tq); break;
+#define FP8Q_T_CASE(V, T, D, F, XP)                                                                      \
+  case V: quant_transpose_block<T, false, D, F>(bi, bj, XP, J.ld_x, J.rows, J.cols, J.qt, J.ld_qt, J.st,   \
+                                                J.ld_st, nullptr, 0, J.q, J.ld_q, J.s, J.ld_s, red, tq); break;
+  if (!TILES) {
+    switch (J.variant) {
+    FP8Q_ACT_CASE(kVAct + 0, F32In, false, 0, xf)
+    FP8Q_ACT_CASE(kVAct + 1, F32In, false, 1, xf)
+    FP8Q_ACT_CASE(kVAct + 2, F32In, true, 0, xf)
+    FP8Q_ACT_CASE(kVAct + 3, F32In, true, 1, xf)
+    FP8Q_ACT_CASE(kVAct + 4, BF16In, false, 0, xb)
+    FP8Q_ACT_CASE(kVAct + 5, BF16In, false, 1, xb)
+    FP8Q_ACT_CASE(kVAct + 6, BF16In, true, 0, xb)
+    FP8Q_ACT_CASE(kVAct + 7, BF16In, true, 1, xb)
+    default: break;
+    }
+    return;
+  }
+  switch (J.variant) {
+    FP8Q_W_CASE(kVWeight + 0, F32In, 0, xf)
+    FP8Q_W_CASE(kVWeight + 1, F32In, 1, xf)
+    FP8Q_W_CASE(kVWeight + 2, BF16In, 0, xb)
+    FP8Q_W_CASE(kVWeight + 3, BF16In, 1, xb)
+    FP8Q_T_CASE(kVTrans + 0, F32In, false, false, xf)
+    FP8Q_T_CASE(kVTrans + 1, F32In, false, true, xf)
+    FP8Q_T_CASE(kVTrans + 2, BF16In, false, false, xb)
+    FP8Q_T_CASE(kVTrans + 3, BF16In, false, true, xb)
+    FP8Q_T_CASE(kVDual + 0, F32In, true, false, xf)
+    FP8Q_T_CASE(kVDual + 1, F32In, true, true, xf)
+    FP8Q_T_CASE(kVDual + 2, BF16In, true, false, xb)
+    FP8Q_T_CASE(kVDual + 3, BF16In, true, true, xb)
+    default: break;
+  }
+#undef FP8Q_ACT_CASE
+#undef FP8Q_W_CASE
+#undef FP8Q_T_CASE
+}
+
+int64_t quant_batch_blocks(const QuantJob* jobs, int n) {
+  int64_t blocks = 0;
+  for (int i = 0; i < n; ++i) {
+    const QuantJob& J = jobs[i];
+    if (J.rows == 0 || J.cols == 0) continue;
+    if (J.kind == 0) blocks += ((J.rows * ((J.cols + 127) / 128) + 4 * kActU - 1) / (4 * kActU) + 3) / 4;
+    else blocks += ((J.cols + 127) / 128) * ((J.rows + 127) / 128);
+  }
+  return blocks;
+}
+
+template <bool TILES>
+static hipError_t launch_batch_class(const QuantJob* jobs, int n, hipStream_t st) {
+  QBatch b{};
+  int m = 0;
+  int64_t blocks = 0;
+  for (int i = 0; i < n; ++i) {
+    const QuantJob& J = jobs[i];
+    if (J.rows == 0 || J.cols == 0 || (J.kind != 0) != TILES) continue;
+    QBody& B = b.job[m];
+    B.x = J.x; B.ld_x = J.ld_x; B.rows = (int)J.rows; B.cols = (int)J.cols;
+    B.q = J.q; B.ld_q = J.ld_q; B.s = J.s; B.ld_s = J.ld_s;
+    B.qt = J.q_t; B.ld_qt = J.ld_qt; B.st = J.s_t; B.ld_st = J.ld_st;
+    B.gx = (int)((J.cols + 127) / 128);
+    const int gy = (int)((J.rows + 127) / 128);
+    const int bf = J.x_bf16 ? 1 : 0;
+    const bool full = J.rows % 128 == 0 && J.cols % 128 == 0;
+    int64_t nb = 0;
+    if (J.kind == 0) {
+      const int64_t ngr = (J.cols + 127) / 128, total = J.rows * ngr;
+      const bool flat = J.cols % 128 == 0 && J.ld_x == J.cols && J.ld_q == J.cols && J.ld_s == ngr;
+      const bool nt = J.rows * J.cols > kNtCodeBytes;
+      B.variant = kVAct + 4 * bf + (flat ? 2 : 0) + (nt ? 1 : 0);
+      B.ngr = (int)ngr;
+      B.total = (int)total;
+      B.gx = 1;
+      nb = ((total + 4 * kActU - 1) / (4 * kActU) + 3) / 4;
+    } else if (J.kind == 1) {
+      B.variant = kVWeight + 2 * bf + (J.rows * J.cols > kNtCodeBytes ? 1 : 0);
+      nb = (int64_t)B.gx * gy;
+    } else {
+      B.variant = (J.kind == 2 ? kVTrans : kVDual) + 2 * bf + (full ? 1 : 0);
+      nb = (int64_t)B.gx * gy;
+    }
+    b.start[m] = (int)blocks;
+    blocks += nb;
+    ++m;
+  }
+  if (m == 0) return hipSuccess;
+  b.start[m] = (int)blocks;
+  b.n = m;
+  hipLaunchKernelGGL(k_quant_batch<TILES>, dim3((uint32_t)blocks), dim3(256), 0, st, b);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_batch(const QuantJob* jobs, int n, hipStream_t st) {
+  if (quant_batch_blocks(jobs, n) > INT32_MAX) return hipErrorInvalidConfiguration;
+  const hipError_t e = launch_batch_class<false>(jobs, n, st);
+  if (e != hipSuccess) return e;
+  return launch_batch_class<true>(jobs, n, st);
 }
 
 }  // namespace fp8q

@@ -148,6 +148,55 @@ fp8q_status fp8q_quant_act_transpose(const void* x, fp8q_dtype xt, int64_t rows,
                                      int64_t ld_qt, float* scale_t, int64_t ld_st, hipStream_t stream);
 
 /*
+ * Batched quantization: up to FP8Q_MAX_QUANT_JOBS independent quantizations
+ * in at most two launches (one for the 1x128 activation jobs, one for the
+ * jobs quantizing 128x128 tiles: weight, transpose, act + transpose; the two
+ * classes need different register and LDS budgets).  A quantizer of a
+ * 25-90 MB tensor spends a few us of its time in the ramp-up and drain of
+ * its own HBM stream; in one grid the next job's workgroups start while the
+ * previous job's last ones drain.  Online
+ * quantization of every tensor right before its use ("How does the unified
+ * E4M3 format contribute to the efficiency of DeepSeek-V3", "Dynamic Scaling
+ * and Online Quantization") puts several independent quantizations next to
+ * each other, e.g. a layer's input X and its weight W before Fprop.
+ *   jobs : HOST array of n_jobs descriptions (read during the call only)
+ *   kind : FP8Q_QUANT_ACT_1X128       x -> q, scale        (fp8q_quant_act_1x128)
+ *          FP8Q_QUANT_WEIGHT_128X128  x -> q, scale, q_t (q_t may be NULL)
+ *                                     (fp8q_quant_weight_128x128)
+ *          FP8Q_QUANT_TRANSPOSE       x -> q_t, scale_t    (fp8q_quant_transpose)
+ *          FP8Q_QUANT_ACT_TRANSPOSE   x -> q, scale, q_t, scale_t
+ *                                     (fp8q_quant_act_transpose)
+ *   Every field a kind does not use is ignored.  Each job's arguments, rules
+ *   and outputs are those of the single entry point named; its outputs are
+ *   bit for bit the same.  Jobs must not write memory another job reads or
+ *   writes.  All jobs are validated before anything is enqueued: the first
+ *   invalid job's status is returned.  n_jobs outside [0, FP8Q_MAX_QUANT_JOBS]
+ *   or an unknown kind gives FP8Q_ERR_SHAPE; n_jobs = 0 is a no-op.
+ */
+#define FP8Q_MAX_QUANT_JOBS 8
+typedef enum {
+  FP8Q_QUANT_ACT_1X128 = 0,
+  FP8Q_QUANT_WEIGHT_128X128 = 1,
+  FP8Q_QUANT_TRANSPOSE = 2,
+  FP8Q_QUANT_ACT_TRANSPOSE = 3
+} fp8q_quant_kind;
+typedef struct {
+  int32_t kind;            /* fp8q_quant_kind */
+  int32_t xt;              /* fp8q_dtype of x */
+  const void* x;           /* [rows, cols], row stride ld_x elements */
+  int64_t rows, cols, ld_x;
+  uint8_t* q;              /* row codes [rows, cols], row stride ld_q bytes */
+  int64_t ld_q;
+  float* scale;            /* row scales, row stride ld_s */
+  int64_t ld_s;
+  uint8_t* q_t;            /* transposed codes [cols, rows], row stride ld_qt bytes */
+  int64_t ld_qt;
+  float* scale_t;          /* transposed scales [cols, ceil(rows/128)], row stride ld_st */
+  int64_t ld_st;
+} fp8q_quant_job;
+fp8q_status fp8q_quant_batch(const fp8q_quant_job* jobs, int n_jobs, hipStream_t stream);
+
+/*
  * Fprop: Y[M,N] = X[M,K] . W[N,K]^T ("DeepSeek FP8 Training", Fprop pipeline:
  * FP8 GEMM with FP32 accumulation, result stored as BF16).
  *   xq : [M, K] codes, contiguous;  xs : [M, K/128] FP32, contiguous

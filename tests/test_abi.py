@@ -150,6 +150,41 @@ def test_interval_study_argument_errors(lib):
     assert f(A16, A16, A16, A16, 0, 128, 512, None, 128, 1024, None) == OK      # M = 0
 
 
+def _job(kind, rows, cols, ld_x=None, **kw):
+    j = fq.QuantJob()
+    j.kind, j.xt, j.x, j.rows, j.cols = kind, 0, A16, rows, cols
+    j.ld_x = cols if ld_x is None else ld_x
+    j.q, j.ld_q, j.scale, j.ld_s = A16, cols, A16, (cols + 127) // 128
+    j.q_t, j.ld_qt, j.scale_t, j.ld_st = A16, rows, A16, (rows + 127) // 128
+    for k, v in kw.items():
+        setattr(j, k, v)
+    return j
+
+
+def _batch(lib, *jobs):
+    arr = (fq.QuantJob * max(1, len(jobs)))(*jobs)
+    return lib.fp8q_quant_batch(ctypes.cast(arr, ctypes.c_void_p), len(jobs), None)
+
+
+def test_quant_batch_argument_errors(lib):
+    import ctypes as C
+    assert lib.fp8q_quant_batch(None, 0, None) == OK
+    assert lib.fp8q_quant_batch(None, 1, None) == NULL
+    assert lib.fp8q_quant_batch(None, 9, None) == SHAPE                       # more than 8 jobs
+    assert lib.fp8q_quant_batch(None, -1, None) == SHAPE
+    assert C.sizeof(fq.QuantJob) == 4 + 4 + 8 * 12
+    assert _batch(lib, _job(4, 128, 128)) == SHAPE                            # unknown kind
+    assert _batch(lib, _job(0, 128, 128, xt=9)) == DTYPE
+    # the first invalid job decides; nothing is launched
+    assert _batch(lib, _job(0, 128, 128, ld_x=100), _job(1, 128, 128, q=None)) == STRIDE
+    assert _batch(lib, _job(0, 128, 128, q=None), _job(1, 128, 128, ld_x=100)) == NULL
+    assert _batch(lib, _job(1, 256, 256, ld_qt=100)) == STRIDE                # weight q_t narrower than rows
+    assert _batch(lib, _job(2, 300, 64, ld_qt=256)) == STRIDE                 # transpose: ld_qt < rows
+    assert _batch(lib, _job(3, 300, 64, ld_qt=304, ld_st=2)) == STRIDE        # dual: ld_st < 3
+    assert _batch(lib, _job(3, 300, 64, ld_q=64, ld_s=1, scale=A16 + 2)) == ALIGN
+    assert _batch(lib, _job(0, 0, 128, x=None, q=None, scale=None)) == OK     # empty jobs are skipped
+
+
 def test_grouped_backward_argument_errors(lib):
     tg = lib.fp8q_quant_transpose_grouped
     # rows 300, E 4: capacity 128 * (2 + 4) = 768 token columns, 6 scale columns
