@@ -46,6 +46,18 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+# --launch-log: the ops in launch order, each with the number of kernels it
+# launches, so that a rocprofv3 trace of the same run can be attributed to
+# ops (several ops share a kernel; see profile_summary)
+LAUNCHES = []
+KERNELS_PER_OP = {"gemm_fprop + quant_act Y": 2, "gemm_dgrad + quant_act dX": 2}
+
+
+def launch(op):
+    LAUNCHES.append((op[0], KERNELS_PER_OP.get(op[0], 1)))
+    op[1]()
+
+
 def cdiv(a, b):
     return (a + b - 1) // b
 
@@ -295,25 +307,31 @@ def tiny_gemm_latency(dev, reps=200):
     import synth
 
     x, w = synth.tiny_fprop()
-    xq, xs = fq.quant_act_1x128(x.to(dev))
-    wq, ws, _ = fq.quant_weight_128x128(w.to(dev), transpose=False)
+    xg, wg = x.to(dev), w.to(dev)
+    xq = torch.empty(128, 256, dtype=torch.uint8, device=dev)
+    xs = torch.empty(128, 2, dtype=torch.float32, device=dev)
+    wq = torch.empty(128, 256, dtype=torch.uint8, device=dev)
+    ws = torch.empty(1, 2, dtype=torch.float32, device=dev)
     y = torch.empty(128, 128, dtype=torch.bfloat16, device=dev)
+    launch(("tiny quant_act X", lambda: fq.fp8q_quant_act_1x128(xg, xq, xs)))
+    launch(("tiny quant_weight W", lambda: fq.fp8q_quant_weight_128x128(wg, wq, None, ws)))
+    op = ("tiny gemm_fprop", lambda: fq.fp8q_gemm_fprop(xq, xs, wq, ws, y))
     stream = torch.cuda.current_stream()
     for _ in range(20):
-        fq.fp8q_gemm_fprop(xq, xs, wq, ws, y)
+        launch(op)
     torch.cuda.synchronize()
     single = []
     for _ in range(50):
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record(stream)
-        fq.fp8q_gemm_fprop(xq, xs, wq, ws, y)
+        launch(op)
         b.record(stream)
         b.synchronize()
         single.append(a.elapsed_time(b) * 1e3)
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     a.record(stream)
     for _ in range(reps):
-        fq.fp8q_gemm_fprop(xq, xs, wq, ws, y)
+        launch(op)
     b.record(stream)
     torch.cuda.synchronize()
     single.sort()
@@ -376,8 +394,8 @@ def telemetry(ops, seconds=1.5):
         t0, n = time.perf_counter(), 0
         while time.perf_counter() - t0 < seconds:
             for _ in range(10):
-                for _, fn, _, _ in ops:
-                    fn()
+                for op in ops:
+                    launch(op)
             n += 10
             torch.cuda.synchronize()
         dt = time.perf_counter() - t0
@@ -445,21 +463,141 @@ def context_error(H, outs, samples=64, seed=7):
     return out
 
 
-def trace_summary(csv_path):
-    """Per-kernel launch count, mean, median and minimum duration (us) from a
-    rocprofv3 --kernel-trace CSV, as a markdown table on stdout (the median
-    is robust to the warm-up launches that the mean includes)."""
+def _algorithmic_mbytes():
+    """Operand + scale + output bytes of each GEMM op of the step and its side
+    sections (the quantizers' bytes are their `mbytes`)."""
+    M, K, N, Mm, E = 4096, 7168, 2048, 16384, 32
+    g = lambda m, n, k, out_es: (m * k + n * k + (m + n) * (k // 128) * 4 + m * n * out_es) / 1e6
+    fp, dg, wg = g(M, N, K, 2), g(M, K, N, 2), g(N, K, M, 4)
+    gr = (Mm * K + E * N * K + (Mm + E * N) * (K // 128) * 4 + Mm * N * 2) / 1e6
+    grd = (Mm * N + E * N * K + (Mm + E * N) * (K // 128) * 4 + Mm * K * 2) / 1e6
+    grw = (Mm * (N + K) + Mm // 128 * (N + K) * 4 + E * N * K * 4) / 1e6
+    return {"gemm_fprop": fp, "gemm_dgrad": dg, "gemm_wgrad": wg, "grouped_gemm": gr, "grouped_gemm_dgrad": grd,
+            "grouped_gemm_wgrad": grw, "gemm_fprop_exact": fp, "gemm_dgrad_exact": dg, "gemm_wgrad_exact": wg,
+            "grouped_gemm_exact": gr, "gemm_fprop_quant": fp + M * N / 1e6 + M * N / 128 * 4 / 1e6,
+            "gemm_dgrad_quant": dg + M * K / 1e6 + M * K / 128 * 4 / 1e6, "mx gemm fprop": fp, "mx gemm dgrad": dg,
+            "mx gemm wgrad": wg}
+
+
+def _csv_rows(d, suffix):
     import csv
+    import glob
+    paths = sorted(glob.glob(os.path.join(d, "**", f"*{suffix}"), recursive=True))
+    if not paths:
+        raise FileNotFoundError(f"no *{suffix} under {d}")
+    with open(paths[0]) as f:
+        return list(csv.DictReader(f))
+
+
+def _attribute(rows, log_path):
+    """rows: one per library kernel dispatch; the launch log names the op of
+    each dispatch in order.  Returns {op: [rows]} (asserts the counts match)."""
     from collections import defaultdict
-    d = defaultdict(list)
-    with open(csv_path) as f:
-        for r in csv.DictReader(f):
-            d[r["Kernel_Name"]].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
-    print("| kernel | launches | mean us | median us | min us |")
-    print("|---|---|---|---|---|")
-    for k, v in sorted(d.items(), key=lambda kv: -sum(kv[1])):
-        v.sort()
-        print(f"| `{k[:90]}` | {len(v)} | {sum(v) / len(v):.2f} | {v[len(v) // 2]:.2f} | {v[0]:.2f} |")
+    with open(log_path) as f:
+        seq = [name for name, nk in json.load(f) for _ in range(nk)]
+    rows = sorted((r for r in rows if "fp8q::" in r["Kernel_Name"]), key=lambda r: int(r["Dispatch_Id"]))
+    if len(rows) != len(seq):
+        raise AssertionError(f"{len(rows)} library dispatches in the trace, {len(seq)} in the launch log")
+    by = defaultdict(list)
+    for r, op in zip(rows, seq):
+        by[op].append(r)
+    return by
+
+
+def _short(name):
+    import re
+    m = re.match(r"void fp8q::(\w+(<[^(]*>)?)\(", name)
+    return (m.group(1) if m else name).replace("fp8q::", "")
+
+
+def profile_summary(prof, bench_json=None):
+    """Summaries of rocprofv3 runs of this bench (each run made with
+    --launch-log <its dir>/launches.json and --no-telemetry): prof/kt (the
+    kernel trace), prof/FETCH_SIZE and prof/WRITE_SIZE (one counter each),
+    prof/cal_FETCH_SIZE and prof/cal_WRITE_SIZE (--copy-calibration 1024).
+    Prints the per-op kernel-trace table and the per-op HBM traffic table
+    (markdown) and writes profiles/traffic.json for the current kernel
+    sources."""
+    ev = {}
+    if bench_json:
+        with open(bench_json) as f:
+            bj = json.loads(f.read().strip().splitlines()[-1])
+        for sec in (None, "step_separate_quantizers", "moe_backward", "dual_output_quantizer", "microscaling_variant",
+                    "exact_variant", "fused_output_quant"):
+            ev.update((bj if sec is None else bj[sec])["kernels"])
+    by = _attribute(_csv_rows(os.path.join(prof, "kt"), "kernel_trace.csv"), os.path.join(prof, "kt", "launches.json"))
+    print("| op | kernel | launches | mean us | median us | min us | bench.py HIP-event avg us |")
+    print("|---|---|---|---|---|---|---|")
+    for op, rows in by.items():
+        d = sorted((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in rows)
+        ks = sorted({_short(r["Kernel_Name"]) for r in rows})
+        print(f"| {op} | {', '.join('`' + k + '`' for k in ks)} | {len(d)} | {sum(d) / len(d):.2f} | "
+              f"{d[len(d) // 2]:.2f} | {d[0]:.2f} | {ev.get(op, {}).get('avg_us', '')} |")
+
+    def counter(c, sub):
+        rows = [r for r in _csv_rows(os.path.join(prof, sub), "counter_collection.csv") if r["Counter_Name"] == c]
+        return rows
+
+    def per_op(c):
+        b = _attribute(counter(c, c), os.path.join(prof, c, "launches.json"))
+        return {op: sum(float(r["Counter_Value"]) for r in v) / len(v) for op, v in b.items()}
+
+    def calib(c):
+        big = [float(r["Counter_Value"]) for r in counter(c, "cal_" + c) if "copyBuffer" in r["Kernel_Name"]]
+        if not big:
+            raise AssertionError(f"no copy kernel in the {c} calibration run")
+        return sum(big) / len(big)
+
+    nbytes = 1024000000
+    ff, wf = nbytes / 1024 / calib("FETCH_SIZE"), nbytes / 1024 / calib("WRITE_SIZE")
+    fc, wc = per_op("FETCH_SIZE"), per_op("WRITE_SIZE")
+    alg = _algorithmic_mbytes()
+    out = {"source_sha": kernel_source_hash(), "copy_calibration": {"bytes": float(nbytes), "fetch_factor": ff,
+                                                                    "write_factor": wf}, "kernels": {}}
+    print()
+    print(f"Calibration: FETCH_SIZE x {ff:.4f}, WRITE_SIZE x {wf:.4f} (a plain copy of {nbytes} bytes)")
+    print()
+    print("| op | FETCH KiB (counted) | WRITE KiB (counted) | traffic MB (scaled) | algorithmic MB | traffic / algorithmic |")
+    print("|---|---|---|---|---|---|")
+    for op in fc:
+        b = (fc[op] * ff + wc.get(op, 0.0) * wf) * 1024
+        a = ev.get(op, {}).get("mbytes") or alg.get(op)
+        ratio = f"{b / 1e6 / a:.2f}" if a else ""
+        print(f"| {op} | {fc[op]:.0f} | {wc.get(op, 0.0):.0f} | {b / 1e6:.1f} | {a or ''} | {ratio} |")
+        out["kernels"][op] = {"fetch_kib_counted": fc[op], "write_kib_counted": wc.get(op, 0.0),
+                              "bytes_per_launch": int(b)}
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+
+
+def counters_summary(prof):
+    """Per-op means of every counter collected under prof/pmc*/ (one rocprofv3
+    --pmc run per directory, each with its launch log), for the GEMM ops, as a
+    markdown table (ops as columns)."""
+    import glob
+    from collections import defaultdict
+    vals = defaultdict(dict)
+    for d in sorted(p for p in glob.glob(os.path.join(prof, "pmc*")) if os.path.isdir(p)):
+        rows = _csv_rows(d, "counter_collection.csv")
+        names = sorted({r["Counter_Name"] for r in rows})
+        for c in names:
+            b = _attribute([r for r in rows if r["Counter_Name"] == c], os.path.join(d, "launches.json"))
+            for op, v in b.items():
+                vals[op][c] = sum(float(r["Counter_Value"]) for r in v) / len(v)
+    ops = [op for op in vals if "gemm" in op and "+" not in op and not op.startswith("tiny")]
+    counters = sorted({c for op in ops for c in vals[op]})
+    print("| counter | " + " | ".join(ops) + " |")
+    print("|---|" + "---|" * len(ops))
+    for c in counters:
+        print(f"| {c} | " + " | ".join(f"{vals[op].get(c, float('nan')):.4g}" for op in ops) + " |")
+    # matrix-core busy: busy cycles per SIMD (1024 SIMDs) over active cycles per XCD (8 XCDs)
+    print()
+    print("| op | MFMA busy (SQ_VALU_MFMA_BUSY_CYCLES / 1024) / (GRBM_GUI_ACTIVE / 8) |")
+    print("|---|---|")
+    for op in ops:
+        v = vals[op]
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in v and "GRBM_GUI_ACTIVE" in v:
+            print(f"| {op} | {v['SQ_VALU_MFMA_BUSY_CYCLES'] / 1024 / (v['GRBM_GUI_ACTIVE'] / 8):.1%} |")
 
 
 def time_ops(ops, steps, warmup, stream, flush=None):
@@ -478,8 +616,8 @@ def time_ops(ops, steps, warmup, stream, flush=None):
     for _ in range(warmup):
         if flush:
             flush()
-        for _, fn, _, _ in ops:
-            fn()
+        for op in ops:
+            launch(op)
     torch.cuda.synchronize()
     ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in ops]
           for _ in range(steps)]
@@ -490,8 +628,8 @@ def time_ops(ops, steps, warmup, stream, flush=None):
         torch.cuda.synchronize()
         t_start.record(stream)
         for s in range(steps):
-            for _, fn, _, _ in ops:
-                fn()
+            for op in ops:
+                launch(op)
         t_end.record(stream)
         torch.cuda.synchronize()
         ms_pass = t_start.elapsed_time(t_end) / steps
@@ -500,9 +638,9 @@ def time_ops(ops, steps, warmup, stream, flush=None):
     for s in range(steps):
         if flush:
             flush()
-        for i, (_, fn, _, _) in enumerate(ops):
+        for i, op in enumerate(ops):
             ev[s][i][0].record(stream)
-            fn()
+            launch(op)
             ev[s][i][1].record(stream)
     torch.cuda.synchronize()
     if flush:
@@ -643,11 +781,20 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=float, default=0.0, metavar="MB",
                     help="only run a plain device copy of MB megabytes (counter calibration) and exit")
-    ap.add_argument("--trace-summary", metavar="CSV",
-                    help="only summarize a rocprofv3 kernel-trace CSV (per-kernel mean/median/min) and exit")
+    ap.add_argument("--no-telemetry", action="store_true",
+                    help="skip the sustained-load telemetry loop (profiling runs: a deterministic launch sequence)")
+    ap.add_argument("--launch-log", metavar="JSON", help="write the ops in launch order (for --profile-summary)")
+    ap.add_argument("--profile-summary", metavar="DIR",
+                    help="only summarize rocprofv3 runs of this bench under DIR (see profile_summary) and exit")
+    ap.add_argument("--bench-json", metavar="FILE", help="with --profile-summary: a bench line to compare against")
+    ap.add_argument("--counters-summary", metavar="DIR",
+                    help="only summarize the rocprofv3 --pmc runs under DIR/pmc* (see counters_summary) and exit")
     args = ap.parse_args()
-    if args.trace_summary:
-        trace_summary(args.trace_summary)
+    if args.profile_summary:
+        profile_summary(args.profile_summary, args.bench_json)
+        return
+    if args.counters_summary:
+        counters_summary(args.counters_summary)
         return
     if args.gpus != 1:
         print("bench.py measures one GPU: the path is built and timed on a single MI355X; "
@@ -671,9 +818,11 @@ def main():
     stream = torch.cuda.current_stream()
     # the step under sustained load first: clock, power and activity, and the
     # GPU at its working clocks before the timed region
-    log("telemetry: the step back to back for ~1.5 s")
-    tele = telemetry(ops)
-    log(f"telemetry {tele}")
+    tele = None
+    if not args.no_telemetry:
+        log("telemetry: the step back to back for ~1.5 s")
+        tele = telemetry(ops)
+        log(f"telemetry {tele}")
     log(f"warmup {args.warmup} steps, timing {args.steps} steps")
     ms_step, kernels = time_ops(ops, args.steps, args.warmup, stream)
     sops, _ = make_ops(L, dev, form="separate")
@@ -834,6 +983,9 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
+    if args.launch_log:
+        with open(args.launch_log, "w") as f:
+            json.dump(LAUNCHES, f)
 
 
 if __name__ == "__main__":
