@@ -23,6 +23,24 @@ struct TileCoord {
 // tile numbers then walk bands of kGroupM m-tiles column by column.  The
 // workgroups of one XCD thus cover a compact block of the output and share
 // their A rows and B columns in that XCD's L2.
+// The coordinates depend only on the workgroup id, the launch arguments and
+// the expert offsets, so they are the same in every lane; the compiler cannot
+// always prove that through the expert walks below, and then keeps them in
+// vector registers and wraps every buffer load that uses them in a loop over
+// lanes (measured: 52 such loops in the grouped weight-gradient kernel).
+// Reading them back from lane 0 makes them scalar again.
+__device__ __forceinline__ int64_t uniform_i64(int64_t v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+__device__ __forceinline__ void make_uniform(TileCoord& tc) {
+  tc.m0 = uniform_i64(tc.m0);
+  tc.mend = uniform_i64(tc.mend);
+  tc.n0 = __builtin_amdgcn_readfirstlane(tc.n0);
+  tc.e = __builtin_amdgcn_readfirstlane(tc.e);
+}
+
 template <int BM, int BN, bool GROUPED>
 __device__ __forceinline__ bool tile_coord(const GemmArgs& p, TileCoord& tc) {
   const int G = gridDim.x, bid = blockIdx.x;
@@ -71,6 +89,7 @@ __device__ __forceinline__ bool tile_coord(const GemmArgs& p, TileCoord& tc) {
     tc.n0 = (t / tiles_m) * BN;
     tc.mend = p.M;
     tc.e = e;
+    make_uniform(tc);
     return true;
   }
   // grouped rows: tiles never straddle experts.  The grid is sized for the
@@ -100,6 +119,7 @@ __device__ __forceinline__ bool tile_coord(const GemmArgs& p, TileCoord& tc) {
   tc.n0 = (int)(local / mt) * BN;
   tc.mend = hi;
   tc.e = e;
+  make_uniform(tc);
   return true;
 }
 
