@@ -41,7 +41,12 @@
 // MFMA operand layout (the same permutation of the 128 K positions for A and
 // B, which leaves every dot product unchanged): lane l supplies row l%16 of
 // the 16-row slice, bytes [16g, 16g+16) and [64+16g, 64+16g+16) of the chunk,
-// g = l/16.  Result: lane l holds C[4g + r][l%16], r = 0..3.
+// g = l/16.  Block-scaled B (Fprop, Dgrad): B is the first operand, so lane l
+// holds C[l%16][4g + r], r = 0..3 (one output row per lane: its promotion
+// needs one row scale per sub-tile, read from LDS, where the other order
+// needed four per sub-tile, broadcast across the lanes with DPP).  Row-scaled
+// B (Wgrad): A first, lane l holds C[4g + r][l%16] (one column per lane, its
+// column scale per lane).
 //
 // Exact mode (the _exact entry points, template flag EX of the 256 x 128
 // kernel).  gfx950's FP8 matrix instruction aligns the 8 products of each
@@ -149,6 +154,11 @@ __global__ __launch_bounds__(kNT) void k_gemm_fp8(GemmArgs p) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
   typedef Stage<SB_MODE, SC4> S;
   constexpr bool ROW = SB_MODE == kSbRow;
+  // Block-scaled B: B is the matrix instruction's first operand, so lane
+  // 16 g + l16 holds output row 16 i + l16 (columns 16 j + 4 g + r) of each
+  // sub-tile and needs one row scale per sub-tile.  Row mode keeps A first
+  // (rows 16 i + 4 g + r, column 16 j + l16), its column scales per lane.
+  constexpr bool TR = !ROW;
   __shared__ __attribute__((aligned(16))) uint8_t st0[S::bytes];
   __shared__ __attribute__((aligned(16))) uint8_t st1[S::bytes];
   __shared__ __attribute__((aligned(16))) uint8_t st2[S::bytes];
@@ -253,16 +263,33 @@ __global__ __launch_bounds__(kNT) void k_gemm_fp8(GemmArgs p) {
     const uint8_t* base = st + S::b + 16 * j * kBK;
     return make_frag(*reinterpret_cast<const uint4*>(base + offLo), *reinterpret_cast<const uint4*>(base + offHi));
   };
-  // Row scales: lane (l16, g) reads the scale of row 16*(l16/4) + 4g + l16%4
-  // of its wave's strip, i.e. the (i, r) = (l16/4, l16%4) entry of its lane
-  // group's 16 values; row_scales hands every lane of the group entry (i, r)
-  // (DPP row_newbcast): one 4-byte LDS read per chunk instead of four
-  // 16-byte ones.
-  const int rowSa = w * 64 + 16 * (l16 >> 2) + 4 * g + (l16 & 3);
-  auto rdSa = [&](const uint8_t* st, int kb) -> float {  // kb: the tile's chunk index
+  // Row scales.  TR: lane (l16, g) needs rows 16 i + l16 of its wave's strip,
+  // one 4-byte read each.  Row mode: lane (l16, g) reads the scale of row
+  // 16*(l16/4) + 4g + l16%4, the (i, r) = (l16/4, l16%4) entry of its lane
+  // group's 16 values, and row_scales hands every lane of the group entry
+  // (i, r) (DPP row_newbcast).
+  // (TR: each of the four reads takes its offset through an empty asm, so the
+  // compiler cannot fuse them into one two-address LDS read: the fused form
+  // loses the operands' LDS objects, and the wait the compiler then puts in
+  // front of it for the pending direct loads drained the load pipeline every
+  // chunk, measured 60 -> 65 us on the 4096 x 2048 x 7168 Fprop.)
+  auto rdSa1 = [&](const uint8_t* st, int kb, int row) -> float {  // kb: the tile's chunk index
     kb += cb;
-    if (SC4) return scA[((kb >> 2) & 1) * 1024 + rowSa * 4 + (kb & 3)];
-    return *reinterpret_cast<const float*>(st + S::sa + 4 * rowSa);
+    if (TR) {
+      int off = SC4 ? ((kb >> 2) & 1) * 1024 + row * 4 + (kb & 3) : row;
+      asm volatile("" : "+v"(off));
+      return SC4 ? scA[off] : reinterpret_cast<const float*>(st + S::sa)[off];
+    }
+    if (SC4) return scA[((kb >> 2) & 1) * 1024 + row * 4 + (kb & 3)];
+    return *reinterpret_cast<const float*>(st + S::sa + 4 * row);
+  };
+  auto rdSa = [&](const uint8_t* st, int kb, float (&v)[kTM]) {
+    if (TR) {
+#pragma unroll
+      for (int i = 0; i < kTM; ++i) v[i] = rdSa1(st, kb, w * 64 + 16 * i + l16);
+    } else {
+      v[0] = rdSa1(st, kb, w * 64 + 16 * (l16 >> 2) + 4 * g + (l16 & 3));
+    }
   };
 
   auto rdSb = [&](const uint8_t* st, int j) -> float {
@@ -278,7 +305,9 @@ __global__ __launch_bounds__(kNT) void k_gemm_fp8(GemmArgs p) {
       for (int r = 0; r < 4; ++r) acc[i][j][r] = 0.f;
   if (KG && nk == 0) {
     // an expert without tokens: its gradient is zero
-    if (!p.accumulate) store_tile<kTM, kTN, OUT_F32, OUT_F32 ? 16 : 32>(acc, st0 + w * 12288, po, tc.m0 + w * 64, tc.mend, tc.n0, lane);
+    if (!p.accumulate)
+      store_tile<kTM, kTN, OUT_F32, OUT_F32 ? 16 : 32, 0, TR>(acc, st0 + w * 12288, po, tc.m0 + w * 64, tc.mend, tc.n0,
+                                                              lane);
     return;
   }
 
@@ -286,8 +315,8 @@ __global__ __launch_bounds__(kNT) void k_gemm_fp8(GemmArgs p) {
   v8i a[kTM];           // A fragments of the current chunk
   v8i bring[3];         // B fragments, ring over the global column index 8c + j
   v4f pp[kTM];          // MFMA partials, ring indexed by slot % 4
-  float sc[kTM][4];     // row scales (times the block's B scale) in use
-  float sa_nx = 0.f;    // the next chunk's row scales, as read (one per lane)
+  float sc[kTM][4];     // row scales (times the block's B scale) in use; TR: [i][0] only
+  float sa_nx[kTM] = {};  // the next chunk's row scales, as read (TR: one per sub-tile; else [0])
   float sbk_nx = 1.f;   // the next chunk's block B scale
   float sbc_prev = 0.f; // row mode: scale of the previous chunk's last column
   float sbc_first = 0.f;  // row mode: scale of the current chunk's column 0
@@ -310,28 +339,36 @@ __global__ __launch_bounds__(kNT) void k_gemm_fp8(GemmArgs p) {
     if (INTV != 1 && !promote_now) return;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const float s = ROW ? sc[i][r] * sbc : sc[i][r];
+      const float s = TR ? sc[i][0] : ROW ? sc[i][r] * sbc : sc[i][r];
       const float part = INTV == 1 ? pp[i][r] : pch[i][j][r];
       acc[i][j][r] = __builtin_fmaf(part, s, acc[i][j][r]);
     }
   };
   auto load_sc = [&](int i) {
     const float k = ROW ? 1.f : sbk_nx;
+    if (TR) {
+      sc[i][0] = sa_nx[i] * k;
+      return;
+    }
     switch (i) {
-      case 0: row_scales<0>(sa_nx, k, sc[0]); break;
-      case 1: row_scales<1>(sa_nx, k, sc[1]); break;
-      case 2: row_scales<2>(sa_nx, k, sc[2]); break;
-      default: row_scales<3>(sa_nx, k, sc[3]); break;
+      case 0: row_scales<0>(sa_nx[0], k, sc[0]); break;
+      case 1: row_scales<1>(sa_nx[0], k, sc[1]); break;
+      case 2: row_scales<2>(sa_nx[0], k, sc[2]); break;
+      default: row_scales<3>(sa_nx[0], k, sc[3]); break;
     }
   };
+  // the chunk partial of A fragment x and B fragment y (TR: B first)
   auto mfma = [&](const v8i& x, const v8i& y) -> v4f {
+    if (TR) return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(y, x, v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(x, y, v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
   };
   // exact mode: the chunk's partial as four BF16 instructions over quarters
   // of 8 K per lane (exact products, FP32 sums); lane group g covers the same
   // K positions of A and B in each, so together they cover the chunk once
   v8bf abf[kTM][4];  // A fragments of the current chunk in BF16 (exact mode)
-  auto mfma_ex = [&](const v8bf (&x)[4], const v8bf (&y)[4]) -> v4f {
+  auto mfma_ex = [&](const v8bf (&xa)[4], const v8bf (&ya)[4]) -> v4f {
+    const v8bf(&x)[4] = TR ? ya : xa;
+    const v8bf(&y)[4] = TR ? xa : ya;
     v4f c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x[0], y[0], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
     c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x[1], y[1], c, 0, 0, 0);
     c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x[2], y[2], c, 0, 0, 0);
@@ -355,7 +392,7 @@ __global__ __launch_bounds__(kNT) void k_gemm_fp8(GemmArgs p) {
 #pragma unroll
   for (int i = 0; i < kTM; ++i) {
     a[i] = rdA(st0, i);
-    if (i == 0) sa_nx = rdSa(st0, 0);
+    if (i == 0) rdSa(st0, 0, sa_nx);
     pp[i] = v4f{0.f, 0.f, 0.f, 0.f};
   }
   bring[0] = rdB(st0, 0);
@@ -409,8 +446,10 @@ __global__ __launch_bounds__(kNT) void k_gemm_fp8(GemmArgs p) {
         } else {
           const bool first = INTV == 0 ? c == 0 : c % INTV == 0;
           const v4f zero = {0.f, 0.f, 0.f, 0.f};
-          pch[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[i], bcur, first ? zero : pch[i][j], 0, 0, 0,
-                                                                       0, 0, 0);
+          pch[i][j] = TR ? __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bcur, a[i], first ? zero : pch[i][j], 0, 0,
+                                                                            0, 0, 0, 0)
+                         : __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[i], bcur, first ? zero : pch[i][j], 0, 0,
+                                                                            0, 0, 0, 0);
         }
         if (t >= kSkew) {
           const int tp = t - kSkew;
@@ -432,7 +471,7 @@ __global__ __launch_bounds__(kNT) void k_gemm_fp8(GemmArgs p) {
           // a[i] is no longer needed for this chunk: fetch the next chunk's
           a[i] = rdA(nxt, i);
           if (i == 0) {
-            sa_nx = rdSa(nxt, min(c + 1, nk - 1));
+            rdSa(nxt, min(c + 1, nk - 1), sa_nx);
             if (!ROW) sbk_nx = sbk_all[min(c + 1, nk - 1)];
           }
         }
@@ -479,11 +518,11 @@ __global__ __launch_bounds__(kNT) void k_gemm_fp8(GemmArgs p) {
   __builtin_amdgcn_s_barrier();
   fence();
   if constexpr (QO) {
-    static_assert(!OUT_F32 && !KG && SB_MODE == kSbBlock, "fused output quantization: BF16 Fprop/Dgrad only");
+    static_assert(!OUT_F32 && !KG && TR, "fused output quantization: BF16 Fprop/Dgrad only");
     store_tile_q<kTM, kTN, 32>(acc, st0 + w * 12288, po, tc.m0 + w * 64, tc.mend, tc.n0, lane);
   } else {
-    store_tile<kTM, kTN, OUT_F32, OUT_F32 ? 16 : 32>(acc, st0 + w * 12288, po, tc.m0 + w * 64, tc.mend, tc.n0,
-                                                   lane);
+    store_tile<kTM, kTN, OUT_F32, OUT_F32 ? 16 : 32, 0, TR>(acc, st0 + w * 12288, po, tc.m0 + w * 64, tc.mend, tc.n0,
+                                                            lane);
   }
 #endif  // __HIP_DEVICE_COMPILE__
 }
@@ -582,8 +621,18 @@ __global__ __launch_bounds__(kWNT) void k_gemm_fp8_wide(GemmArgs p) {
     const uint8_t* base = br + (wc * 128 + 16 * j) * kBK;
     return make_frag(*reinterpret_cast<const uint4*>(base + offLo), *reinterpret_cast<const uint4*>(base + offHi));
   };
-  const int rowSa = wr * 64 + 16 * (l16 >> 2) + 4 * g + (l16 & 3);
-  auto rdSa = [&](int kb) -> float { return scA[((kb >> 2) & 1) * 1024 + rowSa * 4 + (kb & 3)]; };
+  // B is the matrix instruction's first operand (as in k_gemm_fp8's block
+  // mode): lane 16 g + l16 holds row 16 i + l16 of each sub-tile
+  // (the offsets pass an empty asm so that the four reads stay four: see rdSa1
+  // in k_gemm_fp8)
+  auto rdSa = [&](int kb, float (&v)[kTM]) {
+#pragma unroll
+    for (int i = 0; i < kTM; ++i) {
+      int off = ((kb >> 2) & 1) * 1024 + (wr * 64 + 16 * i + l16) * 4 + (kb & 3);
+      asm volatile("" : "+v"(off));
+      v[i] = scA[off];
+    }
+  };
 
   float acc[kTM][kTN][4];
 #pragma unroll
@@ -593,25 +642,19 @@ __global__ __launch_bounds__(kWNT) void k_gemm_fp8_wide(GemmArgs p) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) acc[i][j][r] = 0.f;
 
-  v8i a[kTM];        // A fragments of the current chunk
-  v8i bring[2];      // B fragments: this column's and the next one's
-  v4f pp[kTM];       // MFMA partials, ring indexed by slot % 4
-  float sc[kTM][4];  // row scales times the block's B scale
-  float sa_nx = 0.f, sbk_nx = 1.f;
+  v8i a[kTM];          // A fragments of the current chunk
+  v8i bring[2];        // B fragments: this column's and the next one's
+  v4f pp[kTM];         // MFMA partials, ring indexed by slot % 4
+  float sc[kTM];       // row scales times the block's B scale
+  float sa_nx[kTM] = {};
+  float sbk_nx = 1.f;
   auto promote = [&](int i, int j) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) acc[i][j][r] = __builtin_fmaf(pp[i][r], sc[i][r], acc[i][j][r]);
+    for (int r = 0; r < 4; ++r) acc[i][j][r] = __builtin_fmaf(pp[i][r], sc[i], acc[i][j][r]);
   };
-  auto load_sc = [&](int i) {
-    switch (i) {
-      case 0: row_scales<0>(sa_nx, sbk_nx, sc[0]); break;
-      case 1: row_scales<1>(sa_nx, sbk_nx, sc[1]); break;
-      case 2: row_scales<2>(sa_nx, sbk_nx, sc[2]); break;
-      default: row_scales<3>(sa_nx, sbk_nx, sc[3]); break;
-    }
-  };
-  auto mfma = [&](const v8i& x, const v8i& y) -> v4f {
-    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(x, y, v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
+  auto load_sc = [&](int i) { sc[i] = sa_nx[i] * sbk_nx; };
+  auto mfma = [&](const v8i& x, const v8i& y) -> v4f {  // B first
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(y, x, v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
   };
   auto fence = [] { asm volatile("" ::: "memory"); };
 
@@ -637,7 +680,7 @@ __global__ __launch_bounds__(kWNT) void k_gemm_fp8_wide(GemmArgs p) {
 #pragma unroll
   for (int i = 0; i < kTM; ++i) {
     a[i] = rdA(sa0, i);
-    if (i == 0) sa_nx = rdSa(0);
+    if (i == 0) rdSa(0, sa_nx);
     pp[i] = v4f{0.f, 0.f, 0.f, 0.f};
   }
   bring[0] = rdB(sb0, 0);
@@ -679,7 +722,7 @@ __global__ __launch_bounds__(kWNT) void k_gemm_fp8_wide(GemmArgs p) {
           issue_b(c2, bcur, i);
           a[i] = rdA(anxt, i);
           if (i == 0) {
-            sa_nx = rdSa(min(c + 1, nk - 1));
+            rdSa(min(c + 1, nk - 1), sa_nx);
             sbk_nx = sbk_all[wc * nk + min(c + 1, nk - 1)];
           }
         }
@@ -721,8 +764,8 @@ __global__ __launch_bounds__(kWNT) void k_gemm_fp8_wide(GemmArgs p) {
     static_assert(!OUT_F32 && !GROUPED, "fused output quantization: BF16 Fprop/Dgrad only");
     store_tile_q<kTM, kTN, 32>(acc, ep + (w & 1) * 12288, p, tc.m0 + wr * 64, tc.mend, tc.n0 + wc * 128, lane);
   } else {
-    store_tile<kTM, kTN, OUT_F32, OUT_F32 ? 16 : 32>(acc, ep + (w & 1) * 12288, p, tc.m0 + wr * 64, tc.mend,
-                                                   tc.n0 + wc * 128, lane);
+    store_tile<kTM, kTN, OUT_F32, OUT_F32 ? 16 : 32, 0, true>(acc, ep + (w & 1) * 12288, p, tc.m0 + wr * 64, tc.mend,
+                                                              tc.n0 + wc * 128, lane);
   }
 #endif  // __HIP_DEVICE_COMPILE__
 }

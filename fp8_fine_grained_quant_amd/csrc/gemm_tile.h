@@ -128,12 +128,14 @@ __device__ __forceinline__ bool tile_coord(const GemmArgs& p, TileCoord& tc) {
 // dirty lines that the kernels after them must write back (measured:
 // grouped Wgrad 796 -> 618 us, and the kernel after it 521 -> 465 us).
 //
-// Writes one wave's WM x WN accumulator block (MFMA 16x16 result layout:
-// lane l holds rows 4*(l/16) + r, column l%16 of each sub-tile) to C, staged
-// through the wave's private LDS region `ep` in passes of ER rows so that
-// every global access is a full 16-byte row segment.  Rows at or beyond
-// `mend` are not written.
-template <int TM, int TN, int OUT_F32, int ER, int NTS = 0>
+// Writes one wave's WM x WN accumulator block to C, staged through the
+// wave's private LDS region `ep` in passes of ER rows so that every global
+// access is a full 16-byte row segment.  Rows at or beyond `mend` are not
+// written.  Accumulator layout of sub-tile (i, j), lane l = 16 g + l16:
+// TRL = 0 (A the matrix instruction's first operand): rows 16 i + 4 g + r,
+// column 16 j + l16; TRL = 1 (B first): row 16 i + l16, columns
+// 16 j + 4 g + r.
+template <int TM, int TN, int OUT_F32, int ER, int NTS = 0, bool TRL = false>
 __device__ __forceinline__ void store_tile(const float (&acc)[TM][TN][4], uint8_t* ep, const GemmArgs& p,
                                            int64_t row0, int64_t mend, int col0, int lane) {
   constexpr int WM = 16 * TM, WN = 16 * TN;
@@ -153,15 +155,28 @@ __device__ __forceinline__ void store_tile(const float (&acc)[TM][TN][4], uint8_
 #pragma unroll
     for (int i = pass * (ER / 16); i < (pass + 1) * (ER / 16); ++i)
 #pragma unroll
-      for (int j = 0; j < TN; ++j)
+      for (int j = 0; j < TN; ++j) {
+        if constexpr (TRL) {
+          const int rl = 16 * i + l16 - pass * ER, cl = 16 * j + 4 * g;
+          if (OUT_F32) {
+            *reinterpret_cast<float4*>(ep + rl * P + 4 * cl) =
+                make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
+          } else {
+            const uint32_t lo = f32_to_bf16_rne(acc[i][j][0]) | (f32_to_bf16_rne(acc[i][j][1]) << 16);
+            const uint32_t hi = f32_to_bf16_rne(acc[i][j][2]) | (f32_to_bf16_rne(acc[i][j][3]) << 16);
+            *reinterpret_cast<uint2*>(ep + rl * P + 2 * cl) = make_uint2(lo, hi);
+          }
+        } else {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int rl = 16 * i + 4 * g + r - pass * ER, cl = 16 * j + l16;
-          if (OUT_F32)
-            *reinterpret_cast<float*>(ep + rl * P + 4 * cl) = acc[i][j][r];
-          else
-            *reinterpret_cast<uint16_t*>(ep + rl * P + 2 * cl) = (uint16_t)f32_to_bf16_rne(acc[i][j][r]);
+          for (int r = 0; r < 4; ++r) {
+            const int rl = 16 * i + 4 * g + r - pass * ER, cl = 16 * j + l16;
+            if (OUT_F32)
+              *reinterpret_cast<float*>(ep + rl * P + 4 * cl) = acc[i][j][r];
+            else
+              *reinterpret_cast<uint16_t*>(ep + rl * P + 2 * cl) = (uint16_t)f32_to_bf16_rne(acc[i][j][r]);
+          }
         }
+      }
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS writes are done
     __builtin_amdgcn_wave_barrier();
 #pragma unroll
@@ -183,13 +198,15 @@ __device__ __forceinline__ void store_tile(const float (&acc)[TM][TN][4], uint8_
   }
 }
 
-// The epilogue with the output's own quantization fused in (BF16 output):
-// every wave's strip is 128 columns wide and starts on a multiple of 128, so
-// each of its rows holds exactly one 1x128 group of the output.  Each value
-// is first rounded to BF16 (RNE); the group's max-abs, scale and codes are
-// then taken from those BF16 values with the quantizers' own arithmetic
-// (group_scale, pack4_e4m3), so the codes and scales equal what
-// quant_act_1x128 computes from the stored BF16 output.  The BF16 values
+// The epilogue with the output's own quantization fused in (BF16 output,
+// accumulators in the TRL = 1 layout of store_tile: lane 16 g + l16 holds row
+// 16 i + l16, columns 16 j + 4 g + r): every wave's strip is 128 columns wide
+// and starts on a multiple of 128, so each of its rows holds exactly one 1x128
+// group of the output, spread over the four lanes l16, l16 + 16, l16 + 32,
+// l16 + 48.  Each value is first rounded to BF16 (RNE); the group's max-abs,
+// scale and codes are then taken from those BF16 values with the quantizers'
+// own arithmetic (group_scale, pack4_e4m3), so the codes and scales equal
+// what quant_act_1x128 computes from the stored BF16 output.  The BF16 values
 // leave through store_tile (skipped when p.C is NULL); the scaled values are
 // staged through the wave's LDS region in passes of 16 rows so that every
 // code store is a full 16-byte row segment.  The accumulators are only read.
@@ -201,7 +218,7 @@ __device__ __forceinline__ void store_tile_q(const float (&acc)[TM][TN][4], uint
   const int g = lane >> 4, l16 = lane & 15;
   auto rounded = [](float v) { return bf16_to_f32(f32_to_bf16_rne(v)); };
   if (p.C != nullptr) {
-    store_tile<TM, TN, 0, ER>(acc, ep, p, row0, mend, col0, lane);
+    store_tile<TM, TN, 0, ER, 0, true>(acc, ep, p, row0, mend, col0, lane);
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the staging area is read out
     __builtin_amdgcn_wave_barrier();
   }
@@ -211,33 +228,35 @@ __device__ __forceinline__ void store_tile_q(const float (&acc)[TM][TN][4], uint
       __builtin_amdgcn_s_waitcnt(0xC07F);
       __builtin_amdgcn_wave_barrier();
     }
+    uint32_t m = 0;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      uint32_t m = 0;
+    for (int j = 0; j < TN; ++j)
 #pragma unroll
-      for (int j = 0; j < TN; ++j) m = max(m, abs_bits(rounded(acc[i][j][r])));
-      m = row16_max_u32(m);  // the 16 lanes of lane group g hold the row's 128 columns
-      float sc, inv;
-      group_scale(__uint_as_float(m), sc, inv);
-      const int64_t row = row0 + 16 * i + 4 * g + r;
-      if (l16 == 0 && row < mend) p.so[row * p.ld_so + (col0 >> 7)] = sc;
+      for (int r = 0; r < 4; ++r) m = max(m, abs_bits(rounded(acc[i][j][r])));
+    m = max(m, (uint32_t)__shfl_xor((int)m, 16));  // the row's other three lanes
+    m = max(m, (uint32_t)__shfl_xor((int)m, 32));
+    float sc, inv;
+    group_scale(__uint_as_float(m), sc, inv);
+    const int64_t row = row0 + 16 * i + l16;
+    if (g == 0 && row < mend) p.so[row * p.ld_so + (col0 >> 7)] = sc;
 #pragma unroll
-      for (int j = 0; j < TN; ++j)
-        *reinterpret_cast<float*>(ep + (4 * g + r) * P + 4 * (16 * j + l16)) = rounded(acc[i][j][r]) * inv;
-    }
+    for (int j = 0; j < TN; ++j)
+      *reinterpret_cast<float4*>(ep + l16 * P + 4 * (16 * j + 4 * g)) =
+          make_float4(rounded(acc[i][j][0]) * inv, rounded(acc[i][j][1]) * inv, rounded(acc[i][j][2]) * inv,
+                      rounded(acc[i][j][3]) * inv);
     __builtin_amdgcn_s_waitcnt(0xC07F);
     __builtin_amdgcn_wave_barrier();
     // lane (rl = lane / 8, ch = lane % 8): 16 consecutive values of row rl
 #pragma unroll
     for (int it = 0; it < 2; ++it) {
       const int rl = it * 8 + (lane >> 3), ch = lane & 7;
-      const int64_t row = row0 + 16 * i + rl;
+      const int64_t orow = row0 + 16 * i + rl;
       const float4* src = reinterpret_cast<const float4*>(ep + rl * P + 64 * ch);
       const float4 v0 = src[0], v1 = src[1], v2 = src[2], v3 = src[3];
-      if (row >= mend) continue;
+      if (orow >= mend) continue;
       const uint32_t w0 = pack4_e4m3(v0.x, v0.y, v0.z, v0.w), w1 = pack4_e4m3(v1.x, v1.y, v1.z, v1.w);
       const uint32_t w2 = pack4_e4m3(v2.x, v2.y, v2.z, v2.w), w3 = pack4_e4m3(v3.x, v3.y, v3.z, v3.w);
-      st_stream16<0>(p.qo + row * p.ld_qo + col0 + 16 * ch, w0, w1, w2, w3);
+      st_stream16<0>(p.qo + orow * p.ld_qo + col0 + 16 * ch, w0, w1, w2, w3);
     }
   }
 }
