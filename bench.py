@@ -341,12 +341,16 @@ def tiny_gemm_latency(dev, reps=200):
             "launches": reps}
 
 
-def telemetry(ops, seconds=1.5):
+def telemetry(ops, seconds=3.0, settle=1.2):
     """GPU clock, power and activity while the step runs back to back for
     `seconds` (amdsmi, sampled every 20 ms from a thread), and the step time
-    of that sustained loop.  Every device amdsmi lists is sampled; the one
-    reported is the one whose PCI bus matches cuda:0, else the busiest.
-    Returns the reason instead if telemetry is unavailable."""
+    of that sustained loop.  The device's metrics table trails the hardware
+    by about a second (measured: a busy GPU still read 214 MHz and 1%
+    activity for the first ~1 s of a loop, then ~1.9-2.0 GHz and 100%), so
+    only samples taken `settle` seconds or more after the loop started are
+    reported.  Every device amdsmi lists is sampled; the one reported is the
+    one whose PCI bus matches cuda:0, else the busiest.  Returns the reason
+    instead if telemetry is unavailable."""
     import threading
     import torch
     try:
@@ -364,9 +368,13 @@ def telemetry(ops, seconds=1.5):
                 bus.append("?")
         samples = [{"clk": [], "pwr": [], "act": []} for _ in handles]
         stop = threading.Event()
+        t_keep = [float("inf")]  # samples before this time are dropped
 
         def sample():
             while not stop.is_set():
+                if time.perf_counter() < t_keep[0]:
+                    time.sleep(0.02)
+                    continue
                 for h, smp in zip(handles, samples):
                     try:
                         c = amdsmi.amdsmi_get_clock_info(h, amdsmi.AmdSmiClkType.GFX)
@@ -392,6 +400,7 @@ def telemetry(ops, seconds=1.5):
         th.start()
         torch.cuda.synchronize()
         t0, n = time.perf_counter(), 0
+        t_keep[0] = t0 + settle
         while time.perf_counter() - t0 < seconds:
             for _ in range(10):
                 for op in ops:
@@ -420,7 +429,9 @@ def telemetry(ops, seconds=1.5):
                             "samples": len(smp["pwr"])},
                 "gfx_activity_pct": {"median": med(smp["act"]), "samples": len(smp["act"])},
                 "sustained_ms_per_step": round(dt * 1e3 / n, 4), "steps": n,
-                "note": "sampled while the step ran back to back for ~1.5 s, right before the timed region"}
+                "note": f"sampled every 20 ms over the last {seconds - settle:.1f} s of {seconds:.1f} s of the step "
+                        "running back to back, right before the timed region (the metrics table trails the "
+                        f"hardware by about a second, so the first {settle:.1f} s are not sampled)"}
     finally:
         try:
             amdsmi.amdsmi_shut_down()
