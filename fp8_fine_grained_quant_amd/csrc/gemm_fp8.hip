@@ -377,10 +377,17 @@ __global__ __launch_bounds__(kNT) void k_gemm_fp8(GemmArgs p) {
   auto fence = [] { asm volatile("" ::: "memory"); };
 
   // ---- prologue: block B scales of every chunk to LDS, chunks 0 and 1 in
-  // flight, chunk 0 published, its fragments and scales in registers
+  // flight, chunk 0 published, its fragments and scales in registers.  The
+  // block scales go by direct loads too (4 bytes per lane, entries past the
+  // last chunk out of range), issued first so that their latency overlaps the
+  // chunks' instead of preceding it (a load into registers and an LDS write
+  // made the prologue wait for them before the first chunk's loads).
   if (!ROW) {
     const float* psb = sbp + (int64_t)(tc.n0 / 128) * p.sb_rs;
-    for (int q = tid; q < nk; q += kNT) sbk_all[q] = psb[(int64_t)q * p.sb_cs];
+    const __amdgpu_buffer_rsrc_t rK = make_rsrc(psb, (uint32_t)(((int64_t)(nk - 1) * p.sb_cs + 1) * 4));
+    for (int r = 0; r * kNT < nk; ++r)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rK, (lds_ptr)(sbk_all + r * kNT + w * 64), 4,
+                                               (uint32_t)((r * kNT + w * 64 + lane) * p.sb_cs * 4), 0, 0, 0);
   }
   fence();
   issue(0, st0);
@@ -658,11 +665,15 @@ __global__ __launch_bounds__(kWNT) void k_gemm_fp8_wide(GemmArgs p) {
   };
   auto fence = [] { asm volatile("" ::: "memory"); };
 
-  // ---- prologue: both halves' block B scales of every chunk to LDS; A(0),
+  // ---- prologue: both halves' block B scales of every chunk to LDS (direct
+  // loads as in k_gemm_fp8: waves 0-3 the first half, 4-7 the second); A(0),
   // B(0), A(1), B(1) in flight in that order; chunk 0 published
   {
-    const float* psb = sbp + (int64_t)(tc.n0 / 128) * p.sb_rs;
-    for (int q = tid; q < 2 * nk; q += kWNT) sbk_all[q] = psb[(int64_t)(q / nk) * p.sb_rs + (int64_t)(q % nk) * p.sb_cs];
+    const float* psb = sbp + (int64_t)(tc.n0 / 128 + wc) * p.sb_rs;
+    const __amdgpu_buffer_rsrc_t rK = make_rsrc(psb, (uint32_t)(((int64_t)(nk - 1) * p.sb_cs + 1) * 4));
+    for (int r = 0; r * 256 < nk; ++r)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rK, (lds_ptr)(sbk_all + wc * kMaxChunks + r * 256 + wr * 64), 4,
+                                               (uint32_t)((r * 256 + wr * 64 + lane) * p.sb_cs * 4), 0, 0, 0);
   }
   fence();
 #pragma unroll
@@ -684,7 +695,7 @@ __global__ __launch_bounds__(kWNT) void k_gemm_fp8_wide(GemmArgs p) {
     pp[i] = v4f{0.f, 0.f, 0.f, 0.f};
   }
   bring[0] = rdB(sb0, 0);
-  sbk_nx = sbk_all[wc * nk];
+  sbk_nx = sbk_all[wc * kMaxChunks];
 #pragma unroll
   for (int i = 0; i < kTM; ++i) load_sc(i);
 
@@ -723,7 +734,7 @@ __global__ __launch_bounds__(kWNT) void k_gemm_fp8_wide(GemmArgs p) {
           a[i] = rdA(anxt, i);
           if (i == 0) {
             rdSa(min(c + 1, nk - 1), sa_nx);
-            sbk_nx = sbk_all[wc * nk + min(c + 1, nk - 1)];
+            sbk_nx = sbk_all[wc * kMaxChunks + min(c + 1, nk - 1)];
           }
         }
         __builtin_amdgcn_sched_barrier(0);
