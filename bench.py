@@ -995,6 +995,7 @@ def main():
     }
     print(json.dumps(out), flush=True)
     if args.launch_log:
+        os.makedirs(os.path.dirname(os.path.abspath(args.launch_log)), exist_ok=True)
         with open(args.launch_log, "w") as f:
             json.dump(LAUNCHES, f)
 
