@@ -37,6 +37,9 @@ import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libfp8q.so")
+# the same library built with FP8Q_DEBUG: its grouped entry points also read
+# the device expert offsets back and reject malformed ones (synchronously)
+DEBUG_LIB_PATH = os.path.join(_HERE, "libfp8q_debug.so")
 
 FP8Q_BF16, FP8Q_F32 = 0, 1
 _STATUS = ["FP8Q_OK", "FP8Q_ERR_NULL", "FP8Q_ERR_SHAPE", "FP8Q_ERR_STRIDE",
@@ -78,8 +81,25 @@ def load_library(path=LIB_PATH):
     global _lib
     if _lib is not None:
         return _lib
+    _lib = _open(path)
+    return _lib
+
+
+_debug_lib = None
+
+
+def load_debug_library():
+    """libfp8q_debug.so (once), with the same C signatures; the wrappers of
+    this module keep calling libfp8q.so."""
+    global _debug_lib
+    if _debug_lib is None:
+        _debug_lib = _open(DEBUG_LIB_PATH)
+    return _debug_lib
+
+
+def _open(path):
     if not os.path.exists(path):
-        raise RuntimeError(f"libfp8q.so not built ({path}); run __graft_entry__.build()")
+        raise RuntimeError(f"{os.path.basename(path)} not built ({path}); run __graft_entry__.build()")
     lib = ctypes.CDLL(path)
     P, I64, I32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
     sig = {
@@ -112,7 +132,6 @@ def load_library(path=LIB_PATH):
         fn = getattr(lib, name)
         fn.argtypes = args
         fn.restype = res
-    _lib = lib
     return lib
 
 

@@ -1,13 +1,18 @@
 // C ABI of libfp8q: host-side argument validation, then the asynchronous
 // launch on the caller's stream.  Nothing here allocates, synchronises,
 // prints or throws.  The entry points and their rules are documented in
-// include/fp8q.h.
+// include/fp8q.h.  (Built with FP8Q_DEBUG, as libfp8q_debug.so, the grouped
+// entry points also read the expert offsets back and check them, which
+// synchronises the stream.)
 
 #include "../../include/fp8q.h"
 #include "launch.h"
 
 #include <atomic>
 #include <stdint.h>
+#ifdef FP8Q_DEBUG
+#include <vector>
+#endif
 
 namespace fp8q {
 
@@ -43,6 +48,26 @@ inline bool valid_dtype(fp8q_dtype t) { return t == FP8Q_BF16 || t == FP8Q_F32; 
 inline fp8q_status launched(hipError_t e) { return e == hipSuccess ? FP8Q_OK : FP8Q_ERR_LAUNCH; }
 
 constexpr int64_t kMaxGroups = (int64_t(1) << 31) - 1;
+
+// Expert offsets live on the device and the product library never reads
+// them: malformed offsets are undefined behaviour there.  The FP8Q_DEBUG
+// build copies them to the host (after the work already on the stream) and
+// rejects any that break the rule offsets[0] = 0, non-decreasing,
+// offsets[E] = M_total, with FP8Q_ERR_SHAPE and nothing enqueued.
+fp8q_status debug_check_offsets(const int32_t* offsets, int64_t E, int64_t M_total, hipStream_t stream) {
+#ifdef FP8Q_DEBUG
+  std::vector<int32_t> h((size_t)E + 1);
+  if (hipMemcpyAsync(h.data(), offsets, h.size() * sizeof(int32_t), hipMemcpyDeviceToHost, stream) != hipSuccess ||
+      hipStreamSynchronize(stream) != hipSuccess)
+    return FP8Q_ERR_LAUNCH;
+  if (h[0] != 0 || h[(size_t)E] != M_total) return FP8Q_ERR_SHAPE;
+  for (size_t e = 0; e < (size_t)E; ++e)
+    if (h[e + 1] < h[e]) return FP8Q_ERR_SHAPE;
+#else
+  (void)offsets; (void)E; (void)M_total; (void)stream;
+#endif
+  return FP8Q_OK;
+}
 constexpr int64_t kMaxDim = (int64_t(1) << 31) - 1;
 constexpr int64_t kMaxContraction = 1024 * 128;  // the GEMM keeps one scale per chunk in LDS
 
@@ -153,6 +178,7 @@ fp8q_status fp8q_quant_transpose_grouped(const void* x, fp8q_dtype xt, int64_t r
   if (!offsets) return FP8Q_ERR_NULL;
   if (!aligned4(offsets)) return FP8Q_ERR_ALIGN;
   if (cap / 128 > 65535) return FP8Q_ERR_SHAPE;  // grid y limit
+  if (const fp8q_status d = debug_check_offsets(offsets, E, rows, stream); d != FP8Q_OK) return d;
   return launched(fp8q::launch_quant_transpose_grouped(x, xt == FP8Q_BF16, rows, cols, ld_x, offsets, E, q_t, ld_qt,
                                                        scale_t, ld_st, stream));
 }
@@ -300,6 +326,7 @@ static fp8q_status fp8q_grouped_gemm_impl(int exact, const uint8_t* xq, const fl
     return FP8Q_ERR_ALIGN;
   // the launch grid: a partial m-tile per expert on top of ceil(M_total / 256)
   if (((M_total + 255) / 256 + E) * (N / 128) > kMaxGroups) return FP8Q_ERR_SHAPE;
+  if (const fp8q_status d = debug_check_offsets(offsets, E, M_total, stream); d != FP8Q_OK) return d;
   GemmArgs a{};
   a.A = xq; a.B = wq; a.sa = xs; a.sb = ws; a.C = y;
   a.lda = K; a.ldb = K; a.ld_sa = K / 128; a.sb_rs = K / 128; a.sb_cs = 1; a.ldc = ld_y;
@@ -330,6 +357,7 @@ fp8q_status fp8q_grouped_gemm_dgrad(const uint8_t* dyq, const float* dys, const 
   if (!aligned16(dyq) || !aligned16(wq_t) || !aligned4(dys) || !aligned4(ws) || !aligned4(offsets))
     return FP8Q_ERR_ALIGN;
   if (((M_total + 255) / 256 + E) * (K / 128) > kMaxGroups) return FP8Q_ERR_SHAPE;
+  if (const fp8q_status d = debug_check_offsets(offsets, E, M_total, stream); d != FP8Q_OK) return d;
   // Per expert: the Dgrad NT form (A = dY rows of the expert, contraction N)
   // with B = W_e^T = columns [eN, (e+1)N) of the stacked transposed codes
   // [K, E*N], and the block scale of (output column k, chunk kb) at
@@ -362,6 +390,7 @@ fp8q_status fp8q_grouped_gemm_wgrad(const uint8_t* dyq_t, const float* dys_t, co
       !aligned4(offsets))
     return FP8Q_ERR_ALIGN;
   if (E * ((N + 255) / 256) * (K / 128) > kMaxGroups) return FP8Q_ERR_SHAPE;
+  if (const fp8q_status d = debug_check_offsets(offsets, E, M_total, stream); d != FP8Q_OK) return d;
   // Per expert: the Wgrad NT form over the expert's padded token chunks
   // (A = dY^T codes [N, ld_t], B = X^T codes [K, ld_t], one scale per row
   // per chunk), written to dw + e*N*K.
@@ -524,6 +553,7 @@ fp8q_status fp8q_grouped_gemm_mx(const uint8_t* xq, const uint8_t* xs, const uin
   if (!aligned16(xq) || !aligned16(wq) || !aligned4(xs) || !aligned4(ws) || !aligned4(offsets))
     return FP8Q_ERR_ALIGN;
   if (((M_total + 255) / 256 + E) * (N / 128) > kMaxGroups) return FP8Q_ERR_SHAPE;
+  if (const fp8q_status d = debug_check_offsets(offsets, E, M_total, stream); d != FP8Q_OK) return d;
   fp8q::MxArgs a{};
   a.g.A = xq; a.g.B = wq; a.g.C = y;
   a.g.lda = K; a.g.ldb = K; a.g.ldc = ld_y;
@@ -552,6 +582,7 @@ fp8q_status fp8q_grouped_gemm_mx_dgrad(const uint8_t* dyq, const uint8_t* dys, c
   if (!aligned16(dyq) || !aligned16(wq_t) || !aligned4(dys) || !aligned4(ws_t) || !aligned4(offsets))
     return FP8Q_ERR_ALIGN;
   if (((M_total + 255) / 256 + E) * (K / 128) > kMaxGroups) return FP8Q_ERR_SHAPE;
+  if (const fp8q_status d = debug_check_offsets(offsets, E, M_total, stream); d != FP8Q_OK) return d;
   // Per expert: C = dY rows . B^T with B = W_e^T = columns [eN, (e+1)N) of
   // the stacked transposed codes (row stride E*N) and of their scales (E*N/32)
   fp8q::MxArgs a{};

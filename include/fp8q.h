@@ -56,6 +56,11 @@
  *     16-byte boundaries and have row strides that are multiples of 16 bytes
  *     (vector access), else FP8Q_ERR_ALIGN.  Scale arrays need 4-byte alignment.
  *   - Inputs must be finite; NaN or Inf inputs give unspecified codes.
+ *   - Device-resident expert offsets (the grouped entry points) are never
+ *     read on the host by libfp8q.so.  The same sources compiled with
+ *     FP8Q_DEBUG (libfp8q_debug.so) copy them to the host first, wait for
+ *     the stream, and return FP8Q_ERR_SHAPE, enqueuing nothing, unless
+ *     offsets[0] = 0, they never decrease and offsets[E] = M_total.
  *   - Work is sized for one GPU's share; every size must fit in int64 and the
  *     number of 128-groups of one call must stay below 2^31.  A GEMM's
  *     contraction length is at most 131072 (1024 chunks of 128).
@@ -242,8 +247,9 @@ fp8q_status fp8q_gemm_wgrad(const uint8_t* dyq_t, const float* dys_t, const uint
  *   xq : [M_total, K] codes, xs : [M_total, K/128]
  *   wq : [E, N, K] codes,    ws : [E, N/128, K/128]
  *   offsets : DEVICE int32 [E+1]; offsets[0] = 0, non-decreasing,
- *             offsets[E] = M_total (not checked on the host: it stays on the
- *             device; malformed offsets are undefined behaviour)
+ *             offsets[E] = M_total (it stays on the device and the product
+ *             library does not check it: malformed offsets are undefined
+ *             behaviour; the FP8Q_DEBUG build rejects them, FP8Q_ERR_SHAPE)
  *   y  : [M_total, N] of type yt, row stride ld_y
  * Rules: K % 128 == 0, N % 128 == 0, 1 <= E <= 65536, any M_total >= 0.
  * Experts with no rows are skipped; no host synchronisation happens.
@@ -464,7 +470,8 @@ fp8q_status fp8q_gemm_mx(const uint8_t* aq, const uint8_t* as, int64_t lda, int6
  *   xq : [M_total, K] codes,    xs : [M_total, K/32] E8M0 bytes (contiguous)
  *   wq : [E, N, K] codes,       ws : [E, N, K/32] E8M0 bytes (contiguous)
  *   offsets : DEVICE int32 [E+1], as for fp8q_grouped_gemm (never read on
- *             the host; malformed offsets are undefined behaviour)
+ *             the host by the product library; malformed offsets are undefined
+ *             behaviour, the FP8Q_DEBUG build rejects them)
  *   y  : [M_total, N] of type yt, row stride ld_y
  * Each output element takes the same instructions in the same order as in
  * fp8q_gemm_mx on that expert's rows, so the two agree bit for bit.

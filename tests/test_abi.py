@@ -30,20 +30,28 @@ def lib():
     return fq.load_library()
 
 
-def test_exports_every_declared_symbol(lib):
+BOTH = pytest.mark.parametrize("path", [fq.LIB_PATH, fq.DEBUG_LIB_PATH], ids=["product", "debug"])
+
+
+@BOTH
+def test_exports_every_declared_symbol(lib, path):
+    """Both builds (the product library and its FP8Q_DEBUG twin) load and
+    export every entry point the header declares."""
+    handle = lib if path == fq.LIB_PATH else fq.load_debug_library()
     names = declared_functions()
     assert set(names) == set(fq.EXPORTS)
-    out = subprocess.run(["nm", "-D", "--defined-only", fq.LIB_PATH], capture_output=True, text=True).stdout
+    out = subprocess.run(["nm", "-D", "--defined-only", path], capture_output=True, text=True).stdout
     exported = set(re.findall(r"\bT (fp8q_\w+)", out))
     for n in names:
         assert n in exported, n
-        assert getattr(lib, n) is not None
+        assert getattr(handle, n) is not None
 
 
-def test_every_kernel_launch_stub_is_defined(lib):
+@BOTH
+def test_every_kernel_launch_stub_is_defined(lib, path):
     """A kernel whose host-side launch stub is missing makes dlopen fail on the
     GPU machine only; catch it here."""
-    out = subprocess.run(["nm", "-D", fq.LIB_PATH], capture_output=True, text=True).stdout
+    out = subprocess.run(["nm", "-D", path], capture_output=True, text=True).stdout
     undefined = [l for l in out.splitlines() if " U " in l and "__device_stub__" in l]
     assert not undefined, undefined[:3]
     # quantizers (1x128, 128x128, transposing, grouped, dual; MX rows and
