@@ -5,7 +5,11 @@ s = amax/448 and 448/amax must be IEEE-rounded), FP32 denormals kept, and
 packed-FP32 VALU instructions disabled for all device code.
 
 Each source compiles to its own object (in parallel, under _build/); the
-product library links them all.  libfp8q_debug.so links the same kernel
+product library links them all.  Every kernel must keep its arrays in
+registers: the build fails if a kernel uses scratch (private) memory or an
+unroll the source asks for does not happen (either one turned a quantizer's
+16 x 4 register array into scratch traffic, 2.5x slower, with only a
+warning).  libfp8q_debug.so links the same kernel
 objects with api.cpp compiled under FP8Q_DEBUG, whose grouped entry points
 also copy the device expert offsets to the host and reject malformed ones
 (a synchronous check the product library never makes).
@@ -42,6 +46,7 @@ FLAGS = [
     "-I", os.path.join(ROOT, "include"),
 ]
 _NOISE = "'-packed-fp32-ops' is not a recognized feature"
+_USAGE = "kernel-resource-usage"
 
 
 def _run(cmd, verbose):
@@ -51,12 +56,34 @@ def _run(cmd, verbose):
     err = "\n".join(l for l in res.stderr.splitlines() if _NOISE not in l)
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
-    if verbose and err.strip():
-        print(err, file=sys.stderr)
+    return err
+
+
+def check_resource_report(src, report):
+    """Raise if the compiler's report names a kernel with scratch memory or a
+    requested unroll that did not happen; returns the report's other lines."""
+    kernel, bad, rest = None, [], []
+    for line in report.splitlines():
+        if _USAGE in line:
+            if "Function Name:" in line:
+                kernel = line.split("Function Name:")[1].split("[")[0].strip()
+            elif "ScratchSize" in line and int(line.split("ScratchSize [bytes/lane]:")[1].split()[0]) > 0:
+                bad.append(f"{kernel}: {line.split('remark:')[-1].split('[')[0].strip()}")
+            continue
+        if "loop not unrolled" in line:
+            bad.append(line.strip())
+        rest.append(line)
+    if bad:
+        raise RuntimeError(f"{src}: kernels must not use scratch memory or miss an unroll:\n" + "\n".join(bad))
+    return "\n".join(rest)
 
 
 def _compile(src, obj, extra, verbose):
-    _run([HIPCC] + FLAGS + extra + ["-c", os.path.join(CSRC, src), "-o", obj], verbose)
+    report = [f"-Rpass-analysis={_USAGE}"] if src.endswith(".hip") else []
+    err = _run([HIPCC] + FLAGS + extra + report + ["-c", os.path.join(CSRC, src), "-o", obj], verbose)
+    err = check_resource_report(src, err)
+    if verbose and err.strip():
+        print(err, file=sys.stderr)
     return obj
 
 

@@ -47,6 +47,17 @@ __device__ __forceinline__ uint32_t pack4_e4m3(float v0, float v1, float v2, flo
   return (uint32_t)w;
 }
 
+// The same for values of a group scaled by fl32(448/amax') of its own
+// max-abs: |x| <= amax' gives |fl32(x * fl32(448/amax'))| <= 448 (1 + 2^-23),
+// below the 464 from which the conversion turns to NaN, and the conversion
+// rounds (448, 464) to 448.  The clamp can change no code, so it is left out
+// (it was a sixth of the dual quantizer's vector instructions).
+__device__ __forceinline__ uint32_t pack4_e4m3_grp(float v0, float v1, float v2, float v3) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(v0, v1, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(v2, v3, w, true);
+  return (uint32_t)w;
+}
+
 // Group scale rule: s = fl32(amax'/448) (stored), inv = fl32(448/amax').
 // Both divisions are IEEE correctly rounded (the library is built without
 // fast-math and with correctly rounded FP32 division).
@@ -64,6 +75,12 @@ __device__ __forceinline__ uint32_t row16_max_u32(uint32_t v) {
   v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)0, (int)v, 0x122, 0xF, 0xF, false));
   v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)0, (int)v, 0x121, 0xF, 0xF, false));
   return v;
+}
+
+// Lane L of every 16-lane row, broadcast to the whole row (DPP row_newbcast).
+template <int L>
+__device__ __forceinline__ float row_bcast(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x150 + L, 0xF, 0xF, false));
 }
 
 // Max over the whole 64-lane wave; every lane receives the result.

@@ -132,12 +132,6 @@ struct IC {
   static constexpr int value = V;
 };
 
-// Lane L of every 16-lane row, broadcast to the whole row (DPP row_newbcast).
-template <int L>
-__device__ __forceinline__ float row_bcast(float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x150 + L, 0xF, 0xF, false));
-}
-
 // The four row scales of sub-tile I held by lanes 4I .. 4I+3 of each row.
 template <int I>
 __device__ __forceinline__ void row_scales(float v, float k, float (&out)[4]) {

@@ -205,7 +205,7 @@ __device__ __forceinline__ void store_tile(const float (&acc)[TM][TN][4], uint8_
 // group of the output, spread over the four lanes l16, l16 + 16, l16 + 32,
 // l16 + 48.  Each value is first rounded to BF16 (RNE); the group's max-abs,
 // scale and codes are then taken from those BF16 values with the quantizers'
-// own arithmetic (group_scale, pack4_e4m3), so the codes and scales equal
+// own arithmetic (group_scale, pack4_e4m3_grp), so the codes and scales equal
 // what quant_act_1x128 computes from the stored BF16 output.  The BF16 values
 // leave through store_tile (skipped when p.C is NULL); the scaled values are
 // staged through the wave's LDS region in passes of 16 rows so that every
@@ -254,8 +254,8 @@ __device__ __forceinline__ void store_tile_q(const float (&acc)[TM][TN][4], uint
       const float4* src = reinterpret_cast<const float4*>(ep + rl * P + 64 * ch);
       const float4 v0 = src[0], v1 = src[1], v2 = src[2], v3 = src[3];
       if (orow >= mend) continue;
-      const uint32_t w0 = pack4_e4m3(v0.x, v0.y, v0.z, v0.w), w1 = pack4_e4m3(v1.x, v1.y, v1.z, v1.w);
-      const uint32_t w2 = pack4_e4m3(v2.x, v2.y, v2.z, v2.w), w3 = pack4_e4m3(v3.x, v3.y, v3.z, v3.w);
+      const uint32_t w0 = pack4_e4m3_grp(v0.x, v0.y, v0.z, v0.w), w1 = pack4_e4m3_grp(v1.x, v1.y, v1.z, v1.w);
+      const uint32_t w2 = pack4_e4m3_grp(v2.x, v2.y, v2.z, v2.w), w3 = pack4_e4m3_grp(v3.x, v3.y, v3.z, v3.w);
       st_stream16<0>(p.qo + orow * p.ld_qo + col0 + 16 * ch, w0, w1, w2, w3);
     }
   }

@@ -87,8 +87,8 @@ __device__ __forceinline__ void quant_act_block(int vb, const typename In::elem*
     if (r < 0) continue;
     float sc, inv;
     group_scale(__uint_as_float(m), sc, inv);
-    const uint32_t w0 = pack4_e4m3(v[u][0] * inv, v[u][1] * inv, v[u][2] * inv, v[u][3] * inv);
-    const uint32_t w1 = pack4_e4m3(v[u][4] * inv, v[u][5] * inv, v[u][6] * inv, v[u][7] * inv);
+    const uint32_t w0 = pack4_e4m3_grp(v[u][0] * inv, v[u][1] * inv, v[u][2] * inv, v[u][3] * inv);
+    const uint32_t w1 = pack4_e4m3_grp(v[u][4] * inv, v[u][5] * inv, v[u][6] * inv, v[u][7] * inv);
     if (FLAT) {
       st_stream8<NTS>(q + (int64_t)r * 128 + lig * 8, w0, w1);
       if (lig == 0) s[r] = sc;
@@ -171,13 +171,14 @@ __device__ __forceinline__ void quant_weight_block(int bi, int bj, const typenam
   const int c0 = bj * 128 + c4 * 4;
   const bool full_c = c0 + 4 <= cols;
   float v[16][4];
+  // row addresses by pointer increments (no 64-bit multiply per row)
+  const typename In::elem* p = w + (int64_t)r0 * ld_w + c0;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
+  for (int i = 0; i < 16; ++i, p += ld_w) {
     const int r = r0 + i;
 #pragma unroll
     for (int e = 0; e < 4; ++e) v[i][e] = 0.f;
     if (r < rows) {
-      const typename In::elem* p = w + (int64_t)r * ld_w + c0;
       if (full_c) {
         load4<In>(p, v[i]);
       } else {
@@ -201,12 +202,11 @@ __device__ __forceinline__ void quant_weight_block(int bi, int bj, const typenam
   if (t == 0) s[(int64_t)bi * ld_s + bj] = sc;
 
   // row-wise codes: one dword (4 columns) per row
+  uint8_t* qp = q + (int64_t)r0 * ld_q + c0;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int r = r0 + i;
-    if (r >= rows) break;
-    const uint32_t wd = pack4_e4m3(v[i][0] * inv, v[i][1] * inv, v[i][2] * inv, v[i][3] * inv);
-    uint8_t* qp = q + (int64_t)r * ld_q + c0;
+  for (int i = 0; i < 16; ++i, qp += ld_q) {
+    if (r0 + i >= rows) continue;  // (a break here kept the loop from unrolling)
+    const uint32_t wd = pack4_e4m3_grp(v[i][0] * inv, v[i][1] * inv, v[i][2] * inv, v[i][3] * inv);
     if (full_c) {
       st_stream4<NTS>(qp, wd);
     } else {
@@ -227,18 +227,19 @@ __device__ __forceinline__ void quant_weight_block(int bi, int bj, const typenam
       uint32_t d[4];
 #pragma unroll
       for (int k = 0; k < 4; ++k)
-        d[k] = pack4_e4m3(v[4 * k][e] * inv, v[4 * k + 1][e] * inv, v[4 * k + 2][e] * inv, v[4 * k + 3][e] * inv);
+        d[k] = pack4_e4m3_grp(v[4 * k][e] * inv, v[4 * k + 1][e] * inv, v[4 * k + 2][e] * inv, v[4 * k + 3][e] * inv);
       *reinterpret_cast<u32x4*>(tq + (c4 * 4 + e) * 128 + (rb ^ (c4 & 7)) * 16) = u32x4{d[0], d[1], d[2], d[3]};
     }
     __syncthreads();
     const int k16 = t & 7;
+    uint8_t* pq = qt + (int64_t)(bj * 128 + (t >> 3)) * ld_qt + bi * 128 + k16 * 16;
+    const int64_t pass_step = 32 * ld_qt;
 #pragma unroll
-    for (int pass = 0; pass < 4; ++pass) {
+    for (int pass = 0; pass < 4; ++pass, pq += pass_step) {
       const int cl = pass * 32 + (t >> 3);
-      const int c = bj * 128 + cl;
-      if (c >= cols) break;  // columns ascend with the pass
+      if (bj * 128 + cl >= cols) break;  // columns ascend with the pass
       const u32x4 w4 = *reinterpret_cast<const u32x4*>(tq + cl * 128 + (k16 ^ ((cl >> 2) & 7)) * 16);
-      st_stream16<kNtWeightTStore>(qt + (int64_t)c * ld_qt + bi * 128 + k16 * 16, w4[0], w4[1], w4[2], w4[3]);
+      st_stream16<kNtWeightTStore>(pq, w4[0], w4[1], w4[2], w4[3]);
     }
     return;
   }
@@ -250,7 +251,7 @@ __device__ __forceinline__ void quant_weight_block(int bi, int bj, const typenam
     uint32_t d[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k)
-      d[k] = pack4_e4m3(v[4 * k][e] * inv, v[4 * k + 1][e] * inv, v[4 * k + 2][e] * inv, v[4 * k + 3][e] * inv);
+      d[k] = pack4_e4m3_grp(v[4 * k][e] * inv, v[4 * k + 1][e] * inv, v[4 * k + 2][e] * inv, v[4 * k + 3][e] * inv);
     uint8_t* tp = qt + (int64_t)c * ld_qt + r0;
     if (full_r) {
       st_stream16<kNtWeightTStore>(tp, d[0], d[1], d[2], d[3]);
@@ -320,8 +321,16 @@ hipError_t launch_quant_weight(const void* w, bool w_bf16, int64_t rows, int64_t
 // straight from registers, each segment would arrive as four 32-byte pieces
 // from four waves (measured 26.5 -> 22 us for X [4096,7168], 95 -> 80 us for
 // [16384,7168]).
+// Each group's scale is computed once, not by every thread that holds part
+// of the group (the correctly rounded divisions of group_scale dominated the
+// kernel's vector work): a row group's by one lane of its 16-lane DPP row,
+// then broadcast along the row; a column group's by one thread, handed to the
+// others through LDS.  Row addresses advance by pointer increments, not by
+// 64-bit multiplies per row.
+//
 // One 128-token x 128-channel tile (bi, bj) of the transposing quantizer;
-// red (4 x 128 words) and tq (16 KB, 16-byte aligned) are the tile's LDS.
+// red (5 x 128 words: 4 rows of per-wave column maxima, then the column
+// inverse scales) and tq (16 KB, 16-byte aligned) are the tile's LDS.
 template <class In, bool G, bool D, bool F>
 __device__ __forceinline__ void quant_transpose_block(int bi, int bj, const typename In::elem* __restrict__ x,
                                                       int64_t ld_x, int rows, int cols, uint8_t* __restrict__ qt,
@@ -352,13 +361,13 @@ __device__ __forceinline__ void quant_transpose_block(int bi, int bj, const type
   const int oc0 = bi * 128 + rblk * 8;     // its output token column
   const int c0 = bj * 128 + c8 * 8;
   float v[8][8];
+  const typename In::elem* p = x + (int64_t)r0 * ld_x + c0;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < 8; ++i, p += ld_x) {
     const int r = r0 + i;
 #pragma unroll
     for (int e = 0; e < 8; ++e) v[i][e] = 0.f;
     if (F || r < rhi) {
-      const typename In::elem* p = x + (int64_t)r * ld_x + c0;
       if (F || c0 + 8 <= cols) {
         In::template load8<kNtTransLoad>(p, v[i]);
       } else {
@@ -369,20 +378,34 @@ __device__ __forceinline__ void quant_transpose_block(int bi, int bj, const type
     }
   }
   if (D) {
-    // row groups: the 16 threads of a token row form one DPP row of a wave
+    // row groups: the 16 threads of a token row form one DPP row of a wave;
+    // lane c8 < 8 of the row computes the scale of the thread's row c8, and
+    // lane i hands row i's inverse scale to the whole DPP row
+    uint32_t am[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       uint32_t a = 0;
 #pragma unroll
       for (int e = 0; e < 8; ++e) a = max(a, abs_bits(v[i][e]));
-      a = row16_max_u32(a);
-      const int r = r0 + i;
-      if (!F && r >= rows) continue;
-      float sc, iv;
-      group_scale(__uint_as_float(a), sc, iv);
-      const uint32_t w0 = pack4_e4m3(v[i][0] * iv, v[i][1] * iv, v[i][2] * iv, v[i][3] * iv);
-      const uint32_t w1 = pack4_e4m3(v[i][4] * iv, v[i][5] * iv, v[i][6] * iv, v[i][7] * iv);
-      uint8_t* qp = q + (int64_t)r * ld_q + c0;
+      am[i] = row16_max_u32(a);
+    }
+    uint32_t mine = am[0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) mine = (c8 & 7) == i ? am[i] : mine;
+    float sc_m, iv_m;
+    group_scale(__uint_as_float(mine), sc_m, iv_m);
+    if (c8 < 8 && (F || r0 + c8 < rows)) s[(int64_t)(r0 + c8) * ld_s + bj] = sc_m;
+    float ivr[8];
+    ivr[0] = row_bcast<0>(iv_m); ivr[1] = row_bcast<1>(iv_m); ivr[2] = row_bcast<2>(iv_m);
+    ivr[3] = row_bcast<3>(iv_m); ivr[4] = row_bcast<4>(iv_m); ivr[5] = row_bcast<5>(iv_m);
+    ivr[6] = row_bcast<6>(iv_m); ivr[7] = row_bcast<7>(iv_m);
+    uint8_t* qp = q + (int64_t)r0 * ld_q + c0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i, qp += ld_q) {
+      if (!F && r0 + i >= rows) break;
+      const float iv = ivr[i];
+      const uint32_t w0 = pack4_e4m3_grp(v[i][0] * iv, v[i][1] * iv, v[i][2] * iv, v[i][3] * iv);
+      const uint32_t w1 = pack4_e4m3_grp(v[i][4] * iv, v[i][5] * iv, v[i][6] * iv, v[i][7] * iv);
       if (F || c0 + 8 <= cols) {
         *reinterpret_cast<uint2*>(qp) = make_uint2(w0, w1);
       } else {
@@ -390,7 +413,6 @@ __device__ __forceinline__ void quant_transpose_block(int bi, int bj, const type
         for (int e = 0; e < 8; ++e)
           if (c0 + e < cols) qp[e] = (uint8_t)(((e < 4 ? w0 : w1) >> (8 * (e & 3))) & 0xFF);
       }
-      if (c8 == 0) s[(int64_t)r * ld_s + bj] = sc;
     }
   }
   uint32_t m[8];
@@ -409,14 +431,28 @@ __device__ __forceinline__ void quant_transpose_block(int bi, int bj, const type
     for (int e = 0; e < 8; ++e) red[wv][c8 * 8 + e] = m[e];
   }
   __syncthreads();
-  float inv[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const int cl = c8 * 8 + e;
+  {
+    // column group cl's scale, once: threads 0-127 take one column each
+    // (128-255 compute the same values and store none)
+    const int cl = t & 127;
     const uint32_t a = max(max(red[0][cl], red[1][cl]), max(red[2][cl], red[3][cl]));
-    float sc;
-    group_scale(__uint_as_float(a), sc, inv[e]);
-    if (rblk == 0 && (F || c0 + e < cols)) st[(int64_t)(c0 + e) * ld_st + bi] = sc;
+    float sc, iv;
+    group_scale(__uint_as_float(a), sc, iv);
+    if (t < 128) {
+      red[4][cl] = __float_as_uint(iv);
+      if (F || bj * 128 + cl < cols) st[(int64_t)(bj * 128 + cl) * ld_st + bi] = sc;
+    }
+  }
+  __syncthreads();
+  float inv[8];
+  {
+    const u32x4 i0 = *reinterpret_cast<const u32x4*>(&red[4][c8 * 8]);
+    const u32x4 i1 = *reinterpret_cast<const u32x4*>(&red[4][c8 * 8 + 4]);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      inv[e] = __uint_as_float(i0[e]);
+      inv[4 + e] = __uint_as_float(i1[e]);
+    }
   }
   // grouped: rows past the expert's end are padding, stored as code 0 (their
   // values were loaded as 0)
@@ -427,20 +463,21 @@ __device__ __forceinline__ void quant_transpose_block(int bi, int bj, const type
     const int swz = 2 * (c8 & 7);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const uint32_t d0 = pack4_e4m3(v[0][e] * inv[e], v[1][e] * inv[e], v[2][e] * inv[e], v[3][e] * inv[e]);
-      const uint32_t d1 = pack4_e4m3(v[4][e] * inv[e], v[5][e] * inv[e], v[6][e] * inv[e], v[7][e] * inv[e]);
+      const uint32_t d0 = pack4_e4m3_grp(v[0][e] * inv[e], v[1][e] * inv[e], v[2][e] * inv[e], v[3][e] * inv[e]);
+      const uint32_t d1 = pack4_e4m3_grp(v[4][e] * inv[e], v[5][e] * inv[e], v[6][e] * inv[e], v[7][e] * inv[e]);
       *reinterpret_cast<uint2*>(tq + (c8 * 8 + e) * 128 + (rblk ^ swz) * 8) = make_uint2(d0, d1);
     }
     __syncthreads();
     // lane t writes bytes [16 k, 16 k + 16) of channel 32 pass + t/8, k = t%8
     const int k16 = t & 7;
+    uint8_t* pq = qt + (int64_t)(bj * 128 + (t >> 3)) * ld_qt + bi * 128 + k16 * 16;
+    const int64_t pass_step = 32 * ld_qt;
 #pragma unroll
-    for (int pass = 0; pass < 4; ++pass) {
+    for (int pass = 0; pass < 4; ++pass, pq += pass_step) {
       const int cl = pass * 32 + (t >> 3);
-      const int c = bj * 128 + cl;
-      if (!F && c >= cols) break;  // channels ascend with the pass
+      if (!F && bj * 128 + cl >= cols) break;  // channels ascend with the pass
       const u32x4 w = *reinterpret_cast<const u32x4*>(tq + cl * 128 + (k16 ^ ((cl >> 3) & 7)) * 16);
-      st_stream16<kNtTransStore>(qt + (int64_t)c * ld_qt + bi * 128 + k16 * 16, w[0], w[1], w[2], w[3]);
+      st_stream16<kNtTransStore>(pq, w[0], w[1], w[2], w[3]);
     }
     return;
   }
@@ -450,8 +487,8 @@ __device__ __forceinline__ void quant_transpose_block(int bi, int bj, const type
   for (int e = 0; e < 8; ++e) {
     const int c = c0 + e;
     if (!F && c >= cols) break;
-    const uint32_t d0 = pack4_e4m3(v[0][e] * inv[e], v[1][e] * inv[e], v[2][e] * inv[e], v[3][e] * inv[e]);
-    const uint32_t d1 = pack4_e4m3(v[4][e] * inv[e], v[5][e] * inv[e], v[6][e] * inv[e], v[7][e] * inv[e]);
+    const uint32_t d0 = pack4_e4m3_grp(v[0][e] * inv[e], v[1][e] * inv[e], v[2][e] * inv[e], v[3][e] * inv[e]);
+    const uint32_t d1 = pack4_e4m3_grp(v[4][e] * inv[e], v[5][e] * inv[e], v[6][e] * inv[e], v[7][e] * inv[e]);
     uint8_t* tp = qt + (int64_t)c * ld_qt + oc0;
     if (full_r) {
       st_stream8<kNtTransStore>(tp, d0, d1);
@@ -471,7 +508,7 @@ __global__ __launch_bounds__(256) void k_quant_transpose(const typename In::elem
                                                          const int32_t* __restrict__ offsets, int E,
                                                          uint8_t* __restrict__ q, int64_t ld_q,
                                                          float* __restrict__ s, int64_t ld_s) {
-  __shared__ uint32_t red[4][128];
+  __shared__ __attribute__((aligned(16))) uint32_t red[5][128];
   __shared__ __attribute__((aligned(16))) uint8_t tq[128 * 128];  // [channel][token] codes of the tile
   quant_transpose_block<In, G, D, F>((int)blockIdx.y, (int)blockIdx.x, x, ld_x, rows, cols, qt, ld_qt, st, ld_st,
                                      offsets, E, q, ld_q, s, ld_s, red, tq);
@@ -562,7 +599,7 @@ enum : int { kVAct = 0, kVWeight = 8, kVTrans = 12, kVDual = 16 };
 
 template <bool TILES>
 __global__ __launch_bounds__(256) void k_quant_batch(QBatch b) {
-  __shared__ uint32_t red[TILES ? 4 : 1][128];
+  __shared__ __attribute__((aligned(16))) uint32_t red[TILES ? 5 : 1][128];
   __shared__ __attribute__((aligned(16))) uint8_t tq[TILES ? 128 * 128 : 16];
   const int bid = (int)blockIdx.x;
   int j = 0;
