@@ -22,6 +22,7 @@
 // byte written once, reductions stay in registers and DPP.
 
 #include "device_common.h"
+#include <type_traits>
 #include "launch.h"
 
 namespace fp8q {
@@ -137,7 +138,11 @@ hipError_t launch_quant_mx(const void* x, bool x_bf16, int64_t rows, int64_t col
 // D (dual output): the tile's rows also yield the 1x32 row blocks (a DPP
 // quad of lanes spans 32 consecutive columns of one row), so x is read once
 // for both the row codes q [rows, cols] and the transposed ones.
-template <class In, bool D>
+//
+// F (full tiles): rows and cols are multiples of 128, so every tile is whole
+// and the per-row and per-column bounds checks drop out (with them in, the
+// loads sat in separate branches and could not be issued together).
+template <class In, bool D, bool F>
 __global__ __launch_bounds__(256) void k_quant_mx_t(const typename In::elem* __restrict__ x, int64_t ld_x,
                                                     int rows, int cols,
                                                     uint8_t* __restrict__ qt, int64_t ld_qt,
@@ -151,14 +156,16 @@ __global__ __launch_bounds__(256) void k_quant_mx_t(const typename In::elem* __r
   const int r0 = bi * 128 + rblk * 8;
   const int c0 = bj * 128 + c8 * 8;
   float v[8][8];
+  // row and column addresses advance by pointer increments (a 64-bit
+  // multiply per row or column was a large share of the vector work)
+  const typename In::elem* p = x + (int64_t)r0 * ld_x + c0;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < 8; ++i, p += ld_x) {
     const int r = r0 + i;
 #pragma unroll
     for (int e = 0; e < 8; ++e) v[i][e] = 0.f;
-    if (r < rows) {
-      const typename In::elem* p = x + (int64_t)r * ld_x + c0;
-      if (c0 + 8 <= cols) {
+    if (F || r < rows) {
+      if (F || c0 + 8 <= cols) {
         In::template load8<1>(p, v[i]);
       } else {
 #pragma unroll
@@ -168,27 +175,28 @@ __global__ __launch_bounds__(256) void k_quant_mx_t(const typename In::elem* __r
     }
   }
   if (D) {
+    uint8_t* qp = q + (int64_t)r0 * ld_q + c0;
+    uint8_t* sp = s + (int64_t)r0 * ld_s + (c0 >> 5);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < 8; ++i, qp += ld_q, sp += ld_s) {
       uint32_t a = 0;
 #pragma unroll
       for (int e = 0; e < 8; ++e) a = max(a, abs_bits(v[i][e]));
       a = quad_max_u32(a);
       const int r = r0 + i;
-      if (r >= rows || c0 >= cols) continue;
+      if (!F && (r >= rows || c0 >= cols)) continue;
       float iv;
       const uint32_t byte = mx_scale(a, iv);
       const uint32_t w0 = pack4_e4m3(v[i][0] * iv, v[i][1] * iv, v[i][2] * iv, v[i][3] * iv);
       const uint32_t w1 = pack4_e4m3(v[i][4] * iv, v[i][5] * iv, v[i][6] * iv, v[i][7] * iv);
-      uint8_t* qp = q + (int64_t)r * ld_q + c0;
-      if (c0 + 8 <= cols) {
+      if (F || c0 + 8 <= cols) {
         *reinterpret_cast<uint2*>(qp) = make_uint2(w0, w1);
       } else {
 #pragma unroll
         for (int e = 0; e < 8; ++e)
           if (c0 + e < cols) qp[e] = (uint8_t)(((e < 4 ? w0 : w1) >> (8 * (e & 3))) & 0xFF);
       }
-      if ((c8 & 3) == 0) s[(int64_t)r * ld_s + (c0 >> 5)] = (uint8_t)byte;
+      if ((c8 & 3) == 0) *sp = (uint8_t)byte;
     }
   }
   // column maxima over the wave's 32 rows: all 16 cross-lane exchanges are
@@ -205,29 +213,29 @@ __global__ __launch_bounds__(256) void k_quant_mx_t(const typename In::elem* __r
   for (int e = 0; e < 8; ++e) m[e] = max(m[e], (uint32_t)__shfl_xor((int)m[e], 16));
 #pragma unroll
   for (int e = 0; e < 8; ++e) m[e] = max(m[e], (uint32_t)__shfl_xor((int)m[e], 32));
-  const bool block_present = bi * 128 + wv * 32 < rows;  // this wave's 32-row block has rows
-  const bool full_r = r0 + 8 <= rows;
+  const bool block_present = F || bi * 128 + wv * 32 < rows;  // this wave's 32-row block has rows
+  const bool full_r = F || r0 + 8 <= rows;
   const int oc0 = bi * 128 + rblk * 8;  // output token column of this thread's rows
   // A tile of 128 whole tokens stages its transposed codes in LDS (channel
   // cl's 128 token codes at tq[128 cl], 8-byte token chunk k at slot
   // k ^ (2 (c8 & 7))) so that 8 lanes write each 128-byte q_t row segment
   // together; a partial last token tile stores from registers.
-  const bool staged = bi * 128 + 128 <= rows;
+  const bool staged = F || bi * 128 + 128 <= rows;
   const int swz = 2 * (c8 & 7);
+  uint8_t* stp = st + (int64_t)c0 * ld_st + bi * 4 + wv;
+  uint8_t* tp = qt + (int64_t)c0 * ld_qt + oc0;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const int c = c0 + e;
-    if (c >= cols) break;
+  for (int e = 0; e < 8; ++e, stp += ld_st, tp += ld_qt) {
+    if (!F && c0 + e >= cols) continue;
     float iv;
     const uint32_t byte = mx_scale(m[e], iv);
-    if ((t & 63) < 16 && block_present) st[(int64_t)c * ld_st + bi * 4 + wv] = (uint8_t)byte;
+    if ((t & 63) < 16 && block_present) *stp = (uint8_t)byte;
     const uint32_t d0 = pack4_e4m3(v[0][e] * iv, v[1][e] * iv, v[2][e] * iv, v[3][e] * iv);
     const uint32_t d1 = pack4_e4m3(v[4][e] * iv, v[5][e] * iv, v[6][e] * iv, v[7][e] * iv);
     if (staged) {
       *reinterpret_cast<uint2*>(tq + (c8 * 8 + e) * 128 + (rblk ^ swz) * 8) = make_uint2(d0, d1);
       continue;
     }
-    uint8_t* tp = qt + (int64_t)c * ld_qt + oc0;
     if (full_r) {
       *reinterpret_cast<uint2*>(tp) = make_uint2(d0, d1);
     } else {
@@ -240,13 +248,14 @@ __global__ __launch_bounds__(256) void k_quant_mx_t(const typename In::elem* __r
   __syncthreads();
   // lane t writes bytes [16 k, 16 k + 16) of channel 32 pass + t/8, k = t%8
   const int k16 = t & 7;
+  uint8_t* pq = qt + (int64_t)(bj * 128 + (t >> 3)) * ld_qt + bi * 128 + k16 * 16;
+  const int64_t pass_step = 32 * ld_qt;
 #pragma unroll
-  for (int pass = 0; pass < 4; ++pass) {
+  for (int pass = 0; pass < 4; ++pass, pq += pass_step) {
     const int cl = pass * 32 + (t >> 3);
-    const int c = bj * 128 + cl;
-    if (c >= cols) break;  // channels ascend with the pass
+    if (!F && bj * 128 + cl >= cols) break;  // channels ascend with the pass
     const u32x4 w = *reinterpret_cast<const u32x4*>(tq + cl * 128 + (k16 ^ ((cl >> 3) & 7)) * 16);
-    *reinterpret_cast<u32x4*>(qt + (int64_t)c * ld_qt + bi * 128 + k16 * 16) = w;
+    *reinterpret_cast<u32x4*>(pq) = w;
   }
 }
 
@@ -254,21 +263,22 @@ hipError_t launch_quant_mx_transpose(const void* x, bool x_bf16, int64_t rows, i
                                      uint8_t* q_t, int64_t ld_qt, uint8_t* s_t, int64_t ld_st, uint8_t* q,
                                      int64_t ld_q, uint8_t* s, int64_t ld_s, hipStream_t st) {
   const dim3 grid((uint32_t)((cols + 127) / 128), (uint32_t)((rows + 127) / 128));
-  const bool dual = q != nullptr;
+  const bool dual = q != nullptr, full = rows % 128 == 0 && cols % 128 == 0;
+  auto go = [&](auto in, auto d, auto f) {
+    typedef decltype(in) In;
+    constexpr bool D = decltype(d)::value, F = decltype(f)::value;
+    hipLaunchKernelGGL((k_quant_mx_t<In, D, F>), grid, dim3(256), 0, st, (const typename In::elem*)x, ld_x,
+                       (int)rows, (int)cols, q_t, ld_qt, s_t, ld_st, D ? q : nullptr, D ? ld_q : 0,
+                       D ? s : nullptr, D ? ld_s : 0);
+  };
+  using T = std::true_type;
+  using N = std::false_type;
   if (x_bf16) {
-    if (dual)
-      hipLaunchKernelGGL((k_quant_mx_t<BF16In, true>), grid, dim3(256), 0, st, (const uint16_t*)x, ld_x, (int)rows,
-                         (int)cols, q_t, ld_qt, s_t, ld_st, q, ld_q, s, ld_s);
-    else
-      hipLaunchKernelGGL((k_quant_mx_t<BF16In, false>), grid, dim3(256), 0, st, (const uint16_t*)x, ld_x, (int)rows,
-                         (int)cols, q_t, ld_qt, s_t, ld_st, nullptr, 0, nullptr, 0);
+    if (dual) full ? go(BF16In{}, T{}, T{}) : go(BF16In{}, T{}, N{});
+    else full ? go(BF16In{}, N{}, T{}) : go(BF16In{}, N{}, N{});
   } else {
-    if (dual)
-      hipLaunchKernelGGL((k_quant_mx_t<F32In, true>), grid, dim3(256), 0, st, (const float*)x, ld_x, (int)rows,
-                         (int)cols, q_t, ld_qt, s_t, ld_st, q, ld_q, s, ld_s);
-    else
-      hipLaunchKernelGGL((k_quant_mx_t<F32In, false>), grid, dim3(256), 0, st, (const float*)x, ld_x, (int)rows,
-                         (int)cols, q_t, ld_qt, s_t, ld_st, nullptr, 0, nullptr, 0);
+    if (dual) full ? go(F32In{}, T{}, T{}) : go(F32In{}, T{}, N{});
+    else full ? go(F32In{}, N{}, T{}) : go(F32In{}, N{}, N{});
   }
   return hipGetLastError();
 }
