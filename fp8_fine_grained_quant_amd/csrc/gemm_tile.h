@@ -179,13 +179,17 @@ __device__ __forceinline__ void store_tile(const float (&acc)[TM][TN][4], uint8_
       }
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS writes are done
     __builtin_amdgcn_wave_barrier();
+    // (row addresses by pointer increments: a 64-bit multiply per store was
+    // most of the epilogue's address arithmetic)
+    uint8_t* dst = reinterpret_cast<uint8_t*>(p.C) +
+                   ((row0 + pass * ER + lane / CPR) * p.ldc + col0) * ES + 16 * (lane % CPR);
+    const int64_t it_step = (int64_t)RPI * p.ldc * ES;
 #pragma unroll
-    for (int it = 0; it < ER / RPI; ++it) {
+    for (int it = 0; it < ER / RPI; ++it, dst += it_step) {
       const int rl = it * RPI + lane / CPR, ch = lane % CPR;
       const int64_t row = row0 + pass * ER + rl;
       if (row >= mend) continue;
       const uint4 v = *reinterpret_cast<const uint4*>(ep + rl * P + 16 * ch);
-      uint8_t* dst = reinterpret_cast<uint8_t*>(p.C) + (row * p.ldc + col0) * ES + 16 * ch;
       if (OUT_F32 && p.accumulate) {
         const float4 o = *reinterpret_cast<const float4*>(dst);
         float4 f = *reinterpret_cast<const float4*>(&v);
