@@ -312,8 +312,12 @@ hipError_t launch_quant_weight(const void* w, bool w_bf16, int64_t rows, int64_t
 // tile's 128 channels of one token are exactly one 1x128 group -- so X is
 // read once for both the row codes q [rows, cols] and the transposed ones.
 //
-// F (full tiles, not grouped): rows and cols are multiples of 128, so every
-// tile is whole and the per-row and per-column bounds checks drop out.
+// F (full tiles): cols is a multiple of 128, and (not grouped) so is rows, so
+// every tile is whole and the per-row and per-column bounds checks drop out.
+// Grouped with F: the columns are whole; the rows past the expert's end load
+// the expert's first row of the tile instead and are zeroed by a select, so
+// no load sits in a branch of its own (in branches they were issued and
+// waited for one by one).
 //
 // The transposed codes of a tile that spans 128 whole tokens are staged in
 // LDS (one 128-byte row per channel), so that every global store writes 16
@@ -362,12 +366,20 @@ __device__ __forceinline__ void quant_transpose_block(int bi, int bj, const type
   const int c0 = bj * 128 + c8 * 8;
   float v[8][8];
   const typename In::elem* p = x + (int64_t)r0 * ld_x + c0;
+  const typename In::elem* const p_first = x + (int64_t)rlo * ld_x + c0;  // a valid row of the tile
 #pragma unroll
   for (int i = 0; i < 8; ++i, p += ld_x) {
     const int r = r0 + i;
+    if (G && F) {
+      const bool ok = r < rhi;
+      In::template load8<kNtTransLoad>(ok ? p : p_first, v[i]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[i][e] = ok ? v[i][e] : 0.f;
+      continue;
+    }
 #pragma unroll
     for (int e = 0; e < 8; ++e) v[i][e] = 0.f;
-    if (F || r < rhi) {
+    if ((F && !G) || r < rhi) {
       if (F || c0 + 8 <= cols) {
         In::template load8<kNtTransLoad>(p, v[i]);
       } else {
@@ -552,12 +564,22 @@ hipError_t launch_quant_transpose_grouped(const void* x, bool x_bf16, int64_t ro
                                           float* s_t, int64_t ld_st, hipStream_t st) {
   // one block per padded 128-token chunk of the capacity 128*(rows/128 + E)
   const dim3 grid((uint32_t)((cols + 127) / 128), (uint32_t)(rows / 128 + E));
-  if (x_bf16)
-    hipLaunchKernelGGL((k_quant_transpose<BF16In, true, false, false>), grid, dim3(256), 0, st, (const uint16_t*)x, ld_x,
-                       (int)rows, (int)cols, q_t, ld_qt, s_t, ld_st, offsets, (int)E, nullptr, 0, nullptr, 0);
-  else
-    hipLaunchKernelGGL((k_quant_transpose<F32In, true, false, false>), grid, dim3(256), 0, st, (const float*)x, ld_x,
-                       (int)rows, (int)cols, q_t, ld_qt, s_t, ld_st, offsets, (int)E, nullptr, 0, nullptr, 0);
+  const bool fc = cols % 128 == 0;  // whole column tiles
+  if (x_bf16) {
+    if (fc)
+      hipLaunchKernelGGL((k_quant_transpose<BF16In, true, false, true>), grid, dim3(256), 0, st, (const uint16_t*)x,
+                         ld_x, (int)rows, (int)cols, q_t, ld_qt, s_t, ld_st, offsets, (int)E, nullptr, 0, nullptr, 0);
+    else
+      hipLaunchKernelGGL((k_quant_transpose<BF16In, true, false, false>), grid, dim3(256), 0, st, (const uint16_t*)x,
+                         ld_x, (int)rows, (int)cols, q_t, ld_qt, s_t, ld_st, offsets, (int)E, nullptr, 0, nullptr, 0);
+  } else {
+    if (fc)
+      hipLaunchKernelGGL((k_quant_transpose<F32In, true, false, true>), grid, dim3(256), 0, st, (const float*)x, ld_x,
+                         (int)rows, (int)cols, q_t, ld_qt, s_t, ld_st, offsets, (int)E, nullptr, 0, nullptr, 0);
+    else
+      hipLaunchKernelGGL((k_quant_transpose<F32In, true, false, false>), grid, dim3(256), 0, st, (const float*)x, ld_x,
+                         (int)rows, (int)cols, q_t, ld_qt, s_t, ld_st, offsets, (int)E, nullptr, 0, nullptr, 0);
+  }
   return hipGetLastError();
 }
 
