@@ -40,7 +40,8 @@ def _check_transpose_grouped(x_cpu, counts, what):
 
 
 @pytest.mark.parametrize("counts", RAGGED, ids=[f"case{i}" for i in range(len(RAGGED))])
-@pytest.mark.parametrize("cols,dtype", [(256, torch.bfloat16), (200, torch.float32), (24, torch.bfloat16)])
+@pytest.mark.parametrize("cols,dtype", [(256, torch.bfloat16), (384, torch.float32), (200, torch.float32),
+                                        (24, torch.bfloat16)])
 def test_quant_transpose_grouped_small(counts, cols, dtype):
     m = int(sum(counts))
     x = synth.general(m, cols, seed=m + cols, kind="t3", outlier_frac=0.01, outlier_mul=50.0)
