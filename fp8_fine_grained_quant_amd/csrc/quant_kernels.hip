@@ -15,6 +15,8 @@
 #include "device_common.h"
 #include "launch.h"
 
+#include <type_traits>
+
 namespace fp8q {
 
 // Non-temporal choices per access (see ld_stream16).  Inputs are read once,
@@ -158,8 +160,10 @@ __device__ __forceinline__ void load4<BF16In>(const uint16_t* p, float v[4]) {
 }
 
 // One 128 x 128 block (bi, bj) of the weight quantizer; red (4 words) and tq
-// (16 KB, 16-byte aligned) are the block's LDS.
-template <class In, int NTS>
+// (16 KB, 16-byte aligned) are the block's LDS.  F (full blocks): rows and
+// cols are multiples of 128, so the per-row and per-column checks drop out
+// (with them in, each row's load sat in a branch of its own).
+template <class In, int NTS, bool F>
 __device__ __forceinline__ void quant_weight_block(int bi, int bj, const typename In::elem* __restrict__ w,
                                                    int64_t ld_w, int rows, int cols, uint8_t* __restrict__ q,
                                                    int64_t ld_q, uint8_t* __restrict__ qt, int64_t ld_qt,
@@ -169,7 +173,7 @@ __device__ __forceinline__ void quant_weight_block(int bi, int bj, const typenam
   const int c4 = t & 31, rb = t >> 5;
   const int r0 = bi * 128 + rb * 16;
   const int c0 = bj * 128 + c4 * 4;
-  const bool full_c = c0 + 4 <= cols;
+  const bool full_c = F || c0 + 4 <= cols;
   float v[16][4];
   // row addresses by pointer increments (no 64-bit multiply per row)
   const typename In::elem* p = w + (int64_t)r0 * ld_w + c0;
@@ -178,7 +182,7 @@ __device__ __forceinline__ void quant_weight_block(int bi, int bj, const typenam
     const int r = r0 + i;
 #pragma unroll
     for (int e = 0; e < 4; ++e) v[i][e] = 0.f;
-    if (r < rows) {
+    if (F || r < rows) {
       if (full_c) {
         load4<In>(p, v[i]);
       } else {
@@ -205,7 +209,7 @@ __device__ __forceinline__ void quant_weight_block(int bi, int bj, const typenam
   uint8_t* qp = q + (int64_t)r0 * ld_q + c0;
 #pragma unroll
   for (int i = 0; i < 16; ++i, qp += ld_q) {
-    if (r0 + i >= rows) continue;  // (a break here kept the loop from unrolling)
+    if (!F && r0 + i >= rows) continue;  // (a break here kept the loop from unrolling)
     const uint32_t wd = pack4_e4m3_grp(v[i][0] * inv, v[i][1] * inv, v[i][2] * inv, v[i][3] * inv);
     if (full_c) {
       st_stream4<NTS>(qp, wd);
@@ -221,7 +225,7 @@ __device__ __forceinline__ void quant_weight_block(int bi, int bj, const typenam
   // at tq[128 cl], 16-byte row chunk k at slot k ^ ((cl / 4) % 8)), so that 8
   // lanes write each 128-byte q_t row segment together instead of four waves
   // writing 32 bytes of it each.
-  if (bi * 128 + 128 <= rows) {
+  if (F || bi * 128 + 128 <= rows) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       uint32_t d[4];
@@ -237,7 +241,7 @@ __device__ __forceinline__ void quant_weight_block(int bi, int bj, const typenam
 #pragma unroll
     for (int pass = 0; pass < 4; ++pass, pq += pass_step) {
       const int cl = pass * 32 + (t >> 3);
-      if (bj * 128 + cl >= cols) break;  // columns ascend with the pass
+      if (!F && bj * 128 + cl >= cols) break;  // columns ascend with the pass
       const u32x4 w4 = *reinterpret_cast<const u32x4*>(tq + cl * 128 + (k16 ^ ((cl >> 2) & 7)) * 16);
       st_stream16<kNtWeightTStore>(pq, w4[0], w4[1], w4[2], w4[3]);
     }
@@ -263,7 +267,7 @@ __device__ __forceinline__ void quant_weight_block(int bi, int bj, const typenam
   }
 }
 
-template <class In, int NTS>
+template <class In, int NTS, bool F>
 __global__ __launch_bounds__(256) void k_quant_weight(const typename In::elem* __restrict__ w, int64_t ld_w,
                                                       int rows, int cols,
                                                       uint8_t* __restrict__ q, int64_t ld_q,
@@ -271,31 +275,30 @@ __global__ __launch_bounds__(256) void k_quant_weight(const typename In::elem* _
                                                       float* __restrict__ s, int64_t ld_s) {
   __shared__ uint32_t red[4];
   __shared__ __attribute__((aligned(16))) uint8_t tq[128 * 128];  // [column][row] codes of the block
-  quant_weight_block<In, NTS>((int)blockIdx.y, (int)blockIdx.x, w, ld_w, rows, cols, q, ld_q, qt, ld_qt, s, ld_s,
-                              red, tq);
+  quant_weight_block<In, NTS, F>((int)blockIdx.y, (int)blockIdx.x, w, ld_w, rows, cols, q, ld_q, qt, ld_qt, s,
+                                 ld_s, red, tq);
 }
 
 hipError_t launch_quant_weight(const void* w, bool w_bf16, int64_t rows, int64_t cols, int64_t ld_w,
                                uint8_t* q, int64_t ld_q, uint8_t* q_t, int64_t ld_qt,
                                float* s, int64_t ld_s, hipStream_t st) {
   const dim3 grid((uint32_t)((cols + 127) / 128), (uint32_t)((rows + 127) / 128));
-  const bool nt = rows * cols > kNtCodeBytes;
+  const bool nt = rows * cols > kNtCodeBytes, full = rows % 128 == 0 && cols % 128 == 0;
+  auto go = [&](auto in, auto n, auto f) {
+    typedef decltype(in) In;
+    hipLaunchKernelGGL((k_quant_weight<In, decltype(n)::value, decltype(f)::value>), grid, dim3(256), 0, st,
+                       (const typename In::elem*)w, ld_w, (int)rows, (int)cols, q, ld_q, q_t, ld_qt, s, ld_s);
+  };
+  using N0 = std::integral_constant<int, 0>;
+  using N1 = std::integral_constant<int, 1>;
+  using T = std::true_type;
+  using Fa = std::false_type;
   if (w_bf16) {
-    const uint16_t* wb = (const uint16_t*)w;
-    if (nt)
-      hipLaunchKernelGGL((k_quant_weight<BF16In, 1>), grid, dim3(256), 0, st, wb, ld_w, (int)rows, (int)cols, q,
-                         ld_q, q_t, ld_qt, s, ld_s);
-    else
-      hipLaunchKernelGGL((k_quant_weight<BF16In, 0>), grid, dim3(256), 0, st, wb, ld_w, (int)rows, (int)cols, q,
-                         ld_q, q_t, ld_qt, s, ld_s);
+    if (nt) full ? go(BF16In{}, N1{}, T{}) : go(BF16In{}, N1{}, Fa{});
+    else full ? go(BF16In{}, N0{}, T{}) : go(BF16In{}, N0{}, Fa{});
   } else {
-    const float* wf = (const float*)w;
-    if (nt)
-      hipLaunchKernelGGL((k_quant_weight<F32In, 1>), grid, dim3(256), 0, st, wf, ld_w, (int)rows, (int)cols, q,
-                         ld_q, q_t, ld_qt, s, ld_s);
-    else
-      hipLaunchKernelGGL((k_quant_weight<F32In, 0>), grid, dim3(256), 0, st, wf, ld_w, (int)rows, (int)cols, q,
-                         ld_q, q_t, ld_qt, s, ld_s);
+    if (nt) full ? go(F32In{}, N1{}, T{}) : go(F32In{}, N1{}, Fa{});
+    else full ? go(F32In{}, N0{}, T{}) : go(F32In{}, N0{}, Fa{});
   }
   return hipGetLastError();
 }
@@ -617,7 +620,7 @@ struct QBatch {
   int n;
 };
 
-enum : int { kVAct = 0, kVWeight = 8, kVTrans = 12, kVDual = 16 };
+enum : int { kVAct = 0, kVWeight = 8, kVTrans = 16, kVDual = 20 };
 
 template <bool TILES>
 __global__ __launch_bounds__(256) void k_quant_batch(QBatch b) {
@@ -633,9 +636,9 @@ __global__ __launch_bounds__(256) void k_quant_batch(QBatch b) {
   const float* xf = (const float*)J.x;
 #define FP8Q_ACT_CASE(V, T, F, N, XP)                                                                     \
   case V: quant_act_block<T, F, N>(vb, XP, J.ld_x, J.q, J.ld_q, J.s, J.ld_s, J.cols, J.ngr, J.total); break;
-#define FP8Q_W_CASE(V, T, N, XP)                                                                             \
-  case V: quant_weight_block<T, N>(bi, bj, XP, J.ld_x, J.rows, J.cols, J.q, J.ld_q, J.qt, J.ld_qt, J.s, J.ld_s, \
-                                   &red[0][0], tq); break;
+#define FP8Q_W_CASE(V, T, N, F, XP)                                                                          \
+  case V: quant_weight_block<T, N, F>(bi, bj, XP, J.ld_x, J.rows, J.cols, J.q, J.ld_q, J.qt, J.ld_qt, J.s,      \
+                                      J.ld_s, &red[0][0], tq); break;
 #define FP8Q_T_CASE(V, T, D, F, XP)                                                                      \
   case V: quant_transpose_block<T, false, D, F>(bi, bj, XP, J.ld_x, J.rows, J.cols, J.qt, J.ld_qt, J.st,   \
                                                 J.ld_st, nullptr, 0, J.q, J.ld_q, J.s, J.ld_s, red, tq); break;
@@ -654,10 +657,14 @@ __global__ __launch_bounds__(256) void k_quant_batch(QBatch b) {
     return;
   }
   switch (J.variant) {
-    FP8Q_W_CASE(kVWeight + 0, F32In, 0, xf)
-    FP8Q_W_CASE(kVWeight + 1, F32In, 1, xf)
-    FP8Q_W_CASE(kVWeight + 2, BF16In, 0, xb)
-    FP8Q_W_CASE(kVWeight + 3, BF16In, 1, xb)
+    FP8Q_W_CASE(kVWeight + 0, F32In, 0, false, xf)
+    FP8Q_W_CASE(kVWeight + 1, F32In, 1, false, xf)
+    FP8Q_W_CASE(kVWeight + 2, BF16In, 0, false, xb)
+    FP8Q_W_CASE(kVWeight + 3, BF16In, 1, false, xb)
+    FP8Q_W_CASE(kVWeight + 4, F32In, 0, true, xf)
+    FP8Q_W_CASE(kVWeight + 5, F32In, 1, true, xf)
+    FP8Q_W_CASE(kVWeight + 6, BF16In, 0, true, xb)
+    FP8Q_W_CASE(kVWeight + 7, BF16In, 1, true, xb)
     FP8Q_T_CASE(kVTrans + 0, F32In, false, false, xf)
     FP8Q_T_CASE(kVTrans + 1, F32In, false, true, xf)
     FP8Q_T_CASE(kVTrans + 2, BF16In, false, false, xb)
@@ -711,7 +718,7 @@ static hipError_t launch_batch_class(const QuantJob* jobs, int n, hipStream_t st
       B.gx = 1;
       nb = ((total + 4 * kActU - 1) / (4 * kActU) + 3) / 4;
     } else if (J.kind == 1) {
-      B.variant = kVWeight + 2 * bf + (J.rows * J.cols > kNtCodeBytes ? 1 : 0);
+      B.variant = kVWeight + (full ? 4 : 0) + 2 * bf + (J.rows * J.cols > kNtCodeBytes ? 1 : 0);
       nb = (int64_t)B.gx * gy;
     } else {
       B.variant = (J.kind == 2 ? kVTrans : kVDual) + 2 * bf + (full ? 1 : 0);
