@@ -67,8 +67,10 @@ def check_resource_report(src, report):
         if _USAGE in line:
             if "Function Name:" in line:
                 kernel = line.split("Function Name:")[1].split("[")[0].strip()
-            elif "ScratchSize" in line and int(line.split("ScratchSize [bytes/lane]:")[1].split()[0]) > 0:
-                bad.append(f"{kernel}: {line.split('remark:')[-1].split('[')[0].strip()}")
+            elif "ScratchSize" in line:
+                size = int(line.split("ScratchSize [bytes/lane]:")[1].split()[0])
+                if size > 0:
+                    bad.append(f"{kernel}: {size} bytes of scratch per lane")
             continue
         if "loop not unrolled" in line:
             bad.append(line.strip())
