@@ -25,6 +25,7 @@ Prints one JSON line on stdout; progress goes to stderr.
 
 import argparse
 import hashlib
+import re
 import json
 import os
 import sys
@@ -748,12 +749,17 @@ def cpu_baseline(H, frac):
 
 
 def kernel_source_hash():
-    """SHA-256 over the kernel sources: measured HBM traffic is reported only
-    while the kernels are the ones the counters were taken on."""
+    """SHA-256 over the kernel sources' code (comments and whitespace
+    removed): measured HBM traffic is reported only while the kernels are
+    the ones the counters were taken on, and an edit of a comment does not
+    change them."""
     h = hashlib.sha256()
     for name in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "fp8_fine_grained_quant_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "fp8_fine_grained_quant_amd", "csrc", name)) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

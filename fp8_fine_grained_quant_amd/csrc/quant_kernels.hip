@@ -594,8 +594,8 @@ hipError_t launch_quant_transpose_grouped(const void* x, bool x_bf16, int64_t ro
 // kernel it stands for (the block bodies above), so outputs are bit for bit
 // those of the separate calls.  Jobs go to one of two grids by resource
 // class: the activation quantizer needs ~30 VGPRs and no LDS and runs 8
-// waves per SIMD, the tile quantizers (weight, transpose, dual) up to ~147
-// VGPRs and 18 KB of LDS; one grid for both would hold the activation blocks
+// waves per SIMD, the tile quantizers (weight, transpose, dual) up to ~154
+// VGPRs and 18.5 KB of LDS; one grid for both would hold the activation blocks
 // to the tile blocks' occupancy (measured: X and W in one grid 44.7 us
 // against 36.2 us for the two launches).
 struct QBody {
