@@ -328,6 +328,7 @@ hipError_t launch_quant_weight(const void* w, bool w_bf16, int64_t rows, int64_t
 // straight from registers, each segment would arrive as four 32-byte pieces
 // from four waves (measured 26.5 -> 22 us for X [4096,7168], 95 -> 80 us for
 // [16384,7168]).
+//
 // Each group's scale is computed once, not by every thread that holds part
 // of the group (the correctly rounded divisions of group_scale dominated the
 // kernel's vector work): a row group's by one lane of its 16-lane DPP row,
@@ -393,9 +394,10 @@ __device__ __forceinline__ void quant_transpose_block(int bi, int bj, const type
     }
   }
   if (D) {
-    // row groups: the 16 threads of a token row form one DPP row of a wave;
-    // lane c8 < 8 of the row computes the scale of the thread's row c8, and
-    // lane i hands row i's inverse scale to the whole DPP row
+    // row groups: the 16 threads holding the tile's 8 rows r0..r0+7 form one
+    // DPP row of a wave; lane c8 < 8 computes the scale of row r0 + c8 (lanes
+    // 8-15 repeat rows 0-7), and lane i hands row i's inverse scale to the
+    // whole DPP row
     uint32_t am[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
