@@ -132,10 +132,11 @@ def _counts(rng, experts, tokens):
     cut = np.sort(rng.integers(0, tokens + 1, size=experts - 1))
     counts = np.diff(np.concatenate([[0], cut, [tokens]]))
     for e in range(experts):
-        if rng.random() < 0.25:
+        if rng.random() < 0.25 and experts > 1:  # a lone expert keeps every token
             nb = (e + 1) % experts
             counts[nb] += counts[e]
             counts[e] = 0
+    assert counts.sum() == tokens
     return counts
 
 
