@@ -30,7 +30,7 @@ def _tensor(rows, cols, seed, bf16, rng):
     return synth.to_bf16(x) if bf16 else torch.from_numpy(x.astype(np.float32))
 
 
-@pytest.mark.parametrize("case", range(16))
+@pytest.mark.parametrize("case", range(48))
 def test_quantizers_shape_sweep(case):
     rng = _rng(case)
     rows = int(rng.integers(1, 39)) * 16
@@ -79,7 +79,7 @@ def _with_tile(tile, fn):
         fq.set_gemm_tile("auto")
 
 
-@pytest.mark.parametrize("case", range(16))
+@pytest.mark.parametrize("case", range(48))
 def test_gemms_shape_sweep(case):
     rng = _rng(100 + case)
     m = int(rng.integers(1, 700))
@@ -140,7 +140,7 @@ def _counts(rng, experts, tokens):
     return counts
 
 
-@pytest.mark.parametrize("case", range(6))
+@pytest.mark.parametrize("case", range(24))
 def test_grouped_shape_sweep(case):
     """Grouped Fprop, grouped Dgrad (FP8 and exact where the entry point has
     it), the grouped transposing quantizer and grouped Wgrad over random
